@@ -1,0 +1,155 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check a pin fails.
+
+Each mutation replaces one oracle step with a subtly wrong version; the pin
+suite in test_oracle_pins.py must reject every one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.decode as od
+import oracle.prefill as op
+from tests import test_oracle_pins as pins
+
+F32 = np.float32
+
+
+def _swa_off_by_one(rows, w):
+    lo = max(0, int(rows[0]) - w)
+    union = np.arange(lo, int(rows[-1]) + 1, dtype=np.int64)
+    i, j = rows[:, None], union[None, :]
+    return union, (j <= i) & (j >= i - w)          # keeps w+1 keys
+
+
+def _select_smallest(sc, qb, k):
+    cand = np.arange(1, max(qb, 1), dtype=np.int64)
+    order = np.lexsort((cand, sc))                  # sign flipped
+    top = cand[order[:k]]
+    s_k = float(sc[order[k - 1]]) if 1 <= k <= len(cand) else math.nan
+    s_k1 = float(sc[order[k]]) if k + 1 <= len(cand) else math.nan
+    return np.unique(np.concatenate([[0], top, [qb]])), s_k, s_k1
+
+
+def _select_high_index_ties(sc, qb, k):
+    cand = np.arange(1, max(qb, 1), dtype=np.int64)
+    order = np.lexsort((-cand, -sc))                # ties: higher index
+    top = cand[order[:k]]
+    s_k = float(sc[order[k - 1]]) if 1 <= k <= len(cand) else math.nan
+    s_k1 = float(sc[order[k]]) if k + 1 <= len(cand) else math.nan
+    return np.unique(np.concatenate([[0], top, [qb]])), s_k, s_k1
+
+
+def _score_drop_last_candidate(qbar_row, khat, qb, B):
+    # the block just before the diagonal is wrongly left out
+    sc = _orig_score(qbar_row, khat, qb, B).copy()
+    if len(sc):
+        sc[-1] = -np.inf
+    return sc
+
+
+def _select_diagonal_uses_slot(sc, qb, k):
+    # the diagonal block wrongly counts against the top-k budget
+    return _orig_select(sc, qb, max(k - 1, 0) if qb >= 1 else k)
+
+
+def _score_mean_pool(qbar_row, khat, qb, B):
+    if qb < 2:
+        return np.zeros(0, dtype=F32)
+    dots = khat[B:qb * B] @ qbar_row
+    return dots.reshape(qb - 1, B).mean(axis=1).astype(F32)
+
+
+def _score_shifted_block(qbar_row, khat, qb, B):
+    if qb < 2:
+        return np.zeros(0, dtype=F32)
+    dots = khat[B - 1:qb * B - 1] @ qbar_row        # block edge off by one
+    return dots.reshape(qb - 1, B).max(axis=1)
+
+
+def _project_keys_with_pq_transposed(k_g, p_k):
+    return (k_g @ p_k.T[::-1, ::-1].T).astype(F32)  # reversed coordinates
+
+
+def _qmeans_last_row_only(q_h, p_q, B):
+    S = q_h.shape[0]
+    n_b = -(-S // B)
+    qt = q_h @ p_q.T
+    return np.stack([qt[min(S, (b + 1) * B) - 1] for b in range(n_b)]) \
+        .astype(F32)
+
+
+def _attend_no_scale(q_rows, k_keys, v_keys, member, scale):
+    return _orig_attend(q_rows, k_keys, v_keys, member, 1.0)
+
+
+def _attend_drop_max_row(q_rows, k_keys, v_keys, member, scale):
+    member = member.copy()
+    for r in range(member.shape[0]):            # drops the last key of a row
+        idx = np.nonzero(member[r])[0]
+        if len(idx) > 1:
+            member[r, idx[-1]] = False
+    return _orig_attend(q_rows, k_keys, v_keys, member, scale)
+
+
+def _retrieval_keys_no_causal(rows, sel, B, S):
+    union, _ = _orig_ret_keys(rows, sel, B, S)
+    return union, np.ones((len(rows), len(union)), dtype=bool)
+
+
+def _decode_select_no_recent(q_tilde, cents, n_b, k, n_recent):
+    sel, a, b = _orig_dec_select(q_tilde, cents, n_b, k, n_recent)
+    return sel[sel < n_b - 1] if n_b > 1 else sel, a, b
+
+
+_orig_attend = op.attend
+_orig_score = op.block_score_row
+_orig_select = op.select_row
+_orig_ret_keys = op.retrieval_block_keys
+_orig_dec_select = od.decode_select
+
+MUTATIONS = [
+    (op, "swa_block_keys", _swa_off_by_one),
+    (op, "select_row", _select_smallest),
+    (op, "select_row", _select_high_index_ties),
+    (op, "block_score_row", _score_drop_last_candidate),
+    (op, "select_row", _select_diagonal_uses_slot),
+    (op, "block_score_row", _score_mean_pool),
+    (op, "block_score_row", _score_shifted_block),
+    (op, "project_keys", _project_keys_with_pq_transposed),
+    (op, "query_block_means", _qmeans_last_row_only),
+    (op, "attend", _attend_no_scale),
+    (op, "attend", _attend_drop_max_row),
+    (op, "retrieval_block_keys", _retrieval_keys_no_causal),
+    (od, "decode_select", _decode_select_no_recent),
+]
+
+PIN_TESTS = [
+    lambda: pins.test_full_coverage_equals_dense_causal(300),
+    pins.test_window_one_returns_v_exactly,
+    pins.test_swa_band_matches_masked_sdpa,
+    pins.test_block_sparse_matches_masked_sdpa,
+    pins.test_identity_projection_picks_true_top_blocks,
+    pins.test_random_projection_selection_brute_force,
+    pins.test_planted_selection_known_by_construction,
+    pins.test_indexer_linearity_and_centroids,
+    pins.test_decode_full_coverage_equals_last_row_of_dense,
+    pins.test_decode_window_is_last_w_tokens,
+    pins.test_decode_planted_selection,
+]
+
+
+@pytest.mark.parametrize("mod,name,fn", MUTATIONS,
+                         ids=[m[2].__name__ for m in MUTATIONS])
+def test_pins_reject_mutation(monkeypatch, mod, name, fn):
+    monkeypatch.setattr(mod, name, fn)
+    if mod is op and name == "attend":
+        monkeypatch.setattr(od, "attend", fn)
+    caught = 0
+    for t in PIN_TESTS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError, KeyError):
+            caught += 1
+            break
+    assert caught, f"no pin rejects mutation {fn.__name__}"
