@@ -1,0 +1,204 @@
+/*
+ * rtp.h - C ABI of the headwise hybrid attention library for MI355X (gfx950).
+ *
+ * What it computes (the pages are web articles, cited by title and section):
+ *
+ *  - "阿里Qwen3 RTPurbo：15%全量Attention长文本5倍压缩方案", section
+ *    "化繁为简，被低估的 SWA": each query head is fixed to one of two kinds. A
+ *    small share keeps long-range access; the rest ("streaming heads") use
+ *    causal sliding-window attention (SWA): query i attends keys
+ *    i - window < j <= i.
+ *  - "阿里RTPurboV2：Transformer再次崛起，百步训练实现10倍稀少把稳",
+ *    paragraph on the low-rank projector (D -> r = 16), and the aitop.news
+ *    summary of "Full Attention Strikes Back": long-range ("retrieval")
+ *    heads use a 16-dimensional indexer to guess which earlier tokens
+ *    matter, then run exact softmax attention only on that selected set.
+ *    This library's indexer rule: blocks of `block` tokens; the query block
+ *    qb scores every candidate key block 1 <= kb <= qb-1 by
+ *        sc(qb,kb) = max_{j in kb} ( mean_{i in qb} P_q q_i ) . ( P_k k_j ),
+ *    keeps the top_k candidates (ties: lower block index), and always adds
+ *    the sink block 0 and the diagonal block qb. Query i of block qb then
+ *    attends every key j <= i of the kept blocks.
+ *  - Same RTPurboV2 article, paragraphs on clustering in the low-rank space
+ *    and on the decode recipe: decode scores per-block key centroids
+ *    c_kb = mean_{j in kb} P_k k_j with the projected query, keeps the sink,
+ *    the last n_recent blocks and the top_k candidates, and attends exactly.
+ *
+ * Softmax everywhere: s_j = scale * q.k_j, lse = log sum_j exp(s_j),
+ * out = sum_j exp(s_j - lse) v_j, computed with fp32 accumulation.
+ *
+ * Conventions (every entry point):
+ *  - All tensors are dense, row-major, device memory owned by the caller.
+ *    bf16 tensors are passed as raw 16-bit storage (`const void*`).
+ *  - `is_retrieval` is a HOST array of Hq bytes (nonzero = retrieval head).
+ *    n_ret = number of nonzero entries. Projections p_q/p_k are fp32
+ *    [n_ret, r, d] device arrays for the retrieval heads in ascending head
+ *    order.
+ *  - GQA: query head h reads KV head h / (Hq / Hkv).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream). The library allocates no device memory: scratch space comes
+ *    from the caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned),
+ *    sized by the matching *_workspace_bytes query. Calls never synchronise.
+ *  - Arguments are validated on the host before anything is enqueued. On an
+ *    error nothing is launched, outputs are untouched, and a negative status
+ *    is returned; rtp_last_error() gives a thread-local message.
+ *  - Results are deterministic: no atomics take part in any reduction.
+ *  - Supported shapes: d = 128, block = 64, r a multiple of 16 in [16, 128],
+ *    Hq <= 128, Hq % Hkv == 0. S may be any size >= 0 (a ragged last block
+ *    is handled).
+ *  - Two calls that share a workspace must not overlap in time.
+ */
+#ifndef RTP_H
+#define RTP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define RTP_OK 0
+#define RTP_EINVAL (-1)       /* null pointer, negative or inconsistent size */
+#define RTP_EUNSUPPORTED (-2) /* d != 128, block != 64, bad r, Hq > 128 */
+#define RTP_EWORKSPACE (-3)   /* ws too small or not 256-byte aligned */
+#define RTP_EHIP (-4)         /* HIP runtime or launch error */
+
+typedef struct ihipStream_t* rtp_stream_t; /* hipStream_t */
+
+/* Human-readable name of a status code (static string). */
+const char* rtp_status_string(int status);
+/* Message of the last error on the calling thread ("" if none). */
+const char* rtp_last_error(void);
+/* Library version string. */
+const char* rtp_version(void);
+
+/* Workspace bytes needed by rtp_indexer_select / rtp_hybrid_attn_prefill
+ * for these sizes (0 on invalid arguments). */
+size_t rtp_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int r,
+                                   int block, int top_k);
+
+/*
+ * rtp_indexer_select - the retrieval-head indexer alone (project, score,
+ * select). Defined by the RTPurboV2 low-rank projector paragraph and the
+ * aitop.news indexer summary, with the block rule stated at the top.
+ *
+ *  q [Hq,S,d] bf16, k [Hkv,S,d] bf16           inputs (only retrieval heads
+ *                                               of q are read)
+ *  p_q, p_k [n_ret,r,d] fp32                    projections
+ *  sel [n_ret,n_b,top_k+2] int32   (out)        kept blocks per query block,
+ *                                               ascending, padded with -1
+ *  sel_count [n_ret,n_b] int32     (out)        number of kept blocks
+ *  kth_scores [n_ret,n_b,2] fp32   (out, may be NULL)
+ *        the k-th and (k+1)-th largest candidate scores (NaN when the row
+ *        has fewer candidates), for logging near-ties
+ *  centroids [n_ret,n_b,r] fp32    (out, may be NULL)
+ *        per-block mean of the projected keys P_k k_j
+ *  n_b = ceil(S / block). A row with no more candidates than top_k keeps
+ *  them all.
+ */
+int rtp_indexer_select(const void* q, const void* k, int S, int Hq, int Hkv,
+                       int d, const uint8_t* is_retrieval, const float* p_q,
+                       const float* p_k, int r, int block, int top_k,
+                       int32_t* sel, int32_t* sel_count, float* kth_scores,
+                       float* centroids, void* ws, size_t ws_bytes,
+                       rtp_stream_t stream);
+
+/*
+ * rtp_hybrid_attn_prefill - one layer of headwise hybrid attention over a
+ * whole sequence. Streaming heads: SWA with `window` (window >= S gives
+ * full causal attention). Retrieval heads: indexer selection, then exact
+ * attention on the kept blocks.
+ *
+ *  q [Hq,S,d], k/v [Hkv,S,d] bf16
+ *  scale            softmax scale; <= 0 means 1/sqrt(d)
+ *  sel_in, sel_count_in   (may both be NULL) a selection in the layout of
+ *        rtp_indexer_select; when given, the indexer is skipped and these
+ *        blocks are used (each row ascending, within 0..qb)
+ *  out [Hq,S,d] bf16 (out)        attention output, rounded to nearest even
+ *  lse [Hq,S] fp32 (out, may be NULL)   natural-log sum of exp of scaled
+ *                                        logits over the attended keys
+ *  sel_out, sel_count_out (out, may be NULL) the selection used
+ */
+int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
+                            int S, int Hq, int Hkv, int d,
+                            const uint8_t* is_retrieval, int window,
+                            const float* p_q, const float* p_k, int r,
+                            int block, int top_k, float scale,
+                            const int32_t* sel_in,
+                            const int32_t* sel_count_in, void* out,
+                            float* lse, int32_t* sel_out,
+                            int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                            rtp_stream_t stream);
+
+/* Workspace bytes for rtp_dense_attn_prefill. */
+size_t rtp_dense_workspace_bytes(int S, int Hq, int Hkv, int d);
+
+/*
+ * rtp_dense_attn_prefill - dense causal attention on the same tile engine:
+ * the full-attention baseline the pages compare against (FlashAttention-2
+ * in the aitop.news summary). Same layouts as rtp_hybrid_attn_prefill.
+ */
+int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
+                           int S, int Hq, int Hkv, int d, float scale,
+                           void* out, float* lse, void* ws, size_t ws_bytes,
+                           rtp_stream_t stream);
+
+/*
+ * rtp_build_centroids - decode-side key clustering (RTPurboV2, K-cache
+ * clustering): for every sequence b, retrieval head rho and FULL block kb
+ * (kb < cache_len[b] / block):
+ *     centroids[b,rho,kb,:] = mean_{j in kb} P_k[rho] k_cache[b,g,j,:]
+ * where g is the KV head of retrieval head rho. Entries of partial or
+ * absent blocks are left untouched.
+ *
+ *  k_cache [B,Hkv,Lmax,d] bf16; cache_len [B] int32 DEVICE array
+ *  (0 <= cache_len[b] <= Lmax); p_k [n_ret,r,d] fp32;
+ *  centroids [B,n_ret,Lmax/block,r] fp32 (out)
+ */
+int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
+                        int Lmax, int Hq, int Hkv, int d,
+                        const uint8_t* is_retrieval, const float* p_k, int r,
+                        int block, float* centroids, rtp_stream_t stream);
+
+/* Workspace bytes for rtp_hybrid_attn_decode. */
+size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
+                                  const uint8_t* is_retrieval, int r,
+                                  int block, int top_k, int n_recent);
+
+/*
+ * rtp_hybrid_attn_decode - one decode step for a batch of sequences
+ * (RTPurboV2 decode recipe: sparse retrieval heads via key clustering, SWA
+ * for streaming heads). The new token's K/V are already appended, so
+ * sequence b has L = cache_len[b] >= 1 tokens and the query sits at L-1.
+ *
+ *  Streaming head: attends keys max(0, L-window) .. L-1.
+ *  Retrieval head rho: n_b = ceil(L/block); q~ = P_q[rho] q; candidates
+ *    1 .. n_b-n_recent-1 scored by q~ . centroids[b,rho,kb]; keeps block 0,
+ *    the top_k candidates (ties: lower index) and blocks n_b-n_recent ..
+ *    n_b-1; attends every cached token of the kept blocks.
+ *
+ *  q [B,Hq,d] bf16; k_cache/v_cache [B,Hkv,Lmax,d] bf16;
+ *  cache_len [B] int32 DEVICE array (1 <= cache_len[b] <= Lmax);
+ *  p_q [n_ret,r,d] fp32; centroids [B,n_ret,Lmax/block,r] fp32 from
+ *  rtp_build_centroids;
+ *  out [B,Hq,d] bf16 (out); lse [B,Hq] fp32 (out, may be NULL);
+ *  sel_out [B,n_ret,top_k+1+n_recent] int32 (out, may be NULL): kept blocks
+ *  ascending, -1 padded.
+ */
+int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* cache_len,
+                           int B, int Lmax, int Hq, int Hkv, int d,
+                           const uint8_t* is_retrieval, int window,
+                           const float* p_q, const float* centroids, int r,
+                           int block, int top_k, int n_recent, float scale,
+                           void* out, float* lse, int32_t* sel_out, void* ws,
+                           size_t ws_bytes, rtp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTP_H */

@@ -1,0 +1,314 @@
+"""Headwise hybrid attention on MI355X (gfx950): Python binding of librtp.so.
+
+Streaming heads run causal sliding-window attention; retrieval heads use an
+r = 16 low-rank indexer to keep a few 64-token key blocks (sink, diagonal and
+the top-k by block score) and run exact softmax attention on them; decode
+scores per-block key centroids instead. All computation runs in the HIP
+library; this module only checks tensors and passes pointers, sizes and the
+current HIP stream through the C ABI declared in include/rtp.h. PyTorch is
+used for device memory and streams only.
+
+The library must be built (``python -m long_context_sparse_head_amd.build``);
+every call raises if it is missing. There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "load", "LIB_PATH", "RtpError", "prefill_workspace_bytes",
+    "dense_workspace_bytes", "decode_workspace_bytes", "indexer_select",
+    "hybrid_attn_prefill", "dense_attn_prefill", "build_centroids",
+    "hybrid_attn_decode", "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
+                        "librtp.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_U8P = ctypes.POINTER(ctypes.c_uint8)
+
+_SIGS = {
+    "rtp_status_string": (ctypes.c_char_p, [_I]),
+    "rtp_last_error": (ctypes.c_char_p, []),
+    "rtp_version": (ctypes.c_char_p, []),
+    "rtp_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I, _U8P, _I, _I, _I]),
+    "rtp_dense_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "rtp_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _U8P, _I, _I, _I,
+                                        _I]),
+    "rtp_indexer_select": (_I, [_P, _P, _I, _I, _I, _I, _U8P, _P, _P, _I, _I,
+                                _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "rtp_hybrid_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U8P, _I, _P,
+                                     _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                     _P, _P, _Z, _P]),
+    "rtp_dense_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _P, _P,
+                                    _P, _Z, _P]),
+    "rtp_build_centroids": (_I, [_P, _P, _I, _I, _I, _I, _I, _U8P, _P, _I, _I,
+                                 _P, _P]),
+    "rtp_hybrid_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _U8P,
+                                    _I, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
+                                    _P, _Z, _P]),
+}
+
+
+class RtpError(RuntimeError):
+    pass
+
+
+def load():
+    """Load librtp.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RtpError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m long_context_sparse_head_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return load().rtp_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        lib = load()
+        raise RtpError(f"{what}: {lib.rtp_status_string(status).decode()}: "
+                       f"{lib.rtp_last_error().decode()}")
+
+
+def _mask(is_retrieval, Hq: int):
+    m = np.ascontiguousarray(np.asarray(is_retrieval, dtype=np.uint8))
+    if m.shape != (Hq,):
+        raise ValueError(f"is_retrieval must have shape ({Hq},)")
+    return m, m.ctypes.data_as(_U8P)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws")
+        if ws.numel() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def prefill_workspace_bytes(S: int, Hq: int, Hkv: int, is_retrieval,
+                            r: int = 16, top_k: int = 64, d: int = 128,
+                            block: int = 64) -> int:
+    m, mp = _mask(is_retrieval, Hq)
+    return int(load().rtp_prefill_workspace_bytes(S, Hq, Hkv, d, mp, r, block,
+                                                  top_k))
+
+
+def dense_workspace_bytes(S: int, Hq: int, Hkv: int, d: int = 128) -> int:
+    return int(load().rtp_dense_workspace_bytes(S, Hq, Hkv, d))
+
+
+def decode_workspace_bytes(B: int, Lmax: int, Hq: int, Hkv: int, is_retrieval,
+                           r: int = 16, top_k: int = 64, n_recent: int = 2,
+                           d: int = 128, block: int = 64) -> int:
+    m, mp = _mask(is_retrieval, Hq)
+    return int(load().rtp_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, mp, r,
+                                                 block, top_k, n_recent))
+
+
+def _proj(p, n_ret, r, d, name):
+    if n_ret == 0:
+        return None
+    return _dev(p, torch.float32, name, (n_ret, r, d))
+
+
+def indexer_select(q, k, is_retrieval, p_q, p_k, top_k: int, r: int = 16,
+                   block: int = 64, kth: bool = False,
+                   centroids: bool = False, ws=None):
+    """Returns (sel [n_ret,n_b,top_k+2], sel_count [n_ret,n_b],
+    kth [n_ret,n_b,2] or None, centroids [n_ret,n_b,r] or None)."""
+    lib = load()
+    Hq, S, d = q.shape
+    Hkv = k.shape[0]
+    _dev(q, torch.bfloat16, "q", (Hq, S, d))
+    _dev(k, torch.bfloat16, "k", (Hkv, S, d))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    _proj(p_q, n_ret, r, d, "p_q")
+    _proj(p_k, n_ret, r, d, "p_k")
+    n_b = -(-S // block)
+    dev = q.device
+    sel = torch.full((n_ret, n_b, top_k + 2), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((n_ret, n_b), dtype=torch.int32, device=dev)
+    kt = torch.empty((n_ret, n_b, 2), dtype=torch.float32, device=dev) \
+        if kth else None
+    ce = torch.empty((n_ret, n_b, r), dtype=torch.float32, device=dev) \
+        if centroids else None
+    nb = lib.rtp_prefill_workspace_bytes(S, Hq, Hkv, d, mp, r, block, top_k)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_indexer_select(
+        _ptr(q), _ptr(k), S, Hq, Hkv, d, mp, _ptr(p_q), _ptr(p_k), r, block,
+        top_k, _ptr(sel), _ptr(cnt), _ptr(kt), _ptr(ce), _ptr(w), w.numel(),
+        _stream(dev)), "rtp_indexer_select")
+    return sel, cnt, kt, ce
+
+
+def hybrid_attn_prefill(q, k, v, is_retrieval, window: int, p_q, p_k,
+                        top_k: int, r: int = 16, block: int = 64,
+                        scale: float = 0.0, sel=None, sel_count=None,
+                        want_lse: bool = False, want_sel: bool = False,
+                        ws=None, out=None):
+    """One layer of hybrid prefill. Returns out, or a tuple
+    (out, lse, sel, sel_count) with None for the parts not asked for."""
+    lib = load()
+    Hq, S, d = q.shape
+    Hkv = k.shape[0]
+    _dev(q, torch.bfloat16, "q", (Hq, S, d))
+    _dev(k, torch.bfloat16, "k", (Hkv, S, d))
+    _dev(v, torch.bfloat16, "v", (Hkv, S, d))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    n_b = -(-S // block)
+    dev = q.device
+    if sel is not None:
+        _dev(sel, torch.int32, "sel", (n_ret, n_b, top_k + 2))
+        _dev(sel_count, torch.int32, "sel_count", (n_ret, n_b))
+    else:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _proj(p_k, n_ret, r, d, "p_k")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.bfloat16, "out", (Hq, S, d))
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    so = co = None
+    if want_sel:
+        so = torch.full((n_ret, n_b, top_k + 2), -1, dtype=torch.int32,
+                        device=dev)
+        co = torch.zeros((n_ret, n_b), dtype=torch.int32, device=dev)
+    nb = lib.rtp_prefill_workspace_bytes(S, Hq, Hkv, d, mp, r, block, top_k)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_hybrid_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), S, Hq, Hkv, d, mp, int(window), _ptr(p_q),
+        _ptr(p_k), r, block, top_k, float(scale), _ptr(sel), _ptr(sel_count),
+        _ptr(out), _ptr(lse), _ptr(so), _ptr(co), _ptr(w), w.numel(),
+        _stream(dev)), "rtp_hybrid_attn_prefill")
+    if want_lse or want_sel:
+        return out, lse, so, co
+    return out
+
+
+def dense_attn_prefill(q, k, v, scale: float = 0.0, want_lse: bool = False,
+                       ws=None, out=None):
+    """Dense causal attention on the same tile engine (baseline)."""
+    lib = load()
+    Hq, S, d = q.shape
+    Hkv = k.shape[0]
+    _dev(q, torch.bfloat16, "q", (Hq, S, d))
+    _dev(k, torch.bfloat16, "k", (Hkv, S, d))
+    _dev(v, torch.bfloat16, "v", (Hkv, S, d))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    w = _workspace(lib.rtp_dense_workspace_bytes(S, Hq, Hkv, d), dev, ws)
+    _check(lib.rtp_dense_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), S, Hq, Hkv, d, float(scale), _ptr(out),
+        _ptr(lse), _ptr(w), w.numel(), _stream(dev)), "rtp_dense_attn_prefill")
+    return (out, lse) if want_lse else out
+
+
+def build_centroids(k_cache, cache_len, is_retrieval, p_k, r: int = 16,
+                    block: int = 64, out=None):
+    """Per-block key centroids [B,n_ret,Lmax/block,r] (full blocks only)."""
+    lib = load()
+    B, Hkv, Lmax, d = k_cache.shape
+    Hq = len(is_retrieval)
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    _proj(p_k, n_ret, r, d, "p_k")
+    if out is None:
+        out = torch.zeros((B, n_ret, Lmax // block, r), dtype=torch.float32,
+                          device=k_cache.device)
+    _check(lib.rtp_build_centroids(
+        _ptr(k_cache), _ptr(cache_len), B, Lmax, Hq, Hkv, d, mp, _ptr(p_k), r,
+        block, _ptr(out), _stream(k_cache.device)), "rtp_build_centroids")
+    return out
+
+
+def hybrid_attn_decode(q, k_cache, v_cache, cache_len, is_retrieval,
+                       window: int, p_q, centroids, top_k: int,
+                       n_recent: int = 2, r: int = 16, block: int = 64,
+                       scale: float = 0.0, want_lse: bool = False,
+                       want_sel: bool = False, ws=None, out=None):
+    """One decode step. Returns out, or (out, lse, sel) when asked."""
+    lib = load()
+    B, Hq, d = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    _dev(q, torch.bfloat16, "q", (B, Hq, d))
+    _dev(k_cache, torch.bfloat16, "k_cache", (B, Hkv, Lmax, d))
+    _dev(v_cache, torch.bfloat16, "v_cache", (B, Hkv, Lmax, d))
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    if n_ret:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, Lmax // block, r))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    so = torch.full((B, n_ret, top_k + 1 + n_recent), -1, dtype=torch.int32,
+                    device=dev) if want_sel else None
+    nb = lib.rtp_decode_workspace_bytes(B, Lmax, Hq, Hkv, d, mp, r, block,
+                                        top_k, n_recent)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_hybrid_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), B, Lmax, Hq,
+        Hkv, d, mp, int(window), _ptr(p_q), _ptr(centroids), r, block, top_k,
+        n_recent, float(scale), _ptr(out), _ptr(lse), _ptr(so), _ptr(w),
+        w.numel(), _stream(dev)), "rtp_hybrid_attn_decode")
+    if want_lse or want_sel:
+        return out, lse, so
+    return out

@@ -1,0 +1,434 @@
+// C ABI of the hybrid attention library: argument validation, workspace
+// layout and kernel sequencing. Declarations and semantics: include/rtp.h.
+#include "common.h"
+#include "../../include/rtp.h"
+
+#include <cmath>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return RTP_EHIP;
+}
+
+struct HeadInfo {
+  int n_ret = 0;
+  std::vector<uint8_t> ret_heads;  // query head of each retrieval index
+};
+
+HeadInfo scan_mask(const uint8_t* m, int Hq) {
+  HeadInfo hi;
+  for (int h = 0; h < Hq; ++h)
+    if (m[h]) {
+      hi.ret_heads.push_back((uint8_t)h);
+      ++hi.n_ret;
+    }
+  return hi;
+}
+
+// Shape checks shared by every entry point.
+int check_shape(int S, int Hq, int Hkv, int d) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0)
+    return fail(RTP_EINVAL, "sizes must satisfy S >= 0, Hq > 0, Hkv > 0");
+  if (Hq % Hkv)
+    return fail(RTP_EINVAL, "Hq must be a multiple of Hkv");
+  if (d != rtp::kD) return fail(RTP_EUNSUPPORTED, "only d = 128 is supported");
+  if (Hq > rtp::kMaxHeads)
+    return fail(RTP_EUNSUPPORTED, "at most 128 query heads are supported");
+  return RTP_OK;
+}
+
+int check_indexer(int n_ret, int r, int block, int top_k) {
+  if (block != rtp::kBlk) return fail(RTP_EUNSUPPORTED, "only block = 64 is supported");
+  if (top_k < 0) return fail(RTP_EINVAL, "top_k must be >= 0");
+  if (n_ret > 0 && (r < 16 || r > 128 || r % 16))
+    return fail(RTP_EUNSUPPORTED, "r must be a multiple of 16 in [16, 128]");
+  return RTP_OK;
+}
+
+struct PrefillLayout {
+  size_t vt, khi, klo, qhi, qlo, sc, sel, cnt, total;
+};
+
+PrefillLayout prefill_layout(int S, int Hkv, int n_ret, int r, int top_k) {
+  using rtp::align256;
+  const size_t n_b = (size_t)(S + 63) / 64, S_pad = n_b * 64;
+  PrefillLayout L;
+  size_t off = 0;
+  L.vt = off;  off += align256((size_t)Hkv * rtp::kD * S_pad * 2);
+  L.khi = off; off += align256((size_t)n_ret * S_pad * r * 2);
+  L.klo = off; off += align256((size_t)n_ret * S_pad * r * 2);
+  L.qhi = off; off += align256((size_t)n_ret * n_b * r * 2);
+  L.qlo = off; off += align256((size_t)n_ret * n_b * r * 2);
+  L.sc = off;  off += align256((size_t)n_ret * rtp::tri_rows((int64_t)n_b) * 4);
+  L.sel = off; off += align256((size_t)n_ret * n_b * (top_k + 2) * 4);
+  L.cnt = off; off += align256((size_t)n_ret * n_b * 4);
+  L.total = off;
+  return L;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return RTP_OK;
+  if (!ws || ws_bytes < need)
+    return fail(RTP_EWORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                    " bytes, got " + std::to_string(ws_bytes));
+  if (reinterpret_cast<uintptr_t>(ws) & 255)
+    return fail(RTP_EWORKSPACE, "workspace must be 256-byte aligned");
+  return RTP_OK;
+}
+
+float resolve_scale(float scale, int d) {
+  return scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+}
+
+// Work items of one query block: window heads in pairs of one KV group
+// (they share every key tile), leftovers and retrieval heads alone.
+rtp::AttnItems make_items(int Hq, int G, const uint8_t* is_ret, bool pair) {
+  rtp::AttnItems it;
+  it.n = 0;
+  const int Hkv = Hq / G;
+  int rho = 0;
+  std::vector<int> rho_of(Hq, 0);
+  for (int h = 0; h < Hq; ++h)
+    if (is_ret && is_ret[h]) rho_of[h] = rho++;
+  for (int g = 0; g < Hkv; ++g) {
+    std::vector<int> swa;
+    for (int h = g * G; h < (g + 1) * G; ++h)
+      if (!(is_ret && is_ret[h])) swa.push_back(h);
+    size_t i = 0;
+    if (pair)
+      for (; i + 1 < swa.size(); i += 2)
+        it.desc[it.n++] = 0u | ((uint32_t)swa[i] << 8) | ((uint32_t)swa[i + 1] << 16);
+    for (; i < swa.size(); ++i) it.desc[it.n++] = 1u | ((uint32_t)swa[i] << 8);
+    for (int h = g * G; h < (g + 1) * G; ++h)
+      if (is_ret && is_ret[h])
+        it.desc[it.n++] = 2u | ((uint32_t)h << 8) | ((uint32_t)rho_of[h] << 24);
+  }
+  return it;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rtp_status_string(int s) {
+  switch (s) {
+    case RTP_OK: return "ok";
+    case RTP_EINVAL: return "invalid argument";
+    case RTP_EUNSUPPORTED: return "unsupported configuration";
+    case RTP_EWORKSPACE: return "workspace too small or misaligned";
+    case RTP_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rtp_last_error(void) { return g_err.c_str(); }
+
+const char* rtp_version(void) { return "rtp-hybrid-attn 0.1 (gfx950)"; }
+
+size_t rtp_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int r,
+                                   int block, int top_k) {
+  if (check_shape(S, Hq, Hkv, d) || !is_retrieval) return 0;
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
+  return prefill_layout(S, Hkv, hi.n_ret, r, top_k).total;
+}
+
+size_t rtp_dense_workspace_bytes(int S, int Hq, int Hkv, int d) {
+  if (check_shape(S, Hq, Hkv, d)) return 0;
+  return prefill_layout(S, Hkv, 0, 16, 0).total;
+}
+
+static int run_indexer(const void* q, const void* k, int S, int Hq, int Hkv,
+                       const HeadInfo& hi, const float* p_q, const float* p_k,
+                       int r, int top_k, int32_t* sel, int32_t* sel_count,
+                       float* kth, float* cent, char* ws,
+                       const PrefillLayout& L, hipStream_t st) {
+  rtp::IndexerLaunch a;
+  a.q = static_cast<const rtp::u16*>(q);
+  a.k = static_cast<const rtp::u16*>(k);
+  a.p_q = p_q;
+  a.p_k = p_k;
+  a.S = S;
+  a.n_b = (S + 63) / 64;
+  a.S_pad = a.n_b * 64;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_ret = hi.n_ret;
+  a.r = r;
+  a.top_k = top_k;
+  a.ret_heads = hi.ret_heads.data();
+  a.khi = reinterpret_cast<rtp::u16*>(ws + L.khi);
+  a.klo = reinterpret_cast<rtp::u16*>(ws + L.klo);
+  a.qhi = reinterpret_cast<rtp::u16*>(ws + L.qhi);
+  a.qlo = reinterpret_cast<rtp::u16*>(ws + L.qlo);
+  a.scores = reinterpret_cast<float*>(ws + L.sc);
+  a.sel = sel;
+  a.sel_cnt = sel_count;
+  a.kth = kth;
+  a.centroids = cent;
+  hipError_t e = rtp::launch_indexer(a, st);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  return RTP_OK;
+}
+
+int rtp_indexer_select(const void* q, const void* k, int S, int Hq, int Hkv,
+                       int d, const uint8_t* is_retrieval, const float* p_q,
+                       const float* p_k, int r, int block, int top_k,
+                       int32_t* sel, int32_t* sel_count, float* kth_scores,
+                       float* centroids, void* ws, size_t ws_bytes,
+                       rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(S, Hq, Hkv, d)) return e;
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
+  if (S == 0 || hi.n_ret == 0) return RTP_OK;
+  if (!q || !k || !p_q || !p_k || !sel || !sel_count)
+    return fail(RTP_EINVAL, "q, k, p_q, p_k, sel and sel_count must be non-NULL");
+  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k);
+  if (int e = check_ws(ws, ws_bytes, L.total)) return e;
+  return run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, sel, sel_count,
+                     kth_scores, centroids, static_cast<char*>(ws), L,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
+                            int S, int Hq, int Hkv, int d,
+                            const uint8_t* is_retrieval, int window,
+                            const float* p_q, const float* p_k, int r,
+                            int block, int top_k, float scale,
+                            const int32_t* sel_in,
+                            const int32_t* sel_count_in, void* out,
+                            float* lse, int32_t* sel_out,
+                            int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                            rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(S, Hq, Hkv, d)) return e;
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  if (window < 1) return fail(RTP_EINVAL, "window must be >= 1");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
+  if ((sel_in == nullptr) != (sel_count_in == nullptr))
+    return fail(RTP_EINVAL, "sel_in and sel_count_in must both be given or both NULL");
+  if ((sel_out == nullptr) != (sel_count_out == nullptr))
+    return fail(RTP_EINVAL, "sel_out and sel_count_out must both be given or both NULL");
+  if (S == 0) return RTP_OK;
+  if (!q || !k || !v || !out) return fail(RTP_EINVAL, "q, k, v and out must be non-NULL");
+  if (hi.n_ret > 0 && !sel_in && (!p_q || !p_k))
+    return fail(RTP_EINVAL, "p_q and p_k must be non-NULL when retrieval heads select");
+  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k);
+  if (int e = check_ws(ws, ws_bytes, L.total)) return e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const int n_b = (S + 63) / 64, S_pad = n_b * 64;
+
+  const int32_t* sel = sel_in;
+  const int32_t* cnt = sel_count_in;
+  if (hi.n_ret > 0 && !sel_in) {
+    int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
+    int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
+    if (int e = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
+                            nullptr, nullptr, w, L, st))
+      return e;
+    sel = s;
+    cnt = c;
+  } else if (hi.n_ret > 0 && sel_out) {
+    const size_t n = (size_t)hi.n_ret * n_b;
+    hipError_t e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
+                                  hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sel_count_out, sel_count_in, n * 4,
+                         hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "selection copy");
+  }
+
+  rtp::u16* vt = reinterpret_cast<rtp::u16*>(w + L.vt);
+  hipError_t e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt,
+                                         Hkv, S, S_pad, st);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  rtp::AttnLaunch a;
+  a.q = static_cast<const rtp::u16*>(q);
+  a.k = static_cast<const rtp::u16*>(k);
+  a.vt = vt;
+  a.out = static_cast<rtp::u16*>(out);
+  a.lse = lse;
+  a.sel = sel;
+  a.sel_cnt = cnt;
+  a.sel_stride = top_k + 2;
+  a.S = S;
+  a.S_pad = S_pad;
+  a.n_b = n_b;
+  a.G = Hq / Hkv;
+  a.window = window;
+  a.scale = resolve_scale(scale, d);
+  const rtp::AttnItems items = make_items(Hq, a.G, is_retrieval, true);
+  e = rtp::launch_attention(a, items, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return RTP_OK;
+}
+
+int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
+                           int S, int Hq, int Hkv, int d, float scale,
+                           void* out, float* lse, void* ws, size_t ws_bytes,
+                           rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(S, Hq, Hkv, d)) return e;
+  if (S == 0) return RTP_OK;
+  if (!q || !k || !v || !out) return fail(RTP_EINVAL, "q, k, v and out must be non-NULL");
+  const PrefillLayout L = prefill_layout(S, Hkv, 0, 16, 0);
+  if (int e = check_ws(ws, ws_bytes, L.total)) return e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const int n_b = (S + 63) / 64, S_pad = n_b * 64;
+  rtp::u16* vt = reinterpret_cast<rtp::u16*>(w + L.vt);
+  hipError_t e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt,
+                                         Hkv, S, S_pad, st);
+  if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  rtp::AttnLaunch a;
+  a.q = static_cast<const rtp::u16*>(q);
+  a.k = static_cast<const rtp::u16*>(k);
+  a.vt = vt;
+  a.out = static_cast<rtp::u16*>(out);
+  a.lse = lse;
+  a.sel = nullptr;
+  a.sel_cnt = nullptr;
+  a.sel_stride = 0;
+  a.S = S;
+  a.S_pad = S_pad;
+  a.n_b = n_b;
+  a.G = Hq / Hkv;
+  a.window = S;  // window >= S: full causal attention
+  a.scale = resolve_scale(scale, d);
+  const rtp::AttnItems items = make_items(Hq, a.G, nullptr, true);
+  e = rtp::launch_attention(a, items, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return RTP_OK;
+}
+
+int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
+                        int Lmax, int Hq, int Hkv, int d,
+                        const uint8_t* is_retrieval, const float* p_k, int r,
+                        int block, float* centroids, rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(0, Hq, Hkv, d)) return e;
+  if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, 0)) return e;
+  if (B == 0 || hi.n_ret == 0 || Lmax < 64) return RTP_OK;
+  if (!k_cache || !cache_len || !p_k || !centroids)
+    return fail(RTP_EINVAL, "k_cache, cache_len, p_k and centroids must be non-NULL");
+  hipError_t e = rtp::launch_build_centroids(
+      static_cast<const rtp::u16*>(k_cache), cache_len, p_k, centroids, B, Lmax,
+      Hkv, hi.n_ret, r, Hq / Hkv, hi.ret_heads.data(),
+      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "centroid launch");
+  return RTP_OK;
+}
+
+static const int kDecSplit = 16;
+
+struct DecodeLayout {
+  size_t cs, sel, po, pml, total;
+};
+
+static DecodeLayout decode_layout(int B, int Lmax, int Hq, int n_ret, int top_k,
+                                  int n_recent) {
+  using rtp::align256;
+  const size_t nbmax = (size_t)Lmax / 64, width = (size_t)top_k + 1 + n_recent;
+  DecodeLayout L;
+  size_t off = 0;
+  L.cs = off;  off += align256((size_t)B * n_ret * nbmax * 4);
+  L.sel = off; off += align256((size_t)B * n_ret * (width + 1) * 4);
+  L.po = off;  off += align256((size_t)B * Hq * kDecSplit * rtp::kD * 4);
+  L.pml = off; off += align256((size_t)B * Hq * kDecSplit * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
+                                  const uint8_t* is_retrieval, int r,
+                                  int block, int top_k, int n_recent) {
+  if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0 ||
+      n_recent < 0)
+    return 0;
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
+  return decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent).total;
+}
+
+int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* cache_len,
+                           int B, int Lmax, int Hq, int Hkv, int d,
+                           const uint8_t* is_retrieval, int window,
+                           const float* p_q, const float* centroids, int r,
+                           int block, int top_k, int n_recent, float scale,
+                           void* out, float* lse, int32_t* sel_out, void* ws,
+                           size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(0, Hq, Hkv, d)) return e;
+  if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  if (window < 1) return fail(RTP_EINVAL, "window must be >= 1");
+  if (n_recent < 0) return fail(RTP_EINVAL, "n_recent must be >= 0");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
+  if (B == 0) return RTP_OK;
+  if (!q || !k_cache || !v_cache || !cache_len || !out)
+    return fail(RTP_EINVAL, "q, k_cache, v_cache, cache_len and out must be non-NULL");
+  if (hi.n_ret > 0 && (!p_q || !centroids))
+    return fail(RTP_EINVAL, "p_q and centroids must be non-NULL with retrieval heads");
+  const DecodeLayout L = decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent);
+  if (int e = check_ws(ws, ws_bytes, L.total)) return e;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  rtp::DecodeLaunch a;
+  a.q = static_cast<const rtp::u16*>(q);
+  a.kc = static_cast<const rtp::u16*>(k_cache);
+  a.vc = static_cast<const rtp::u16*>(v_cache);
+  a.cache_len = cache_len;
+  a.p_q = p_q;
+  a.cent = centroids;
+  a.B = B;
+  a.Lmax = Lmax;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_ret = hi.n_ret;
+  a.r = r;
+  a.window = window;
+  a.top_k = top_k;
+  a.n_recent = n_recent;
+  a.n_split = kDecSplit;
+  a.scale = resolve_scale(scale, d);
+  a.ret_heads = hi.ret_heads.data();
+  a.is_ret = is_retrieval;
+  a.out = static_cast<rtp::u16*>(out);
+  a.lse = lse;
+  a.sel = reinterpret_cast<int32_t*>(w + L.sel);
+  a.cscores = reinterpret_cast<float*>(w + L.cs);
+  a.part_o = reinterpret_cast<float*>(w + L.po);
+  a.part_ml = reinterpret_cast<float*>(w + L.pml);
+  hipError_t e = rtp::launch_decode(a, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (sel_out && hi.n_ret > 0) {
+    const size_t width = (size_t)top_k + 1 + n_recent;
+    e = hipMemcpyAsync(sel_out, a.sel, (size_t)B * hi.n_ret * width * 4,
+                       hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "selection copy");
+  }
+  return RTP_OK;
+}
+
+}  // extern "C"

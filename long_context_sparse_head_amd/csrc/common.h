@@ -1,0 +1,91 @@
+// Shared device helpers and internal launcher declarations (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace rtp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr int kD = 128;      // head dim
+constexpr int kBlk = 64;     // indexer block = attention key tile
+constexpr int kMaxHeads = 128;
+
+// MFMA lane layouts on gfx950 (checked on hardware against a CPU matmul):
+//  v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+e] and
+//  B[8*(l/32)+e][l%32] (e = 0..7); accumulator element i of lane l is
+//  C[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(u16 b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ u16 f2bf(float f) {  // round to nearest even
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(u16, b);
+}
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return the launch status.
+
+struct AttnItems {
+  // One entry per work item of a query block: bits 0-1 kind (0 = SWA head
+  // pair, 1 = single SWA head, 2 = single retrieval head), bits 8-15 head a,
+  // bits 16-23 head b, bits 24-31 retrieval index of head a.
+  uint32_t desc[kMaxHeads];
+  int n;
+};
+
+struct AttnLaunch {
+  const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
+  const int32_t* sel; const int32_t* sel_cnt; int sel_stride;
+  int S, S_pad, n_b, G, window;
+  float scale;
+};
+
+hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
+                              hipStream_t st);
+hipError_t launch_attention(const AttnLaunch& a, const AttnItems& items,
+                            hipStream_t st);
+
+struct IndexerLaunch {
+  const u16* q; const u16* k; const float* p_q; const float* p_k;
+  int S, S_pad, n_b, Hq, Hkv, n_ret, r, top_k;
+  const uint8_t* ret_heads;  // host: query head of each retrieval index
+  u16* khi; u16* klo; u16* qhi; u16* qlo; float* scores;
+  int32_t* sel; int32_t* sel_cnt; float* kth; float* centroids;
+};
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
+
+struct DecodeLaunch {
+  const u16* q; const u16* kc; const u16* vc; const int32_t* cache_len;
+  const float* p_q; const float* cent;
+  int B, Lmax, Hq, Hkv, n_ret, r, window, top_k, n_recent, n_split;
+  float scale;
+  const uint8_t* ret_heads;  // host
+  const uint8_t* is_ret;     // host [Hq]
+  u16* out; float* lse; int32_t* sel; float* cscores; float* part_o;
+  float* part_ml;
+};
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st);
+
+hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
+                                  const float* p_k, float* cent, int B,
+                                  int Lmax, int Hkv, int n_ret, int r, int G,
+                                  const uint8_t* ret_heads, hipStream_t st);
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline int64_t tri_rows(int64_t n_b) {  // candidates of rows 2..n_b-1
+  return n_b >= 3 ? (n_b - 2) * (n_b - 1) / 2 : 0;
+}
+
+}  // namespace rtp

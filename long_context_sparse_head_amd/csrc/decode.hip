@@ -1,0 +1,429 @@
+// Hybrid decode for gfx950: block-centroid selection for retrieval heads,
+// sliding window for streaming heads, exact split-K attention, LSE merge.
+//
+// What it computes (RTPurboV2 article: keys cluster in the low-rank space, so
+// whole groups of unrelated tokens can be skipped; for the Qwen3-Coder model
+// the K cache is clustered at prefill and decode runs sparsely on the
+// retrieval heads while the other heads keep an SWA window). This library's
+// reading: groups are contiguous 64-token blocks with centroid
+// c_kb = mean_{j in kb} P_k k_j; the projected query scores the candidates
+// 1 .. n_b-n_recent-1; the sink block, the top_k candidates and the last
+// n_recent blocks are attended exactly.
+//
+// Decode is bound by HBM bandwidth: every key/value byte is read once. The
+// window heads of one KV group share one pass over the window (up to 8 heads
+// per pass, GQA), retrieval heads gather their own blocks, and the keys of a
+// (sequence, unit) are split over many workgroups whose partial softmax
+// states are merged by log-sum-exp.
+#include "common.h"
+#include "select.h"
+
+namespace rtp {
+
+constexpr int kDecMaxUnitHeads = 8;
+
+// ---------------------------------------------------------------- centroids
+struct CentArgs {
+  int Hkv, Lmax, n_ret, r, nbmax;
+  uint8_t kvh_of_rho[kMaxHeads];
+};
+
+// grid (nbmax, n_ret, B), one wave: mean of the block's keys, then projected
+// (equal to the mean of the projected keys by linearity). Full blocks only.
+__global__ __launch_bounds__(64) void build_centroids_kernel(
+    const u16* __restrict__ kc, const int32_t* __restrict__ cache_len,
+    const float* __restrict__ p_k, const CentArgs ca, float* __restrict__ cent) {
+  __shared__ float mean[kD];
+  const int kb = blockIdx.x, rho = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  int L = cache_len[b];
+  L = L < 0 ? 0 : (L > ca.Lmax ? ca.Lmax : L);
+  if ((kb + 1) * 64 > L) return;
+  const int g = ca.kvh_of_rho[rho];
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(
+      kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD) + lane;
+  float s0 = 0.f, s1 = 0.f;
+  for (int i = 0; i < 64; ++i) {
+    const uint32_t w = rows[(size_t)i * (kD / 2)];
+    s0 += __uint_as_float(w << 16);
+    s1 += __uint_as_float(w & 0xffff0000u);
+  }
+  mean[2 * lane] = s0 * (1.f / 64.f);
+  mean[2 * lane + 1] = s1 * (1.f / 64.f);
+  __syncthreads();
+  for (int rr = lane; rr < ca.r; rr += 64) {
+    const float* prow = p_k + ((size_t)rho * ca.r + rr) * kD;
+    float acc = 0.f;
+    for (int d = 0; d < kD; ++d) acc = fmaf(prow[d], mean[d], acc);
+    cent[(((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r + rr] = acc;
+  }
+}
+
+hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
+                                  const float* p_k, float* cent, int B,
+                                  int Lmax, int Hkv, int n_ret, int r, int G,
+                                  const uint8_t* ret_heads, hipStream_t st) {
+  const int nbmax = Lmax / 64;
+  if (B == 0 || n_ret == 0 || nbmax == 0) return hipSuccess;
+  CentArgs ca;
+  ca.Hkv = Hkv;
+  ca.Lmax = Lmax;
+  ca.n_ret = n_ret;
+  ca.r = r;
+  ca.nbmax = nbmax;
+  for (int i = 0; i < kMaxHeads; ++i)
+    ca.kvh_of_rho[i] = i < n_ret ? ret_heads[i] / G : 0;
+  hipLaunchKernelGGL(build_centroids_kernel, dim3(nbmax, n_ret, B), dim3(64), 0,
+                     st, kc, cache_len, p_k, ca, cent);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- block choice
+struct DecSelArgs {
+  int Hq, Lmax, n_ret, r, nbmax, top_k, n_recent, width;
+  uint8_t head_of_rho[kMaxHeads];
+};
+
+// grid (n_ret, B), 256 threads.
+__global__ __launch_bounds__(256) void dec_select_kernel(
+    const u16* __restrict__ q, const float* __restrict__ p_q,
+    const float* __restrict__ cent, const int32_t* __restrict__ cache_len,
+    const DecSelArgs a, float* __restrict__ cscores, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_cnt) {
+  __shared__ uint32_t keys[TK_LDS + TK_LDS / 32];
+  __shared__ float qt[kD];
+  __shared__ TopkShared sh;
+  const int rho = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int L = cache_len[b];
+  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
+  const int n_b = (L + 63) / 64;
+  const int n_c = max(n_b - a.n_recent - 1, 0);
+  const size_t row_id = (size_t)b * a.n_ret + rho;
+  int32_t* out = sel + row_id * a.width;
+  if (n_c <= a.top_k) {  // short cache: every block
+    for (int t = tid; t < a.width; t += 256) out[t] = t < n_b ? t : -1;
+    if (tid == 0) sel_cnt[row_id] = n_b;
+    return;
+  }
+  const int h = a.head_of_rho[rho];
+  const u16* qrow = q + ((size_t)b * a.Hq + h) * kD;
+  if (tid < a.r) {
+    const float* prow = p_q + ((size_t)rho * a.r + tid) * kD;
+    float acc = 0.f;
+    for (int d = 0; d < kD; ++d) acc = fmaf(prow[d], bf2f(qrow[d]), acc);
+    qt[tid] = acc;
+  }
+  __syncthreads();
+  const float* cb = cent + row_id * a.nbmax * a.r;
+  float* srow = cscores + row_id * a.nbmax;
+  const bool in_lds = n_c <= TK_LDS;
+  for (int e = tid; e < n_c; e += 256) {
+    const float* c = cb + (size_t)(e + 1) * a.r;
+    float s = 0.f;
+    for (int rr = 0; rr < a.r; ++rr) s = fmaf(qt[rr], c[rr], s);
+    if (in_lds) keys[e + (e >> 5)] = order_key(s);
+    else srow[e] = s;
+  }
+  __syncthreads();
+  auto getk = [&](int e) -> uint32_t {
+    return in_lds ? keys[e + (e >> 5)] : order_key(srow[e]);
+  };
+  radix_topk(getk, n_c, a.top_k, out + 1, 1, sh);
+  const int n_rec = n_b - 1 - n_c;  // = n_recent here
+  if (tid == 0) {
+    out[0] = 0;
+    sel_cnt[row_id] = 1 + a.top_k + n_rec;
+  }
+  for (int j = tid; j < n_rec; j += 256) out[1 + a.top_k + j] = n_c + 1 + j;
+}
+
+// ---------------------------------------------------------------- attention
+struct DecAttnArgs {
+  const u16* q; const u16* kc; const u16* vc; const int32_t* cache_len;
+  const int32_t* sel; const int32_t* sel_cnt;
+  float* part_o; float* part_ml;
+  int Hq, Hkv, Lmax, n_ret, window, n_split, sel_width, n_units;
+  float c;  // scale * log2(e)
+  // unit u: bits 0-1 kind (0 window heads of one KV group, 1 retrieval
+  // head), bits 8-15 KV head, bits 16-23 head count, bits 24-31 first index
+  // into hlist
+  uint32_t desc[2 * kMaxHeads];
+  uint8_t rho[2 * kMaxHeads];
+  uint8_t hlist[kMaxHeads];
+};
+
+// grid (n_split, n_units, B), 256 threads. Each wave takes 32-key tiles in
+// turn; S^T = K Q^T on MFMA (heads along N), P.V on the vector ALU.
+__global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
+  __shared__ float Pw[4][32][33];     // p[key row][head], per wave
+  __shared__ float alw[4][32];        // per-head rescale of this tile
+  __shared__ float red_o[4][kDecMaxUnitHeads][kD];
+  __shared__ float red_ml[4][kDecMaxUnitHeads][2];
+  const int s = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, n = lane & 31;
+  const uint32_t desc = a.desc[u];
+  const int kind = desc & 3, kvh = (desc >> 8) & 255, nh = (desc >> 16) & 255,
+            first = desc >> 24;
+  int L = a.cache_len[b];
+  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
+
+  // key tiles of this split
+  int nt = 0, k_begin = 0, k_end = 0, blk0 = 0;
+  const int32_t* list = nullptr;
+  if (kind == 0) {
+    const int lo = max(0, L - a.window);
+    const int nk = L - lo;
+    const int per = ((nk + a.n_split - 1) / a.n_split + 31) & ~31;
+    k_begin = min(lo + s * per, L);
+    k_end = min(lo + (s + 1) * per, L);
+    nt = (k_end - k_begin + 31) / 32;
+  } else {
+    const int rho = a.rho[u];
+    const int nsel = a.sel_cnt[(size_t)b * a.n_ret + rho];
+    list = a.sel + ((size_t)b * a.n_ret + rho) * a.sel_width;
+    const int bps = (nsel + a.n_split - 1) / a.n_split;
+    blk0 = min(s * bps, nsel);
+    const int blk1 = min(blk0 + bps, nsel);
+    nt = 2 * (blk1 - blk0);
+  }
+
+  const size_t kv_off = ((size_t)b * a.Hkv + kvh) * a.Lmax * kD;
+  const u16* kbase = a.kc + kv_off;
+  const u16* vbase = a.vc + kv_off;
+
+  // B operand: Q^T, column n = head n of the unit (zero beyond nh)
+  bf16x8 qf[8];
+  {
+    const int h = n < nh ? a.hlist[first + n] : a.hlist[first];
+    const u16* qp = a.q + ((size_t)b * a.Hq + h) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      if (n >= nh) { bf16x8 z = {}; v = z; }
+      qf[ks] = v;
+    }
+  }
+
+  float m_run = -1e30f, l_run = 0.f;  // softmax state of head n (lane pair)
+  float o[kDecMaxUnitHeads][8];       // PV lanes: key group kg, d chunk dc
+#pragma unroll
+  for (int j = 0; j < kDecMaxUnitHeads; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+  const int kg = lane >> 4, dc = lane & 15;
+
+  const int iters = (nt + 3) / 4;
+  for (int it = 0; it < iters; ++it) {
+    const int t = it * 4 + wave;
+    int base = 0, nvalid = 0;
+    if (t < nt) {
+      if (kind == 0) {
+        base = k_begin + 32 * t;
+        nvalid = min(32, k_end - base);
+      } else {
+        const int blk = list[blk0 + (t >> 1)];
+        base = blk * 64 + 32 * (t & 1);
+        nvalid = max(0, min(32, L - base));
+      }
+    }
+    if (t < nt && nvalid > 0) {
+      f32x16 sacc = {};
+      const int krow = n < nvalid ? base + n : base;
+      const u16* kp = kbase + (size_t)krow * kD + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sacc = mfma32(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qf[ks], sacc);
+      // accumulator element i: key row 8*(i/4) + 4*g + i%4, head n
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * g + (i & 3);
+        if (row >= nvalid) sacc[i] = -INFINITY;
+        tmax = fmaxf(tmax, sacc[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = fast_exp2((m_run - m_new) * a.c);
+      m_run = m_new;
+      const float mc = m_new * a.c;
+      float ls = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * g + (i & 3);
+        const float pv = fast_exp2(fmaf(sacc[i], a.c, -mc));
+        ls += pv;
+        Pw[wave][row][n] = pv;
+      }
+      l_run = l_run * alpha + ls;
+      if (g == 0) alw[wave][n] = alpha;
+    }
+    __syncthreads();
+    if (t < nt && nvalid > 0) {
+#pragma unroll
+      for (int j = 0; j < kDecMaxUnitHeads; ++j) {
+        if (j < nh) {
+          const float al = alw[wave][j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[j][e] *= al;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int row = 4 * jj + kg;
+        if (row < nvalid) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(
+              vbase + (size_t)(base + row) * kD + 8 * dc);
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          }
+#pragma unroll
+          for (int j = 0; j < kDecMaxUnitHeads; ++j) {
+            if (j < nh) {
+              const float pj = Pw[wave][row][j];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pj, v[e], o[j][e]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // wave-level totals: PV over the 4 key groups, l over the lane pair
+#pragma unroll
+  for (int j = 0; j < kDecMaxUnitHeads; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = o[j][e];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      o[j][e] = x;
+    }
+  l_run += __shfl_xor(l_run, 32);
+  if (kg == 0) {
+#pragma unroll
+    for (int j = 0; j < kDecMaxUnitHeads; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[wave][j][8 * dc + e] = o[j][e];
+  }
+  if (g == 0 && n < kDecMaxUnitHeads) {
+    red_ml[wave][n][0] = m_run;
+    red_ml[wave][n][1] = l_run;
+  }
+  __syncthreads();
+  // merge the 4 waves and write this split's partial state
+  for (int idx = tid; idx < nh * kD; idx += 256) {
+    const int j = idx / kD, d = idx % kD;
+    float M = -1e30f;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][j][0]);
+    float acc = 0.f, lsum = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2((red_ml[w][j][0] - M) * a.c);
+      acc += f * red_o[w][j][d];
+      lsum += f * red_ml[w][j][1];
+    }
+    const int h = a.hlist[first + j];
+    const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + s;
+    a.part_o[pidx * kD + d] = acc;
+    if (d == 0) {
+      a.part_ml[pidx * 2 + 0] = M;
+      a.part_ml[pidx * 2 + 1] = lsum;
+    }
+  }
+}
+
+// grid (Hq, B), 128 threads: combine the splits of one (sequence, head).
+__global__ __launch_bounds__(128) void dec_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    int Hq, int n_split, float c, u16* __restrict__ out, float* __restrict__ lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const size_t p0 = ((size_t)b * Hq + h) * n_split;
+  float M = -1e30f;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[(p0 + s) * 2]);
+  float acc = 0.f, l = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float f = fast_exp2((part_ml[(p0 + s) * 2] - M) * c);
+    acc += f * part_o[(p0 + s) * kD + d];
+    l += f * part_ml[(p0 + s) * 2 + 1];
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  out[((size_t)b * Hq + h) * kD + d] = f2bf(acc * inv);
+  if (lse && d == 0)
+    lse[(size_t)b * Hq + h] = (M * c + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  const int G = a.Hq / a.Hkv;
+  const int nbmax = a.Lmax / 64;
+  const int width = a.top_k + 1 + a.n_recent;
+  if (a.n_ret > 0) {
+    DecSelArgs sa;
+    sa.Hq = a.Hq;
+    sa.Lmax = a.Lmax;
+    sa.n_ret = a.n_ret;
+    sa.r = a.r;
+    sa.nbmax = nbmax;
+    sa.top_k = a.top_k;
+    sa.n_recent = a.n_recent;
+    sa.width = width;
+    for (int i = 0; i < kMaxHeads; ++i) sa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
+    hipLaunchKernelGGL(dec_select_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st,
+                       a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
+                       a.sel + (size_t)a.B * a.n_ret * width);
+  }
+  DecAttnArgs da;
+  da.q = a.q;
+  da.kc = a.kc;
+  da.vc = a.vc;
+  da.cache_len = a.cache_len;
+  da.sel = a.sel;
+  da.sel_cnt = a.sel + (size_t)a.B * a.n_ret * width;
+  da.part_o = a.part_o;
+  da.part_ml = a.part_ml;
+  da.Hq = a.Hq;
+  da.Hkv = a.Hkv;
+  da.Lmax = a.Lmax;
+  da.n_ret = a.n_ret;
+  da.window = a.window;
+  da.n_split = a.n_split;
+  da.sel_width = width;
+  da.c = a.scale * 1.4426950408889634f;
+  int nu = 0, nl = 0, rho = 0;
+  for (int g = 0; g < a.Hkv; ++g) {
+    int cnt = 0, start = nl;
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+      if (a.is_ret[h]) continue;
+      da.hlist[nl++] = (uint8_t)h;
+      if (++cnt == kDecMaxUnitHeads) {
+        da.desc[nu] = 0u | ((uint32_t)g << 8) | ((uint32_t)cnt << 16) | ((uint32_t)start << 24);
+        da.rho[nu++] = 0;
+        cnt = 0;
+        start = nl;
+      }
+    }
+    if (cnt) {
+      da.desc[nu] = 0u | ((uint32_t)g << 8) | ((uint32_t)cnt << 16) | ((uint32_t)start << 24);
+      da.rho[nu++] = 0;
+    }
+  }
+  for (int h = 0; h < a.Hq; ++h) {
+    if (!a.is_ret[h]) continue;
+    da.hlist[nl] = (uint8_t)h;
+    da.desc[nu] = 1u | ((uint32_t)(h / G) << 8) | (1u << 16) | ((uint32_t)nl << 24);
+    da.rho[nu++] = (uint8_t)rho++;
+    ++nl;
+  }
+  da.n_units = nu;
+  hipLaunchKernelGGL(dec_attn_kernel, dim3(a.n_split, nu, a.B), dim3(256), 0, st, da);
+  hipLaunchKernelGGL(dec_merge_kernel, dim3(a.Hq, a.B), dim3(kD), 0, st,
+                     a.part_o, a.part_ml, a.Hq, a.n_split, da.c, a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace rtp

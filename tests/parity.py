@@ -1,0 +1,77 @@
+"""Comparison helpers for GPU-vs-oracle parity tests.
+
+Bars (the tolerances the method is held to):
+* selected block indices: identical to the oracle's, except in a row whose
+  k-th and (k+1)-th oracle scores differ by less than TIE_BAND relative; there
+  every differing block must itself score within that band (logged as a tie);
+* outputs: max-abs difference <= OUT_TOL against the fp32 oracle, for bf16
+  inputs with fp32 accumulation;
+* log-sum-exp: max-abs difference <= LSE_TOL.
+
+OUT_TOL comes from the arithmetic: P is rounded to bf16 (relative 2^-9) before
+the P.V product and the output is rounded to bf16 (relative 2^-9); with |v|
+below ~5 for N(0,1) data that bounds the error by ~1e-2, the figure the
+method's accuracy target states.
+"""
+import math
+
+import numpy as np
+
+import oracle
+
+TIE_BAND = 1e-4
+OUT_TOL = 1e-2
+LSE_TOL = 2e-3
+
+
+def sel_sets(sel, cnt):
+    return [set(int(x) for x in sel[i][:cnt[i]]) for i in range(len(cnt))]
+
+
+def compare_selection(gsel, gcnt, osel, ocnt, okth, score_fn, label=""):
+    """gsel/osel [n_rows, width]; returns list of logged ties.
+
+    score_fn(row) -> oracle candidate scores of that row (index kb-1)."""
+    ties = []
+    for i in range(len(ocnt)):
+        g = set(int(x) for x in gsel[i][:gcnt[i]])
+        o = set(int(x) for x in osel[i][:ocnt[i]])
+        assert int(gcnt[i]) == int(ocnt[i]), (label, i, gcnt[i], ocnt[i])
+        assert list(gsel[i][:gcnt[i]]) == sorted(g), (label, i, "not ascending")
+        assert all(int(x) == -1 for x in gsel[i][gcnt[i]:]), (label, i)
+        if g == o:
+            continue
+        s_k, s_k1 = float(okth[i][0]), float(okth[i][1])
+        assert not math.isnan(s_k1) and abs(s_k - s_k1) <= TIE_BAND * abs(s_k), \
+            (label, i, sorted(g ^ o), s_k, s_k1)
+        sc = score_fn(i)
+        for b in g ^ o:
+            assert abs(sc[b - 1] - s_k) <= TIE_BAND * abs(s_k), (label, i, b)
+        ties.append((label, i, s_k, s_k1))
+    return ties
+
+
+def bf16_to_f32(t):
+    return t.float().cpu().numpy()
+
+
+def max_abs(a, b):
+    d = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    return float(np.nanmax(d)) if d.size else 0.0
+
+
+def prefill_rows_fn(x, qbits, kbits, rho, head):
+    """Oracle candidate scores of retrieval head rho, row qb (lazy)."""
+    g = head // (qbits.shape[0] // kbits.shape[0])
+    cache = {}
+
+    def fn(qb):
+        if "khat" not in cache:
+            kf = oracle.bf16_to_f32(kbits[g])
+            qf = oracle.bf16_to_f32(qbits[head])
+            cache["khat"] = oracle.project_keys(kf, x["p_k"][rho])
+            cache["qbar"] = oracle.query_block_means(qf, x["p_q"][rho],
+                                                     x["block"])
+        return oracle.block_score_row(cache["qbar"][qb], cache["khat"], qb,
+                                      x["block"])
+    return fn

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/rtp.h, and rejects bad arguments with the documented
+status before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_context_sparse_head_amd as rtp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rtp.LIB_PATH),
+                                reason="librtp.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("rtp_indexer_select", "rtp_hybrid_attn_prefill",
+              "rtp_hybrid_attn_decode", "rtp_build_centroids",
+              "rtp_dense_attn_prefill", "rtp_prefill_workspace_bytes",
+              "rtp_decode_workspace_bytes", "rtp_status_string",
+              "rtp_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rtp.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    # the binding's signature table covers the same set
+    assert set(declared_functions()) == set(rtp._SIGS)
+
+
+def test_status_strings_and_version():
+    lib = rtp.load()
+    assert lib.rtp_status_string(0) == b"ok"
+    assert b"invalid" in lib.rtp_status_string(-1)
+    assert b"unsupported" in lib.rtp_status_string(-2)
+    assert b"workspace" in lib.rtp_status_string(-3)
+    assert b"HIP" in lib.rtp_status_string(-4)
+    assert b"gfx950" in lib.rtp_version()
+
+
+def _mask(bits):
+    m = np.array(bits, dtype=np.uint8)
+    return m, m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def test_workspace_queries():
+    lib = rtp.load()
+    m, mp = _mask([1, 0, 0, 0])
+    S, n_b = 2048, 32
+    got = lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 16, 64, 8)
+    al = lambda x: (x + 255) // 256 * 256
+    want = (al(1 * 128 * S * 2) + 2 * al(1 * S * 16 * 2) +
+            2 * al(n_b * 16 * 2) + al((n_b - 2) * (n_b - 1) // 2 * 4) +
+            al(n_b * 10 * 4) + al(n_b * 4))
+    assert got == want
+    assert lib.rtp_prefill_workspace_bytes(S, 4, 1, 64, mp, 16, 64, 8) == 0
+    assert lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 16, 32, 8) == 0
+    assert lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 24, 64, 8) == 0
+    assert lib.rtp_dense_workspace_bytes(S, 4, 1, 128) == al(128 * S * 2)
+    assert lib.rtp_decode_workspace_bytes(2, 4096, 4, 1, 128, mp, 16, 64, 8,
+                                          2) > 0
+
+
+def _prefill(lib, mp, **kw):
+    a = dict(q=1, k=1, v=1, S=128, Hq=4, Hkv=1, d=128, window=16, pq=1, pk=1,
+             r=16, block=64, top_k=4, scale=0.0, sel_in=None, cnt_in=None,
+             out=1, lse=None, sel_out=None, cnt_out=None, ws=None, wsb=0)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.rtp_hybrid_attn_prefill(
+        P(a["q"]), P(a["k"]), P(a["v"]), a["S"], a["Hq"], a["Hkv"], a["d"],
+        mp, a["window"], P(a["pq"]), P(a["pk"]), a["r"], a["block"],
+        a["top_k"], a["scale"], P(a["sel_in"]), P(a["cnt_in"]), P(a["out"]),
+        P(a["lse"]), P(a["sel_out"]), P(a["cnt_out"]), P(a["ws"]), a["wsb"],
+        None)
+
+
+def test_prefill_argument_validation_returns_codes():
+    lib = rtp.load()
+    m, mp = _mask([1, 0, 0, 0])
+    assert _prefill(lib, mp, d=64) == -2
+    assert _prefill(lib, mp, block=32) == -2
+    assert _prefill(lib, mp, r=20) == -2
+    assert _prefill(lib, mp, Hq=6, Hkv=4) == -1
+    assert _prefill(lib, mp, S=-1) == -1
+    assert _prefill(lib, mp, window=0) == -1
+    assert _prefill(lib, mp, top_k=-1) == -1
+    assert _prefill(lib, mp, q=None) == -1
+    assert _prefill(lib, mp, pq=None) == -1
+    assert _prefill(lib, mp, sel_in=8) == -1       # count missing
+    assert _prefill(lib, mp, sel_out=8) == -1      # count missing
+    assert _prefill(lib, mp) == -3                 # no workspace
+    assert _prefill(lib, mp, ws=1 << 20 | 8, wsb=1 << 40) == -3  # misaligned
+    assert b"workspace" in lib.rtp_last_error()
+    assert _prefill(lib, mp, S=0) == 0             # empty: nothing to do
+    m2, mp2 = _mask([0] * 130)
+    assert _prefill(lib, mp2, Hq=130, Hkv=130) == -2
+
+
+def test_decode_and_centroid_validation():
+    lib = rtp.load()
+    m, mp = _mask([0, 1])
+    P = ctypes.c_void_p
+    st = lib.rtp_hybrid_attn_decode(P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                                    128, mp, 0, P(1), P(1), 16, 64, 8, 2, 0.0,
+                                    P(1), None, None, None, 0, None)
+    assert st == -1  # window 0
+    st = lib.rtp_hybrid_attn_decode(P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                                    128, mp, 64, None, P(1), 16, 64, 8, 2, 0.0,
+                                    P(1), None, None, None, 0, None)
+    assert st == -1  # p_q missing with a retrieval head
+    st = lib.rtp_hybrid_attn_decode(P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                                    128, mp, 64, P(1), P(1), 16, 64, 8, 2, 0.0,
+                                    P(1), None, None, None, 0, None)
+    assert st == -3  # no workspace
+    st = lib.rtp_build_centroids(P(1), P(1), 2, 4096, 2, 1, 128, mp, None, 16,
+                                 64, P(1), None)
+    assert st == -1
+    st = lib.rtp_build_centroids(P(1), P(1), 2, 4096, 2, 1, 128, mp, P(1), 16,
+                                 48, P(1), None)
+    assert st == -2
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rtp.dense_attn_prefill(q, q[:1], q[:1])
