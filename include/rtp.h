@@ -178,7 +178,9 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
  *  Retrieval head rho: n_b = ceil(L/block); q~ = P_q[rho] q; candidates
  *    1 .. n_b-n_recent-1 scored by q~ . centroids[b,rho,kb]; keeps block 0,
  *    the top_k candidates (ties: lower index) and blocks n_b-n_recent ..
- *    n_b-1; attends every cached token of the kept blocks.
+ *    n_b-1; attends every cached token of the kept blocks. n_recent >= 1:
+ *    the block holding the new token (possibly partial, so without a
+ *    centroid) is always kept.
  *
  *  q [B,Hq,d] bf16; k_cache/v_cache [B,Hkv,Lmax,d] bf16;
  *  cache_len [B] int32 DEVICE array (1 <= cache_len[b] <= Lmax);

@@ -362,7 +362,7 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
                                   const uint8_t* is_retrieval, int r,
                                   int block, int top_k, int n_recent) {
   if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0 ||
-      n_recent < 0)
+      n_recent < 1)
     return 0;
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
@@ -382,7 +382,8 @@ int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
   if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
   if (window < 1) return fail(RTP_EINVAL, "window must be >= 1");
-  if (n_recent < 0) return fail(RTP_EINVAL, "n_recent must be >= 0");
+  if (n_recent < 1)
+    return fail(RTP_EINVAL, "n_recent must be >= 1 (the block of the new token is always kept)");
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
   if (B == 0) return RTP_OK;

@@ -1,0 +1,125 @@
+"""GPU parity of hybrid decode (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import parity
+from workloads import DecodeWorkload, make_decode, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(batch, L, Hq, Hkv, ret, window, top_k, n_recent=2, seed=0):
+    return DecodeWorkload("t", batch=batch, L=L, Hq=Hq, Hkv=Hkv, d=128,
+                          n_ret=len(ret), window=window, r=16, block=64,
+                          top_k=top_k, n_recent=n_recent, seed=seed,
+                          retrieval_heads=tuple(ret))
+
+
+def run_gpu(rtp, y):
+    dev = "cuda"
+    kc, vc = y["k_cache"].to(dev), y["v_cache"].to(dev)
+    cl = torch.from_numpy(y["cache_len"]).to(dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    pq = torch.from_numpy(y["p_q"]).to(dev)
+    cent = rtp.build_centroids(kc, cl, y["is_retrieval"], pk)
+    out, lse, sel = rtp.hybrid_attn_decode(
+        y["q"].to(dev), kc, vc, cl, y["is_retrieval"], y["window"], pq, cent,
+        y["top_k"], n_recent=y["n_recent"], want_lse=True, want_sel=True)
+    torch.cuda.synchronize()
+    return out, lse, sel, cent
+
+
+def check(rtp, y, label, seqs=None):
+    out, lse, sel, cent = run_gpu(rtp, y)
+    ora = oracle.hybrid_decode(bf16_bits(y["q"]), bf16_bits(y["k_cache"]),
+                               bf16_bits(y["v_cache"]), y["cache_len"],
+                               y["is_retrieval"], y["window"], y["p_q"],
+                               y["p_k"], 64, y["top_k"], y["n_recent"],
+                               seqs=seqs)
+    seqs = range(len(y["cache_len"])) if seqs is None else seqs
+    gsel = sel.cpu().numpy()
+    gcent = cent.cpu().numpy()
+    ties = []
+    for b in seqs:
+        L = int(y["cache_len"][b])
+        n_full = L // 64
+        for rho in range(len(y["retrieval_heads"])):
+            c_o = ora["centroids"][(b, rho)]
+            c_g = gcent[b, rho, :n_full]
+            if n_full:
+                assert np.abs(c_g - c_o).max() <= 1e-5 * max(
+                    np.abs(c_o).max(), 1.0), (label, b, rho)
+            g = gsel[b, rho]
+            gcnt = int((g >= 0).sum())
+            qt = (y["p_q"][rho] @ oracle.bf16_to_f32(bf16_bits(
+                y["q"][b, y["retrieval_heads"][rho]])))
+
+            def fn(_, c_o=c_o, qt=qt):
+                return c_o[1:] @ qt.astype(np.float32)
+            ties += parity.compare_selection(
+                g[None], np.array([gcnt]), ora["sel"][b, rho][None],
+                ora["sel_count"][b, rho][None], ora["kth"][b, rho][None], fn,
+                f"{label} b={b} rho={rho}")
+    # rows whose choice differs at a logged near-tie are left out of the
+    # output comparison (the oracle attended a different, equally valid set)
+    assert len(ties) <= 2, ties
+    skip = {(int(t[0].split("b=")[1].split()[0]),
+             int(y["retrieval_heads"][int(t[0].split("rho=")[1])]))
+            for t in ties}
+    o_g = parity.bf16_to_f32(out)
+    l_g = lse.cpu().numpy()
+    for b in seqs:
+        for h in range(o_g.shape[1]):
+            if (b, h) in skip:
+                continue
+            err = parity.max_abs(o_g[b, h], ora["out"][b, h])
+            assert err <= parity.OUT_TOL, (label, b, h, err)
+            assert abs(l_g[b, h] - ora["lse"][b, h]) <= parity.LSE_TOL, \
+                (label, b, h)
+    return out, ora
+
+
+def test_decode_ragged_batch(gpu_lib):
+    y = make_decode(_wl(5, 6000, Hq=8, Hkv=2, ret=(1, 6), window=512,
+                        top_k=8), cache_len=[6000, 4096, 777, 65, 4161])
+    check(gpu_lib, y, "ragged")
+
+
+def test_decode_short_caches_keep_every_block(gpu_lib):
+    y = make_decode(_wl(4, 200, Hq=4, Hkv=1, ret=(0, 2), window=64, top_k=8),
+                    cache_len=[1, 63, 64, 130])
+    out, ora = check(gpu_lib, y, "short")
+
+
+def test_decode_full_coverage_equals_dense(gpu_lib):
+    # window >= L and top_k >= n_b: every head attends the whole cache
+    y = make_decode(_wl(3, 3000, Hq=8, Hkv=2, ret=(0, 3, 5), window=10 ** 6,
+                        top_k=64), cache_len=[3000, 2049, 100])
+    check(gpu_lib, y, "full")
+
+
+def test_decode_window_one_returns_last_value(gpu_lib):
+    y = make_decode(_wl(3, 500, Hq=4, Hkv=1, ret=(), window=1, top_k=1),
+                    cache_len=[500, 1, 77])
+    out = run_gpu(gpu_lib, y)[0].cpu()
+    for b, L in enumerate([500, 1, 77]):
+        for h in range(4):
+            assert torch.equal(out[b, h], y["v_cache"][b, 0, L - 1])
+
+
+def test_decode_many_heads_per_group(gpu_lib):
+    # 16 window heads share one KV head: two passes of 8 heads
+    y = make_decode(_wl(2, 3000, Hq=16, Hkv=1, ret=(3,), window=700,
+                        top_k=4), cache_len=[3000, 1800])
+    check(gpu_lib, y, "gqa16")
+
+
+def test_decode_deterministic(gpu_lib):
+    y = make_decode(_wl(4, 4000, Hq=8, Hkv=2, ret=(2, 7), window=300,
+                        top_k=6), cache_len=[4000, 3000, 2000, 999])
+    a = run_gpu(gpu_lib, y)
+    b = run_gpu(gpu_lib, y)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
