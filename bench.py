@@ -1,0 +1,385 @@
+#!/usr/bin/env python3
+"""Benchmark of headwise hybrid attention on one MI355X.
+
+One step = one call of rtp_hybrid_attn_prefill on the 128K-token workload
+(one attention layer at Qwen3-30B-A3B shape: 32 query / 4 KV heads, d = 128,
+5 retrieval heads with the r = 16 indexer, 27 window heads with w = 8192,
+block 64, top-128 blocks, planted needle blocks): the indexer (projection,
+block scores, top-k), the V transpose and the attention kernel. Inputs are
+synthetic and resident in HBM before timing starts.
+
+The same run also measures, as secondary figures: the 1M-token all-sparse
+prefill, the 32K prefill, a decode step of 32 sequences x 256K cached tokens,
+and the dense causal kernel of the same library on the 128K inputs. The CPU
+oracle is timed on a bounded sample of the 128K workload.
+
+Prints ONE JSON line. Usage: python bench.py [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ accounting
+def prefill_pairs(S, Hq, is_ret, window, sel_cnt_np):
+    """Executed (query, key) pairs: causal-, window- and selection-exact."""
+    i = np.arange(S, dtype=np.int64)
+    swa_per_head = int(np.minimum(i + 1, window).sum())
+    n_swa = int((np.asarray(is_ret) == 0).sum())
+    ret = 0
+    n_b = -(-S // 64)
+    last = S - 64 * (n_b - 1)
+    for rho in range(sel_cnt_np.shape[0]):
+        cnt = sel_cnt_np[rho].astype(np.int64)
+        diag = np.full(n_b, 64 * 65 // 2, dtype=np.int64)
+        diag[-1] = last * (last + 1) // 2
+        rows = np.full(n_b, 64, dtype=np.int64)
+        rows[-1] = last
+        ret += int(((cnt - 1) * 64 * rows + diag).sum())
+    return n_swa * swa_per_head, ret
+
+
+def kernel_stats(records, steps):
+    out = {}
+    for name, ms in records:
+        d = out.setdefault(name, {"launches": 0, "ms_total": 0.0})
+        d["launches"] += 1
+        d["ms_total"] += ms
+    for d in out.values():
+        d["ms_per_launch"] = d["ms_total"] / d["launches"]
+        d["ms_per_step"] = d["ms_total"] / steps
+    return out
+
+
+# ------------------------------------------------------------ GPU legs
+def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
+    from workloads import make_prefill
+    dev = "cuda"
+    t0 = time.time()
+    x = make_prefill(w, device=dev)
+    pq = torch.from_numpy(x["p_q"]).to(dev)
+    pk = torch.from_numpy(x["p_k"]).to(dev)
+    S, Hq, Hkv = w.S, w.Hq, w.Hkv
+    out = torch.empty_like(x["q"])
+    n_b = -(-S // 64)
+    n_ret = int(x["is_retrieval"].sum())
+    sel = torch.empty((n_ret, n_b, w.top_k + 2), dtype=torch.int32, device=dev)
+    cnt = torch.empty((n_ret, n_b), dtype=torch.int32, device=dev)
+    if dense:
+        ws = torch.empty(rtp.dense_workspace_bytes(S, Hq, Hkv), dtype=torch.uint8,
+                         device=dev)
+        call = lambda: rtp.dense_attn_prefill(x["q"], x["k"], x["v"], ws=ws,
+                                              out=out)
+    else:
+        ws = torch.empty(rtp.prefill_workspace_bytes(S, Hq, Hkv,
+                                                     x["is_retrieval"], w.r,
+                                                     w.top_k),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            return rtp.hybrid_attn_prefill(
+                x["q"], x["k"], x["v"], x["is_retrieval"], w.window, pq, pk,
+                w.top_k, r=w.r, ws=ws, out=out)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}{' dense' if dense else ''}: inputs ready in "
+        f"{time.time() - t0:.1f}s, workspace {ws.numel() / 2**30:.2f} GiB")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    with rtp.KernelTimer() as kt:
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+    ms = (t2 - t1) * 1e3 / steps
+    ks = kernel_stats(kt.records, steps)
+    if dense:
+        i = np.arange(S, dtype=np.int64)
+        swa_pairs, ret_pairs = Hq * int((i + 1).sum()), 0
+    else:
+        # the selection of one more call, for exact pair counts
+        _, _, s2, c2 = rtp.hybrid_attn_prefill(
+            x["q"], x["k"], x["v"], x["is_retrieval"], w.window, pq, pk,
+            w.top_k, r=w.r, ws=ws, out=out, want_sel=True)
+        torch.cuda.synchronize()
+        swa_pairs, ret_pairs = prefill_pairs(S, Hq, x["is_retrieval"],
+                                             w.window, c2.cpu().numpy())
+    flops = 4 * 128 * (swa_pairs + ret_pairs)
+    att = ks["attn"]
+    res = {
+        "workload": w.name, "S": S, "ms_per_step": ms,
+        "tokens_per_s": S / (ms / 1e3),
+        "attn_pairs": {"window": swa_pairs, "retrieval": ret_pairs},
+        "attn_flops": flops,
+        "attn_ms": att["ms_per_launch"],
+        "attn_tflops": flops / (att["ms_per_launch"] / 1e3) / 1e12,
+        "step_tflops": flops / (ms / 1e3) / 1e12,
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4)
+                                for k, v in ks.items()},
+    }
+    res["attn_frac_bf16_peak"] = res["attn_tflops"] / PEAK_BF16_TFLOPS
+    if not dense and n_ret:
+        # indexer figures (algorithmic): scores are 2r flops per (query
+        # block, candidate key); projections read K and Q once
+        cand_keys = 64 * sum(max(q - 1, 0) for q in range(n_b))
+        sc = ks.get("block_scores")
+        if sc:
+            res["block_scores_tflops_alg"] = (n_ret * cand_keys * 2 * w.r /
+                                              (sc["ms_per_launch"] / 1e3) / 1e12)
+        pkk = ks.get("proj_keys")
+        if pkk:
+            byt = n_ret * S * (256 + 64)
+            res["proj_keys_gbs_alg"] = byt / (pkk["ms_per_launch"] / 1e3) / 1e9
+    del x, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(rtp, torch, w, steps, warmup):
+    from workloads import make_decode
+    dev = "cuda"
+    t0 = time.time()
+    y = make_decode(w, device=dev)
+    cl = torch.from_numpy(y["cache_len"]).to(dev)
+    pq = torch.from_numpy(y["p_q"]).to(dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    with rtp.KernelTimer() as kb:
+        cent = rtp.build_centroids(y["k_cache"], cl, y["is_retrieval"], pk)
+        torch.cuda.synchronize()
+    B, Hq, Hkv, L = w.batch, w.Hq, w.Hkv, w.L
+    ws = torch.empty(rtp.decode_workspace_bytes(B, L, Hq, Hkv,
+                                                y["is_retrieval"], w.r,
+                                                w.top_k, w.n_recent),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(y["q"])
+
+    def call(want_sel=False):
+        return rtp.hybrid_attn_decode(y["q"], y["k_cache"], y["v_cache"], cl,
+                                      y["is_retrieval"], w.window, pq, cent,
+                                      w.top_k, n_recent=w.n_recent, ws=ws,
+                                      out=out, want_sel=want_sel)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs + centroids ready in {time.time() - t0:.1f}s")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    with rtp.KernelTimer() as kt:
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+    ms = (t2 - t1) * 1e3 / steps
+    ks = kernel_stats(kt.records, steps)
+    _, _, sel = call(want_sel=True)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    n_swa = int((y["is_retrieval"] == 0).sum())
+    G = Hq // Hkv
+    swa_groups = sum(1 for g in range(Hkv)
+                     if any(not y["is_retrieval"][h]
+                            for h in range(g * G, (g + 1) * G)))
+    kv_row = 2 * 128 * 2  # K and V bytes per token
+    byt = B * swa_groups * min(w.window, L) * kv_row          # window passes
+    byt += int((sel >= 0).sum()) * 64 * kv_row                # gathered blocks
+    n_b = -(-L // 64)
+    byt += B * sel.shape[1] * (n_b - w.n_recent - 1) * w.r * 4  # centroids
+    att = ks["dec_attn"]
+    res = {
+        "workload": w.name, "batch": B, "cache_len": L,
+        "ms_per_step": ms, "tokens_per_s": B / (ms / 1e3),
+        "bytes_per_step_alg": byt,
+        "step_gbs_alg": byt / (ms / 1e3) / 1e9,
+        "dec_attn_gbs_alg": (byt - B * sel.shape[1] * (n_b - w.n_recent - 1)
+                             * w.r * 4) / (att["ms_per_launch"] / 1e3) / 1e9,
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4)
+                                for k, v in ks.items()},
+        "centroid_build_ms": kb.total("build_centroids"),
+    }
+    res["step_frac_hbm"] = res["step_gbs_alg"] / PEAK_HBM_GBS
+    del y, ws, out, cent
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------ CPU oracle
+def cpu_baseline(w, ret_pairs_total, budget_s=15.0):
+    """Time the oracle on a bounded sample of the workload and scale it to
+    the whole layer by exact work counts (pairs, candidate keys)."""
+    import torch
+    import oracle
+    from workloads import make_prefill, bf16_bits, draw_projections
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads") for p in threadpool_info()
+                if p.get("user_api") == "blas"]
+        cores = int(max(blas)) if blas else os.cpu_count()
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    x = make_prefill(w, device="cuda")
+    S, B = w.S, 64
+    n_b = -(-S // B)
+    G = w.Hq // w.Hkv
+    ret_heads = list(x["retrieval_heads"])
+    swa_heads = [h for h in range(w.Hq) if not x["is_retrieval"][h]]
+    h_r, h_s = ret_heads[0], swa_heads[0]
+    g_r, g_s = h_r // G, h_s // G
+    qr = oracle.bf16_to_f32(bf16_bits(x["q"][h_r]))
+    kr = oracle.bf16_to_f32(bf16_bits(x["k"][g_r]))
+    vr = oracle.bf16_to_f32(bf16_bits(x["v"][g_r]))
+    qs = oracle.bf16_to_f32(bf16_bits(x["q"][h_s]))
+    ks_ = oracle.bf16_to_f32(bf16_bits(x["k"][g_s]))
+    vs = oracle.bf16_to_f32(bf16_bits(x["v"][g_s]))
+    del x
+    torch.cuda.empty_cache()
+    scale = 1.0 / math.sqrt(128)
+    rng = np.random.default_rng(1)
+    t_start = time.perf_counter()
+    # indexer of one retrieval head: projections in full
+    t0 = time.perf_counter()
+    p_q, p_k = draw_projections(len(ret_heads), w.r, 128, w.seed)
+    khat = oracle.project_keys(kr, p_k[0])
+    qbar = oracle.query_block_means(qr, p_q[0], B)
+    t_proj = time.perf_counter() - t0
+    # sampled selection rows and attention blocks, until the budget is used
+    rows_done = cand_done = 0
+    t_rows = 0.0
+    ret_pairs = swa_pairs = 0
+    t_ret = t_swa = 0.0
+    i_blk = 0
+    while time.perf_counter() - t_start < budget_s and i_blk < 20000:
+        qb = int(rng.integers(2, n_b))
+        t0 = time.perf_counter()
+        sc = oracle.block_score_row(qbar[qb], khat, qb, B)
+        sel, _, _ = oracle.select_row(sc, qb, w.top_k)
+        t_rows += time.perf_counter() - t0
+        rows_done += 1
+        cand_done += qb - 1
+        rows = np.arange(qb * B, min(S, (qb + 1) * B))
+        t0 = time.perf_counter()
+        union, mem = oracle.retrieval_block_keys(rows, sel, B, S)
+        oracle.attend(qr[rows], kr[union], vr[union], mem, scale)
+        t_ret += time.perf_counter() - t0
+        ret_pairs += int(mem.sum())
+        t0 = time.perf_counter()
+        union, mem = oracle.swa_block_keys(rows, w.window)
+        oracle.attend(qs[rows], ks_[union], vs[union], mem, scale)
+        t_swa += time.perf_counter() - t0
+        swa_pairs += int(mem.sum())
+        i_blk += 1
+    wall = time.perf_counter() - t_start
+    # scale to the whole layer
+    i = np.arange(S, dtype=np.int64)
+    swa_total = int(np.minimum(i + 1, w.window).sum()) * len(swa_heads)
+    cand_total = sum(max(q - 1, 0) for q in range(n_b))
+    est = (len(ret_heads) * (t_proj + t_rows / max(cand_done, 1) * cand_total)
+           + t_ret / max(ret_pairs, 1) * ret_pairs_total
+           + t_swa / max(swa_pairs, 1) * swa_total)
+    return {
+        "value": S / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{w.name}: indexer projections of 1 retrieval head, "
+                   f"{rows_done} selection rows, {i_blk} query blocks of 1 "
+                   f"retrieval and 1 window head ({wall:.1f}s of CPU work), "
+                   f"scaled by exact pair / candidate counts to the whole "
+                   f"layer (extrapolated {est:.0f}s)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only-main", action="store_true",
+                    help="time the 128K prefill only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU "
+              "path (see DESIGN.md for how it would shard); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_sparse_head_amd as rtp
+    from workloads import PREFILL_128K, PREFILL_1M, PREFILL_32K, DECODE_32x256K
+    rtp.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup)
+    log(f"[bench] 128K: {main['ms_per_step']:.3f} ms/step, "
+        f"{main['tokens_per_s']:.3e} tok/s, attn {main['attn_tflops']:.0f} TF/s")
+    extra = {}
+    if not args.only_main:
+        extra["prefill_1m"] = bench_prefill(rtp, torch, PREFILL_1M,
+                                            max(2, args.steps // 4), 1)
+        log(f"[bench] 1M: {extra['prefill_1m']['ms_per_step']:.1f} ms/step")
+        extra["prefill_32k"] = bench_prefill(rtp, torch, PREFILL_32K,
+                                             args.steps, args.warmup)
+        log(f"[bench] 32K: {extra['prefill_32k']['ms_per_step']:.3f} ms/step")
+        extra["decode"] = bench_decode(rtp, torch, DECODE_32x256K, args.steps,
+                                       args.warmup)
+        log(f"[bench] decode: {extra['decode']['ms_per_step']:.3f} ms/step")
+        extra["dense_128k"] = bench_prefill(rtp, torch, PREFILL_128K,
+                                            max(2, args.steps // 4), 1,
+                                            dense=True)
+        log(f"[bench] dense 128K: {extra['dense_128k']['ms_per_step']:.1f} "
+            f"ms/step")
+        extra["speedup_vs_dense_128k"] = (extra["dense_128k"]["ms_per_step"] /
+                                          main["ms_per_step"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(PREFILL_128K, main["attn_pairs"]["retrieval"],
+                           args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.1f} tok/s")
+    w = PREFILL_128K
+    line = {
+        "metric": METRIC,
+        "value": main["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq_len": w.S, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.d,
+                   "retrieval_heads": w.n_ret, "window": w.window,
+                   "rank": w.r, "block": w.block, "top_k": w.top_k,
+                   "needle_blocks": w.needles},
+        "roofline": {"bound": "mfma", "kernel": "attn",
+                     "achieved": main["attn_tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": main["attn_frac_bf16_peak"], "traffic": None},
+        "cpu_baseline": cpu,
+        "detail": {"prefill_128k": main, **extra},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

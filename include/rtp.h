@@ -74,6 +74,15 @@ const char* rtp_last_error(void);
 /* Library version string. */
 const char* rtp_version(void);
 
+/* Kernel timing for measurement tools. rtp_profile(1) clears the record and
+ * makes every later call record a pair of HIP events on its stream around
+ * each kernel it launches; rtp_profile(0) stops. rtp_profile_read() waits for
+ * the recorded events, writes up to `max` kernel names (static strings) and
+ * elapsed milliseconds, clears the record and returns the count (or a
+ * negative status). Not meant to be used while calls run on other threads. */
+int rtp_profile(int enable);
+int rtp_profile_read(const char** names, float* ms, int max);
+
 /* Workspace bytes needed by rtp_indexer_select / rtp_hybrid_attn_prefill
  * for these sizes (0 on invalid arguments). */
 size_t rtp_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,

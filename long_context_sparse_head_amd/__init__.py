@@ -24,7 +24,7 @@ __all__ = [
     "load", "LIB_PATH", "RtpError", "prefill_workspace_bytes",
     "dense_workspace_bytes", "decode_workspace_bytes", "indexer_select",
     "hybrid_attn_prefill", "dense_attn_prefill", "build_centroids",
-    "hybrid_attn_decode", "version",
+    "hybrid_attn_decode", "version", "KernelTimer",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
@@ -41,6 +41,9 @@ _SIGS = {
     "rtp_status_string": (ctypes.c_char_p, [_I]),
     "rtp_last_error": (ctypes.c_char_p, []),
     "rtp_version": (ctypes.c_char_p, []),
+    "rtp_profile": (_I, [_I]),
+    "rtp_profile_read": (_I, [ctypes.POINTER(ctypes.c_char_p),
+                              ctypes.POINTER(ctypes.c_float), _I]),
     "rtp_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I, _U8P, _I, _I, _I]),
     "rtp_dense_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "rtp_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _U8P, _I, _I, _I,
@@ -83,6 +86,35 @@ def load():
 
 def version() -> str:
     return load().rtp_version().decode()
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of library calls made inside the block.
+
+    with KernelTimer() as kt: ...; then kt.records = [(name, ms), ...]."""
+
+    def __enter__(self):
+        load().rtp_profile(1)
+        self.records = []
+        return self
+
+    def __exit__(self, *exc):
+        lib = load()
+        cap = 1 << 14
+        names = (ctypes.c_char_p * cap)()
+        ms = (ctypes.c_float * cap)()
+        n = lib.rtp_profile_read(names, ms, cap)
+        lib.rtp_profile(0)
+        if n < 0:
+            _check(n, "rtp_profile_read")
+        self.records = [(names[i].decode(), float(ms[i])) for i in range(n)]
+        return False
+
+    def total(self, name: str) -> float:
+        return sum(t for k, t in self.records if k == name)
+
+    def count(self, name: str) -> int:
+        return sum(1 for k, _ in self.records if k == name)
 
 
 def _check(status: int, what: str):

@@ -4,6 +4,7 @@
 #include "../../include/rtp.h"
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -117,9 +118,69 @@ rtp::AttnItems make_items(int Hq, int G, const uint8_t* is_ret, bool pair) {
   return it;
 }
 
+// ------------------------------------------------------- kernel timing
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_prof_pool;
+std::vector<ProfRec> g_prof_recs;
+constexpr size_t kProfMax = 1 << 14;
+
 }  // namespace
 
+namespace rtp {
+void prof_begin(const char* name, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_recs.size() >= kProfMax) return;
+  if (g_prof_recs.size() == g_prof_pool.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
+    }
+    g_prof_pool.push_back({a, b});
+  }
+  const auto& ev = g_prof_pool[g_prof_recs.size()];
+  if (hipEventRecord(ev.first, st) != hipSuccess) return;
+  g_prof_recs.push_back({name, ev.first, ev.second});
+}
+void prof_end(hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_recs.empty()) return;
+  (void)hipEventRecord(g_prof_recs.back().b, st);
+}
+}  // namespace rtp
+
 extern "C" {
+
+int rtp_profile(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  g_prof_recs.clear();
+  return RTP_OK;
+}
+
+int rtp_profile_read(const char** names, float* ms, int max) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int n = 0;
+  for (const auto& r : g_prof_recs) {
+    if (n >= max) break;
+    hipError_t e = hipEventSynchronize(r.b);
+    float t = -1.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "rtp_profile_read");
+    if (names) names[n] = r.name;
+    if (ms) ms[n] = t;
+    ++n;
+  }
+  g_prof_recs.clear();
+  return n;
+}
+
 
 const char* rtp_status_string(int s) {
   switch (s) {

@@ -330,7 +330,9 @@ hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
                               hipStream_t st) {
   if (S_pad == 0) return hipSuccess;
   dim3 grid(S_pad / 64, Hkv);
+  prof_begin("transpose_v", st);
   hipLaunchKernelGGL(transpose_v_kernel, grid, dim3(256), 0, st, v, vt, S, S_pad);
+  prof_end(st);
   return hipGetLastError();
 }
 
@@ -345,7 +347,9 @@ hipError_t launch_attention(const AttnLaunch& a, const AttnItems& items,
   p.n_items = a.n_b * items.n;
   p.chunk = items.n;
   for (int i = 0; i < kMaxHeads; ++i) p.desc[i] = i < items.n ? items.desc[i] : 0;
+  prof_begin("attn", st);
   hipLaunchKernelGGL(attn_kernel, dim3(p.n_items), dim3(256), 0, st, p);
+  prof_end(st);
   return hipGetLastError();
 }
 

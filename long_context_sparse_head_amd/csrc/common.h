@@ -34,6 +34,11 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+// Optional per-kernel timing (off unless rtp_profile(1) was called): HIP
+// events recorded on the launch stream right before and after a kernel.
+void prof_begin(const char* name, hipStream_t st);
+void prof_end(hipStream_t st);
+
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 

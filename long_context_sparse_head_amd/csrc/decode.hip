@@ -72,8 +72,10 @@ hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
   ca.nbmax = nbmax;
   for (int i = 0; i < kMaxHeads; ++i)
     ca.kvh_of_rho[i] = i < n_ret ? ret_heads[i] / G : 0;
+  prof_begin("build_centroids", st);
   hipLaunchKernelGGL(build_centroids_kernel, dim3(nbmax, n_ret, B), dim3(64), 0,
                      st, kc, cache_len, p_k, ca, cent);
+  prof_end(st);
   return hipGetLastError();
 }
 
@@ -373,9 +375,11 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     sa.n_recent = a.n_recent;
     sa.width = width;
     for (int i = 0; i < kMaxHeads; ++i) sa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
+    prof_begin("dec_select", st);
     hipLaunchKernelGGL(dec_select_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st,
                        a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
                        a.sel + (size_t)a.B * a.n_ret * width);
+    prof_end(st);
   }
   DecAttnArgs da;
   da.q = a.q;
@@ -420,9 +424,13 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     ++nl;
   }
   da.n_units = nu;
+  prof_begin("dec_attn", st);
   hipLaunchKernelGGL(dec_attn_kernel, dim3(a.n_split, nu, a.B), dim3(256), 0, st, da);
+  prof_end(st);
+  prof_begin("dec_merge", st);
   hipLaunchKernelGGL(dec_merge_kernel, dim3(a.Hq, a.B), dim3(kD), 0, st,
                      a.part_o, a.part_ml, a.Hq, a.n_split, da.c, a.out, a.lse);
+  prof_end(st);
   return hipGetLastError();
 }
 

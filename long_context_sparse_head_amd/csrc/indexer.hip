@@ -326,12 +326,17 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
     pa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
     pa.kvh_of_rho[i] = i < a.n_ret ? a.ret_heads[i] / G : 0;
   }
+  prof_begin("proj_keys", st);
   hipLaunchKernelGGL(proj_keys_kernel, dim3(a.n_ret, a.S_pad / 64), dim3(64), 0,
                      st, a.k, a.p_k, pa, a.khi, a.klo, a.centroids);
+  prof_end(st);
+  prof_begin("proj_qmeans", st);
   hipLaunchKernelGGL(proj_qmeans_kernel, dim3(a.n_ret, a.n_b), dim3(64), 0, st,
                      a.q, a.p_q, pa, a.qhi, a.qlo);
+  prof_end(st);
   if (a.n_b >= 3) {
     dim3 grid((a.n_b + KBC - 1) / KBC, (a.n_b + 127) / 128, a.n_ret);
+    prof_begin("block_scores", st);
     switch (a.r / 16) {
 #define RTP_SCORE_CASE(R)                                                    \
   case R:                                                                    \
@@ -343,10 +348,13 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
 #undef RTP_SCORE_CASE
       default: return hipErrorInvalidValue;
     }
+    prof_end(st);
   }
+  prof_begin("topk", st);
   hipLaunchKernelGGL(topk_kernel, dim3(a.n_b, a.n_ret), dim3(256), 0, st,
                      a.scores, a.n_b, a.top_k, a.top_k + 2, a.sel, a.sel_cnt,
                      a.kth);
+  prof_end(st);
   return hipGetLastError();
 }
 
