@@ -92,32 +92,6 @@ float resolve_scale(float scale, int d) {
   return scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
 }
 
-// Work items of one query block: window heads in pairs of one KV group
-// (they share every key tile), leftovers and retrieval heads alone.
-rtp::AttnItems make_items(int Hq, int G, const uint8_t* is_ret, bool pair) {
-  rtp::AttnItems it;
-  it.n = 0;
-  const int Hkv = Hq / G;
-  int rho = 0;
-  std::vector<int> rho_of(Hq, 0);
-  for (int h = 0; h < Hq; ++h)
-    if (is_ret && is_ret[h]) rho_of[h] = rho++;
-  for (int g = 0; g < Hkv; ++g) {
-    std::vector<int> swa;
-    for (int h = g * G; h < (g + 1) * G; ++h)
-      if (!(is_ret && is_ret[h])) swa.push_back(h);
-    size_t i = 0;
-    if (pair)
-      for (; i + 1 < swa.size(); i += 2)
-        it.desc[it.n++] = 0u | ((uint32_t)swa[i] << 8) | ((uint32_t)swa[i + 1] << 16);
-    for (; i < swa.size(); ++i) it.desc[it.n++] = 1u | ((uint32_t)swa[i] << 8);
-    for (int h = g * G; h < (g + 1) * G; ++h)
-      if (is_ret && is_ret[h])
-        it.desc[it.n++] = 2u | ((uint32_t)h << 8) | ((uint32_t)rho_of[h] << 24);
-  }
-  return it;
-}
-
 // ------------------------------------------------------- kernel timing
 struct ProfRec {
   const char* name;
@@ -332,10 +306,10 @@ int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
   a.S_pad = S_pad;
   a.n_b = n_b;
   a.G = Hq / Hkv;
+  a.Hkv = Hkv;
   a.window = window;
   a.scale = resolve_scale(scale, d);
-  const rtp::AttnItems items = make_items(Hq, a.G, is_retrieval, true);
-  e = rtp::launch_attention(a, items, st);
+  e = rtp::launch_attention(a, is_retrieval, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RTP_OK;
 }
@@ -370,10 +344,10 @@ int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
   a.S_pad = S_pad;
   a.n_b = n_b;
   a.G = Hq / Hkv;
+  a.Hkv = Hkv;
   a.window = S;  // window >= S: full causal attention
   a.scale = resolve_scale(scale, d);
-  const rtp::AttnItems items = make_items(Hq, a.G, nullptr, true);
-  e = rtp::launch_attention(a, items, st);
+  e = rtp::launch_attention(a, nullptr, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RTP_OK;
 }

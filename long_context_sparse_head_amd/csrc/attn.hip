@@ -1,7 +1,7 @@
-// Attention tile engine for gfx950: sliding-window heads, dense causal heads
-// and block-sparse retrieval heads in one persistent-free launch.
+// Attention kernels for gfx950: sliding-window / dense causal heads and
+// block-sparse retrieval heads.
 //
-// What it computes (Synced RTPurbo article, "化繁为简，被低估的 SWA": most
+// What they compute (Synced RTPurbo article, "化繁为简，被低估的 SWA": most
 // heads attend only a recent window; aitop.news summary of "Full Attention
 // Strikes Back": retrieval heads run exact attention on an indexer-selected
 // set): for query i and its key set J_i,
@@ -9,299 +9,557 @@
 // with J_i = {i-w < j <= i} for a window head and J_i = {j <= i in the kept
 // blocks} for a retrieval head.
 //
-// Design (MI355X-first):
-//  * One workgroup = 4 waves = 64 queries of one query block; key tiles are
-//    64-token blocks, so a block-sparse list and a window range drive the same
-//    loop. Work items: a PAIR of window heads of one KV group (each wave owns
-//    32 queries of one head and the whole key tile), or a SINGLE head (each
-//    wave owns 32 queries and one 32-key half of every tile; the two halves
-//    are merged through LDS at the end).
-//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with the query along the lanes,
-//    so a query's scores sit in one lane pair and the row max needs a single
-//    cross-lane exchange. K rows are stored in LDS in an order that makes the
-//    accumulator directly the B operand of the P.V MFMA (no shuffles), and V
-//    arrives pre-transposed (V^T) so its A operand is one 16-byte LDS read.
+// Shared design (MI355X-first):
+//  * A wave owns 64 queries (one 64-token query block) of one head; its O
+//    accumulator (64 x 128 fp32) lives in AGPRs. S^T = K Q^T runs on
+//    v_mfma_f32_32x32x16_bf16 with queries along the lanes, so a query's
+//    scores sit in one lane pair; every K or V^T operand read from LDS feeds
+//    two MFMAs (two 32-query tiles), halving LDS traffic per flop.
+//  * Key rows are placed so that the S^T accumulator is directly the B
+//    operand of the P.V MFMA (no shuffles), and V arrives pre-transposed (V^T)
+//    so its A operand is one 16-byte read.
 //  * Online softmax in base 2 with lazy rescaling: the running max moves only
-//    when a tile exceeds it by more than 8 (in log2 units), so the O rescale is
+//    when a tile exceeds it by more than 8 (log2 units), so the O rescale is
 //    rare; exact because the final normalisation uses the same reference.
-//  * Masks are evaluated only on tiles that straddle the causal diagonal or
-//    the window's lower edge; tiles outside every query's set are skipped
-//    (the pages' point about SWA without three-segment KV concat or a custom
-//    mask tensor, RTP-LLM section of the Synced article).
+//  * Software pipeline: the QK MFMAs of tile t+1 are issued next to the
+//    exp/pack VALU work of tile t, then P.V of tile t, so the matrix and vector
+//    units overlap.
+//  * Masks only on tiles that straddle the causal diagonal or the window's
+//    lower edge; tiles outside a wave's set are skipped (the pages' point
+//    about SWA without three-segment KV concat or a mask tensor, RTP-LLM
+//    section of the Synced article).
 //  * Work order: query blocks from last to first (heaviest first, the pages'
-//    sparsity-aware scheduling), items of one query block grouped onto one
-//    XCD so heads sharing a KV head share that XCD's L2.
+//    sparsity-aware scheduling).
+//
+// Window kernel: 4 waves = 4 (head, query block) jobs of one KV group share
+// one stream of 64-key tiles, staged by direct global->LDS loads
+// (global_load_lds_dwordx4) into a 3-deep LDS ring with an XOR swizzle.
+// Workgroups are interleaved over KV groups, so with round-robin placement
+// each XCD serves one KV group from its own L2.
+//
+// Sparse kernel: each wave runs its own (retrieval head, query block) job over
+// its block list in 32-key half tiles: K goes straight into registers in MFMA
+// operand layout (vector-memory path), V^T through a per-wave LDS slot (LDS
+// DMA path), so the gather traffic is split over both paths.
 #include "common.h"
 
 namespace rtp {
 
-constexpr int KSTR = 136;             // LDS row of K: 128 bf16 + 16 B pad
-constexpr int VSTR = 72;              // LDS row of V^T: 64 bf16 + 16 B pad
-constexpr int K_ELEMS = 64 * KSTR;
-constexpr int V_ELEMS = 128 * VSTR;
-constexpr int STAGE = K_ELEMS + V_ELEMS;  // bf16 elements per pipeline stage
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-struct AttnParams {
-  AttnLaunch a;
-  float c;      // scale * log2(e)
-  float tau;    // lazy-rescale threshold, raw logit units
-  int n_items, per_qb, chunk;
-  uint32_t desc[kMaxHeads];
-};
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
+// s_waitcnt vmcnt(8), other counters at their maximum (gfx9 encoding)
+__device__ __forceinline__ void wait_vm8() {
+  __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
+}
 
-// Key row r of a 32-key sub-tile is stored at LDS row perm(r) (swap bits 2
-// and 3). Then accumulator element i of lane l of S^T = K Q^T holds key
-// 16*(i/8) + 8*(l/32) + i%8 of the sub-tile: the 8 values a lane feeds as the
-// B operand of one P.V MFMA step are 8 consecutive keys.
+// Row of a 32-key sub-tile that MFMA row m reads: swap bits 2 and 3. Then
+// accumulator element i of lane l of S^T holds key 16*(i/8) + 8*(l/32) + i%8
+// of the sub-tile, i.e. the 8 values a lane feeds to one P.V step are 8
+// consecutive keys.
 __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// ------------------------------------------------------------ softmax core
+// One 32-key sub-tile x two 32-query tiles of scores.
+struct Soft {
+  float mref[2];
+  float lsum[2];
+};
+
+// max over the scores of a tile for query tile j (lane pair combined)
 template <int NS>
-__device__ __forceinline__ void process_tile(
-    const u16* __restrict__ sk, const u16* __restrict__ sv, int k0, int sub0,
-    const bf16x8 (&qf)[8], f32x16 (&acc)[4], float& m_ref, float& lsum,
-    int qi, int qmin, int window, float c, float tau, int lane) {
-  const int g = lane >> 5, n = lane & 31;
-  const int qmax = qmin + 31;
-  f32x16 s[NS];
-  bool act[NS];
-  bool any = false;
-  float tmax = -INFINITY;
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[NS][2], int j) {
+  float m = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const int st = sub0 + u;
-    const int kmin = k0 + 32 * st, kmax = kmin + 31;
-    act[u] = !(kmin > qmax || kmax <= qmin - window);
-    any |= act[u];
-    if (act[u]) {
-      f32x16 z = {};
-      s[u] = z;
-      const u16* arow = sk + (32 * st + n) * KSTR + 8 * g;
+  for (int u = 0; u < NS; ++u)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s[u] = mfma32(*reinterpret_cast<const bf16x8*>(arow + 16 * ks), qf[ks],
-                      s[u]);
-      if (kmax > qmin || kmin <= qmax - window) {
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, s[u][j][i]);
+  return fmaxf(m, __shfl_xor(m, 32));
+}
+
+// Lazy rescale: move the reference only when the tile max exceeds it by tau.
+template <int NS>
+__device__ __forceinline__ void rescale(const f32x16 (&s)[NS][2], Soft& sf,
+                                        f32x16 (&acc)[2][4], float c,
+                                        float tau) {
+  float alpha[2];
+  bool need = false;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kmin + 16 * (i >> 3) + 8 * g + (i & 7);
-          const bool ok = key <= qi && key > qi - window;
-          s[u][i] = ok ? s[u][i] : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[u][i]);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const float tm = tile_max<NS>(s, j);
+    const bool nj = tm > sf.mref[j] + tau;
+    alpha[j] = nj ? fast_exp2((sf.mref[j] - tm) * c) : 1.f;
+    sf.mref[j] = nj ? tm : sf.mref[j];
+    sf.lsum[j] *= alpha[j];
+    need |= nj;
   }
-  if (!any) return;  // wave-uniform
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  if (tmax > m_ref + tau) {
-    const float alpha = fast_exp2((m_ref - tmax) * c);
-    m_ref = tmax;
-    lsum *= alpha;
+  if (__any(need)) {  // wave-uniform: rare after the first tiles
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mt][i] *= alpha;
-  }
-  const float mc = m_ref * c;
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    if (!act[u]) continue;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pv = fast_exp2(fmaf(s[u][i], c, -mc));
-      lsum += pv;
-      pb[i >> 3][i & 7] = (__bf16)pv;
-    }
-    const int st = sub0 + u;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const u16* vrow = sv + (32 * mt + n) * VSTR + 32 * st + 16 * ks + 8 * g;
-        acc[mt] = mfma32(*reinterpret_cast<const bf16x8*>(vrow), pb[ks],
-                         acc[mt]);
-      }
+        for (int i = 0; i < 16; ++i) acc[j][mt][i] *= alpha[j];
   }
 }
 
-__global__ __launch_bounds__(256, 2) void attn_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * STAGE];
-  const AttnLaunch& a = p.a;
-  const int nb = a.n_b;
-  const int S = a.S;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// exp of one tile's scores against the current references; packs bf16 P
+// (the B operand of P.V) and adds the packed values to the row sums.
+template <int NS>
+__device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2], Soft& sf,
+                                         bf16x8 (&pb)[NS][2][2], float c) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float mc = sf.mref[j] * c;
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = fast_exp2(fmaf(s[u][j][i], c, -mc));
+        ls += pv;
+        pb[u][j][i >> 3][i & 7] = (__bf16)pv;
+      }
+    sf.lsum[j] += ls;
+  }
+}
+
+// Mask scores of sub-tile starting at key kmin for query tiles with first
+// query q0 (+32 for the second): valid iff key <= i and key > i - window.
+__device__ __forceinline__ void mask_sub(f32x16 (&s)[2], int kmin, int q0,
+                                         int window, int lane) {
   const int g = lane >> 5, n = lane & 31;
-
-  // XCD-aware order: consecutive workgroups land on different XCDs, so give
-  // each XCD runs of `chunk` consecutive logical items.
-  int item = blockIdx.x;
-  {
-    const int grp = 8 * p.chunk;
-    const int full = (p.n_items / grp) * grp;
-    if (item < full) {
-      const int x = item & 7, s = item >> 3;
-      item = (s / p.chunk) * grp + x * p.chunk + (s % p.chunk);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qi = q0 + 32 * j + n;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kmin + 16 * (i >> 3) + 8 * g + (i & 7);
+      const bool ok = key <= qi && key > qi - window;
+      s[j][i] = ok ? s[j][i] : -INFINITY;
     }
   }
-  const int qb = nb - 1 - item / p.per_qb;  // heaviest (last) blocks first
-  const uint32_t desc = p.desc[item % p.per_qb];
-  const int kind = desc & 3;
-  const int ha = (desc >> 8) & 255, hb = (desc >> 16) & 255;
-  const int rho = desc >> 24;
-  const int head = (kind == 0 && wave >= 2) ? hb : ha;
-  const int kvh = ha / a.G;
-  const int qmin = qb * 64 + 32 * (wave & 1);
-  const int qi = qmin + n;
-  const int window = (kind == 2) ? (1 << 30) : a.window;
+}
 
-  int kt_lo = 0, nt;
-  const int32_t* sel_row = nullptr;
-  if (kind == 2) {
-    sel_row = a.sel + ((size_t)rho * nb + qb) * a.sel_stride;
-    nt = a.sel_cnt[(size_t)rho * nb + qb];
-    nt = nt < 0 ? 0 : (nt > a.sel_stride ? a.sel_stride : nt);
-  } else {
-    const int lo = qb * 64 - window + 1;
-    kt_lo = lo > 0 ? (lo >> 6) : 0;
-    nt = qb - kt_lo + 1;
-  }
-  auto tile_of = [&](int t) -> int {
-    if (kind != 2) return kt_lo + t;
-    int kb = sel_row[t];
-    return kb < 0 ? 0 : (kb > qb ? qb : kb);  // memory-safe on bad input
-  };
-
-  bf16x8 qf[8];
-  {
-    const u16* qp = a.q + ((size_t)head * S + (qi < S ? qi : 0)) * kD + 8 * g;
+__device__ __forceinline__ void store_out(const f32x16 (&acc)[2][4],
+                                          const Soft& sf, float c, u16* out,
+                                          float* lse, int head, int q0, int S,
+                                          int lane) {
+  const int g = lane >> 5, n = lane & 31;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
-      if (qi >= S) { bf16x8 z = {}; v = z; }
-      qf[ks] = v;
-    }
-  }
-
-  const u16* kbase = a.k + (size_t)kvh * S * kD;
-  const u16* vtbase = a.vt + (size_t)kvh * kD * a.S_pad;
-  uint4 kreg[4], vreg[4];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i, row = cidx >> 4, ch = cidx & 15;
-      const int key = kb * 64 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < S)
-        v = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kD + ch * 8);
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i, dr = cidx >> 3, ch = cidx & 7;
-      vreg[i] = *reinterpret_cast<const uint4*>(
-          vtbase + (size_t)dr * a.S_pad + kb * 64 + ch * 8);
-    }
-  };
-  auto sstore = [&](u16* st) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i, row = cidx >> 4, ch = cidx & 15;
-      *reinterpret_cast<uint4*>(st + perm_row(row) * KSTR + ch * 8) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = tid + 256 * i, dr = cidx >> 3, ch = cidx & 7;
-      *reinterpret_cast<uint4*>(st + K_ELEMS + dr * VSTR + ch * 8) = vreg[i];
-    }
-  };
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    f32x16 z = {};
-    acc[mt] = z;
-  }
-  float m_ref = -1e30f, lsum = 0.f;
-
-  if (nt > 0) {
-    gload(tile_of(0));
-    sstore(smem);
-  }
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    u16* cur = smem + (t & 1) * STAGE;
-    u16* nxt = smem + ((t + 1) & 1) * STAGE;
-    if (t + 1 < nt) gload(tile_of(t + 1));
-    const int k0 = tile_of(t) * 64;
-    if (kind == 0)
-      process_tile<2>(cur, cur + K_ELEMS, k0, 0, qf, acc, m_ref, lsum, qi,
-                      qmin, window, p.c, p.tau, lane);
-    else
-      process_tile<1>(cur, cur + K_ELEMS, k0, wave >> 1, qf, acc, m_ref, lsum,
-                      qi, qmin, window, p.c, p.tau, lane);
-    if (t + 1 < nt) sstore(nxt);
-    __syncthreads();
-  }
-
-  lsum += __shfl_xor(lsum, 32);
-  if (kind != 0) {
-    // merge the two key halves: waves 2,3 hand (m, l, O) to waves 0,1
-    float* xs = reinterpret_cast<float*>(smem);
-    if (wave >= 2) {
-      float* d = xs + (wave - 2) * 66 * 64 + lane;
-      d[0] = m_ref;
-      d[64] = lsum;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) d[(2 + mt * 16 + i) * 64] = acc[mt][i];
-    }
-    __syncthreads();
-    if (wave < 2) {
-      const float* s2 = xs + wave * 66 * 64 + lane;
-      const float m2 = s2[0], l2 = s2[64];
-      const float mm = fmaxf(m_ref, m2);
-      const float a1 = fast_exp2((m_ref - mm) * p.c);
-      const float a2 = fast_exp2((m2 - mm) * p.c);
-      lsum = lsum * a1 + l2 * a2;
-      m_ref = mm;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc[mt][i] = acc[mt][i] * a1 + s2[(2 + mt * 16 + i) * 64] * a2;
-    }
-  }
-  if (kind != 0 && wave >= 2) return;
-  if (qi < S) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    u16* op = a.out + ((size_t)head * S + qi) * kD;
+  for (int j = 0; j < 2; ++j) {
+    const int qi = q0 + 32 * j + n;
+    const float l = sf.lsum[j] + __shfl_xor(sf.lsum[j], 32);
+    if (qi >= S) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    u16* op = out + ((size_t)head * S + qi) * kD;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * mt + 8 * q4 + 4 * g;
         uint2 w;
-        w.x = (uint32_t)f2bf(acc[mt][4 * q4 + 0] * inv) |
-              ((uint32_t)f2bf(acc[mt][4 * q4 + 1] * inv) << 16);
-        w.y = (uint32_t)f2bf(acc[mt][4 * q4 + 2] * inv) |
-              ((uint32_t)f2bf(acc[mt][4 * q4 + 3] * inv) << 16);
+        w.x = (uint32_t)f2bf(acc[j][mt][4 * q4 + 0] * inv) |
+              ((uint32_t)f2bf(acc[j][mt][4 * q4 + 1] * inv) << 16);
+        w.y = (uint32_t)f2bf(acc[j][mt][4 * q4 + 2] * inv) |
+              ((uint32_t)f2bf(acc[j][mt][4 * q4 + 3] * inv) << 16);
         *reinterpret_cast<uint2*>(op + d0) = w;
       }
-    if (a.lse && g == 0)
-      a.lse[(size_t)head * S + qi] =
-          (m_ref * p.c + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f;
+    if (lse && g == 0)
+      lse[(size_t)head * S + qi] =
+          (sf.mref[j] * c + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
   }
 }
 
-// V [Hkv,S,128] -> V^T [Hkv,128,S_pad], zero beyond S.
+__device__ __forceinline__ void load_q(const u16* q, int head, int q0, int S,
+                                       bf16x8 (&qf)[2][8], int lane) {
+  const int g = lane >> 5, n = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qi = q0 + 32 * j + n;
+    const u16* qp = q + ((size_t)head * S + (qi < S ? qi : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      if (qi >= S) { bf16x8 z = {}; v = z; }
+      qf[j][ks] = v;
+    }
+  }
+}
+
+// =====================================================================
+// Window / dense kernel
+// =====================================================================
+constexpr int WSTAGES = 3;
+// Padded LDS rows (conflict-free for 8 consecutive rows, and every operand
+// address of a lane is one base register plus an immediate offset).
+constexpr int KROW_B = 272;                 // 256 B of K + 16 B pad
+constexpr int VROW_B = 144;                 // 128 B of V^T + 16 B pad
+constexpr int KTILE_B = 64 * KROW_B;        // 17408
+constexpr int VTILE_B = 128 * VROW_B;       // 18432
+constexpr int STAGE_B = KTILE_B + VTILE_B;  // 35840
+constexpr int K_DMA = KTILE_B / 1024;       // 17 loads of 1 KB
+constexpr int V_DMA = VTILE_B / 1024;       // 18 loads of 1 KB
+constexpr int DMA_PER_WAVE = (K_DMA + V_DMA + 3) / 4;  // 9
+
+struct WinParams {
+  const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
+  int S, S_pad, n_b, Hkv, window;
+  float c, tau;
+  uint8_t hlist[kMaxHeads];   // window heads grouped by KV head
+  int16_t hoff[kMaxHeads + 1];
+};
+
+// The 35 DMA loads of a tile (17 K, 18 V^T) are dealt round-robin to the 4
+// waves. Load i writes LDS bytes [1024 i, 1024 i + 1024) of the stage (K rows
+// first, then V^T rows); a lane's 16-byte unit either holds data or is a pad
+// unit (then it re-reads a neighbouring chunk). A lane's global byte offset
+// inside a tile does not depend on the tile, so it is computed once.
+// K row r (MFMA row order) holds key (r & 32) + perm_row(r & 31).
+struct WinLaneOffsets {
+  uint32_t off[DMA_PER_WAVE];
+};
+
+__device__ __forceinline__ uint32_t win_unit_offset(int ld, int lane,
+                                                    int S_pad) {
+  if (ld < K_DMA) {
+    const int u = 64 * ld + lane;
+    const int r = u / 17, c = min(u % 17, 15);
+    return (uint32_t)(((r & 32) + perm_row(r & 31)) * 256 + c * 16);
+  }
+  const int u = 64 * (ld - K_DMA) + lane;
+  const int d = u / 9, c = min(u % 9, 7);
+  return (uint32_t)(d * S_pad * 2 + c * 16);
+}
+
+__device__ __forceinline__ WinLaneOffsets win_offsets(int S_pad, int wave,
+                                                      int lane) {
+  WinLaneOffsets o;
+#pragma unroll
+  for (int j = 0; j < DMA_PER_WAVE; ++j) {
+    const int ld = wave + 4 * j;
+    o.off[j] = ld < K_DMA + V_DMA ? win_unit_offset(ld, lane, S_pad) : 0u;
+  }
+  return o;
+}
+
+__device__ __attribute__((noinline)) void win_issue_ragged_k(
+    const WinParams& p, int g, int kb, char* stage, int ld, int lane) {
+  const int u = 64 * ld + lane;
+  const int r = u / 17, c = min(u % 17, 15);
+  int key = kb * 64 + (r & 32) + perm_row(r & 31);
+  key = key < p.S ? key : p.S - 1;
+  dma16(p.k + ((size_t)g * p.S + key) * kD + c * 8, stage + ld * 1024);
+}
+
+__device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
+                                          char* stage, const WinLaneOffsets& o,
+                                          int wave, int lane) {
+  const char* kt = reinterpret_cast<const char*>(p.k) +
+                   ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
+  const char* vt = reinterpret_cast<const char*>(p.vt) +
+                   ((size_t)g * kD * p.S_pad + (size_t)kb * 64) * 2;
+  const bool ragged = (kb + 1) * 64 > p.S;  // last block of a ragged S
+#pragma unroll
+  for (int j = 0; j < DMA_PER_WAVE; ++j) {
+    const int ld = wave + 4 * j;  // wave-uniform
+    if (ld < K_DMA) {
+      if (!ragged) {
+        dma16(kt + o.off[j], stage + ld * 1024);
+      } else {  // rows past S re-read row S-1 (masked anyway)
+        win_issue_ragged_k(p, g, kb, stage, ld, lane);
+      }
+    } else if (ld < K_DMA + V_DMA) {
+      dma16(vt + o.off[j], stage + ld * 1024);
+    }
+  }
+}
+
+// S^T for one 32-key sub-tile st of a staged tile: s[0][j], j = query tile
+__device__ __forceinline__ void win_qk(const char* stage, int st,
+                                       const bf16x8 (&qf)[2][8],
+                                       f32x16 (&s)[1][2], int lane) {
+  const int g = lane >> 5, n = lane & 31;
+  f32x16 z = {};
+  s[0][0] = z;
+  s[0][1] = z;
+  const char* row = stage + (32 * st + n) * KROW_B + 16 * g;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(row + 32 * ks);
+    s[0][0] = mfma32(a, qf[0][ks], s[0][0]);
+    s[0][1] = mfma32(a, qf[1][ks], s[0][1]);
+  }
+}
+
+__device__ __forceinline__ void win_pv(const char* stage, int st,
+                                       const bf16x8 (&pb)[1][2][2],
+                                       f32x16 (&acc)[2][4], int lane) {
+  const int g = lane >> 5, n = lane & 31;
+  const char* base = stage + KTILE_B + n * VROW_B + 16 * g + 64 * st;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+          base + 32 * mt * VROW_B + 32 * ks);
+      acc[0][mt] = mfma32(a, pb[0][0][ks], acc[0][mt]);
+      acc[1][mt] = mfma32(a, pb[0][1][ks], acc[1][mt]);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[WSTAGES * STAGE_B];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = blockIdx.x % p.Hkv;
+  const int ig = blockIdx.x / p.Hkv;
+  const int h0 = p.hoff[g], nsw = p.hoff[g + 1] - h0;
+  const int njobs = nsw * p.n_b;
+  if (nsw == 0 || 4 * ig >= njobs) return;  // whole workgroup
+  const int job = 4 * ig + wave;
+  const bool active = job < njobs;  // idle waves still stage tiles
+  const int jl = active ? job : njobs - 1;
+  const int qb = p.n_b - 1 - jl / nsw;
+  const int head = p.hlist[h0 + jl % nsw];
+  const int q0 = qb * 64;
+  const int w = p.window;
+  // union tile range of the workgroup's jobs (at most two query blocks)
+  const int qb_hi = p.n_b - 1 - (4 * ig) / nsw;
+  const int qb_lo = p.n_b - 1 - min(4 * ig + 3, njobs - 1) / nsw;
+  const int lo = qb_lo * 64 - w + 1;
+  const int kt_lo = lo > 0 ? (lo >> 6) : 0;
+  const int nt = qb_hi - kt_lo + 1;
+  // A 32-key sub-tile needs masking unless every key is inside every query's
+  // window; sub-tiles entirely outside (edges only) are masked to nothing.
+  auto masked = [&](int kmin) -> bool {
+    const int kmax = kmin + 31, qmax = q0 + 63;
+    return !(kmax <= q0 && kmin > qmax - w);
+  };
+  const WinLaneOffsets off = win_offsets(p.S_pad, wave, lane);
+
+  bf16x8 qf[2][8];
+  load_q(p.q, head, q0, p.S, qf, lane);
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 z = {};
+      acc[j][mt] = z;
+    }
+  Soft sf;
+  sf.mref[0] = sf.mref[1] = -1e30f;
+  sf.lsum[0] = sf.lsum[1] = 0.f;
+
+  win_issue(p, g, kt_lo, smem, off, wave, lane);
+  if (nt > 1) win_issue(p, g, kt_lo + 1, smem + STAGE_B, off, wave, lane);
+  wait_vm_all();
+  __syncthreads();
+  f32x16 s[1][2];
+  bf16x8 pb[1][2][2];
+  win_qk(smem, 0, qf, s, lane);
+  if (masked(kt_lo * 64)) mask_sub(s[0], kt_lo * 64, q0, w, lane);
+  rescale<1>(s, sf, acc, p.c, p.tau);
+  // step u works on 32-key sub-tile u (tile u/2, half u%2): the QK MFMAs of
+  // sub-tile u+1 run next to the exp/pack of sub-tile u, then P.V(u)
+  const int nu = 2 * nt;
+  for (int u = 0; u + 1 < nu; ++u) {
+    const int tn = (u + 1) >> 1;
+    if (u & 1) {  // sub-tile u+1 opens tile tn
+      wait_vm_all();
+      __syncthreads();  // tile tn resident; stage of tile tn-2 free
+      if (tn + 1 < nt)
+        win_issue(p, g, kt_lo + tn + 1, smem + ((tn + 1) % WSTAGES) * STAGE_B,
+                  off, wave, lane);
+    }
+    f32x16 sn[1][2];
+    win_qk(smem + (tn % WSTAGES) * STAGE_B, (u + 1) & 1, qf, sn, lane);
+    exp_pack<1>(s, sf, pb, p.c);
+    win_pv(smem + ((u >> 1) % WSTAGES) * STAGE_B, u & 1, pb, acc, lane);
+    const int kn = (kt_lo + tn) * 64 + 32 * ((u + 1) & 1);
+    if (masked(kn)) mask_sub(sn[0], kn, q0, w, lane);
+    rescale<1>(sn, sf, acc, p.c, p.tau);
+    s[0][0] = sn[0][0];
+    s[0][1] = sn[0][1];
+  }
+  exp_pack<1>(s, sf, pb, p.c);
+  win_pv(smem + ((nt - 1) % WSTAGES) * STAGE_B, 1, pb, acc, lane);
+  if (active) store_out(acc, sf, p.c, p.out, p.lse, head, q0, p.S, lane);
+}
+
+// =====================================================================
+// Sparse kernel
+// =====================================================================
+constexpr int VHALF_B = 8192;  // V^T of 32 keys: 128 d x 64 B
+
+struct SparseParams {
+  const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
+  const int32_t* sel; const int32_t* sel_cnt;
+  int sel_stride, S, S_pad, n_b, G, n_ret, n_jobs;
+  float c, tau;
+  uint8_t head_of_rho[kMaxHeads];
+};
+
+// V^T half tile (32 keys): row d x 4 chunks of 16 B, chunk c at
+// c ^ ((d >> 1) & 3).
+__device__ __forceinline__ void sp_issue_v(const u16* vbase, int S_pad, int k0,
+                                           char* slot, int lane) {
+#pragma unroll
+  for (int ins = 0; ins < 8; ++ins) {
+    const int u = 64 * ins + lane;
+    const int d = u >> 2, cs = u & 3;
+    const int c = cs ^ ((d >> 1) & 3);
+    dma16(vbase + (size_t)d * S_pad + k0 + c * 8, slot + ins * 1024);
+  }
+}
+
+// K operand of a 32-key half tile straight from global memory: lane l holds
+// the row of MFMA row l%32 (key perm_row(l%32)), 8 d-chunks.
+__device__ __forceinline__ void sp_load_k(const u16* kbase, int S, int k0,
+                                          bf16x8 (&kr)[8], int lane) {
+  const int g = lane >> 5, n = lane & 31;
+  int key = k0 + perm_row(n);
+  key = key < S ? key : S - 1;
+  const u16* kp = kbase + (size_t)key * kD + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    kr[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+}
+
+__device__ __forceinline__ void sp_qk(const bf16x8 (&kr)[8],
+                                      const bf16x8 (&qf)[2][8],
+                                      f32x16 (&s)[1][2]) {
+  f32x16 z = {};
+  s[0][0] = z;
+  s[0][1] = z;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s[0][0] = mfma32(kr[ks], qf[0][ks], s[0][0]);
+    s[0][1] = mfma32(kr[ks], qf[1][ks], s[0][1]);
+  }
+}
+
+__device__ __forceinline__ void sp_pv(const char* slot,
+                                      const bf16x8 (&pb)[1][2][2],
+                                      f32x16 (&acc)[2][4], int lane) {
+  const int g = lane >> 5, n = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int d = 32 * mt + n;
+      const int c = (2 * ks + g) ^ ((d >> 1) & 3);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + d * 64 + c * 16);
+      acc[0][mt] = mfma32(a, pb[0][0][ks], acc[0][mt]);
+      acc[1][mt] = mfma32(a, pb[0][1][ks], acc[1][mt]);
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * VHALF_B];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int job = 4 * blockIdx.x + wave;
+  if (job >= p.n_jobs) return;  // waves are independent: no block barriers
+  const int rho = job % p.n_ret;
+  const int qb = p.n_b - 1 - job / p.n_ret;
+  const int head = p.head_of_rho[rho];
+  const int g = head / p.G;
+  const int q0 = qb * 64;
+  const int S = p.S;
+  const int32_t* list = p.sel + ((size_t)rho * p.n_b + qb) * p.sel_stride;
+  int cnt = p.sel_cnt[(size_t)rho * p.n_b + qb];
+  cnt = cnt < 0 ? 0 : (cnt > p.sel_stride ? p.sel_stride : cnt);
+  const int nt = 2 * cnt;  // 32-key half tiles
+  char* slots = smem + wave * 2 * VHALF_B;
+  const u16* kbase = p.k + (size_t)g * S * kD;
+  const u16* vbase = p.vt + (size_t)g * kD * p.S_pad;
+  auto tile_k0 = [&](int t) -> int {
+    int kb = list[t >> 1];
+    kb = kb < 0 ? 0 : (kb > qb ? qb : kb);  // memory-safe on bad input
+    return kb * 64 + 32 * (t & 1);
+  };
+  // only half tiles of the diagonal block straddle the causal edge; a half
+  // tile entirely after every query is masked to nothing
+  auto masked = [&](int k0) -> bool { return k0 + 31 > q0; };
+
+  bf16x8 qf[2][8];
+  load_q(p.q, head, q0, S, qf, lane);
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 z = {};
+      acc[j][mt] = z;
+    }
+  Soft sf;
+  sf.mref[0] = sf.mref[1] = -1e30f;
+  sf.lsum[0] = sf.lsum[1] = 0.f;
+  if (nt == 0) {
+    store_out(acc, sf, p.c, p.out, p.lse, head, q0, S, lane);
+    return;
+  }
+
+  // prologue: K(0), V(0), K(1), V(1) in flight
+  bf16x8 kr[8];
+  int k0c = tile_k0(0);
+  sp_load_k(kbase, S, k0c, kr, lane);
+  sp_issue_v(vbase, p.S_pad, k0c, slots, lane);
+  int k0n = k0c;
+  if (nt > 1) {
+    k0n = tile_k0(1);
+    sp_issue_v(vbase, p.S_pad, k0n, slots + VHALF_B, lane);
+  }
+  wait_vm_all();
+  f32x16 s[1][2];
+  sp_qk(kr, qf, s);
+  if (masked(k0c)) mask_sub(s[0], k0c, q0, 1 << 30, lane);
+  rescale<1>(s, sf, acc, p.c, p.tau);
+  if (nt > 1) sp_load_k(kbase, S, k0n, kr, lane);
+  bf16x8 pb[1][2][2];
+  for (int t = 0; t + 1 < nt; ++t) {
+    // K(t+1) registers and V(t) slot are ready once everything issued
+    // before V(t+1) has landed
+    wait_vm8();
+    f32x16 sn[1][2];
+    sp_qk(kr, qf, sn);
+    exp_pack<1>(s, sf, pb, p.c);
+    sp_pv(slots + (t & 1) * VHALF_B, pb, acc, lane);
+    const int k0cur = k0n;
+    if (t + 2 < nt) {  // prefetch tile t+2: K to registers, V^T to the slot
+      k0n = tile_k0(t + 2);
+      sp_load_k(kbase, S, k0n, kr, lane);
+      wait_lgkm0();  // this wave's reads of the slot are done
+      sp_issue_v(vbase, p.S_pad, k0n, slots + (t & 1) * VHALF_B, lane);
+    }
+    if (masked(k0cur)) mask_sub(sn[0], k0cur, q0, 1 << 30, lane);
+    rescale<1>(sn, sf, acc, p.c, p.tau);
+    s[0][0] = sn[0][0];
+    s[0][1] = sn[0][1];
+  }
+  wait_vm_all();
+  exp_pack<1>(s, sf, pb, p.c);
+  sp_pv(slots + ((nt - 1) & 1) * VHALF_B, pb, acc, lane);
+  store_out(acc, sf, p.c, p.out, p.lse, head, q0, S, lane);
+}
+
+// =====================================================================
+// V transpose: V [Hkv,S,128] -> V^T [Hkv,128,S_pad], zero beyond S
+// =====================================================================
+constexpr int TSTR = 136;
 __global__ __launch_bounds__(256) void transpose_v_kernel(
     const u16* __restrict__ v, u16* __restrict__ vt, int S, int S_pad) {
-  __shared__ __attribute__((aligned(16))) u16 t[64 * KSTR];
+  __shared__ __attribute__((aligned(16))) u16 t[64 * TSTR];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const u16* src = v + (size_t)g * S * kD;
 #pragma unroll
@@ -310,7 +568,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
     const int key = kb * 64 + row;
     uint4 x = make_uint4(0, 0, 0, 0);
     if (key < S) x = *reinterpret_cast<const uint4*>(src + (size_t)key * kD + ch * 8);
-    *reinterpret_cast<uint4*>(t + row * KSTR + ch * 8) = x;
+    *reinterpret_cast<uint4*>(t + row * TSTR + ch * 8) = x;
   }
   __syncthreads();
 #pragma unroll
@@ -319,8 +577,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[(kc * 8 + 2 * e) * KSTR + dr] |
-             ((uint32_t)t[(kc * 8 + 2 * e + 1) * KSTR + dr] << 16);
+      w[e] = (uint32_t)t[(kc * 8 + 2 * e) * TSTR + dr] |
+             ((uint32_t)t[(kc * 8 + 2 * e + 1) * TSTR + dr] << 16);
     *reinterpret_cast<uint4*>(vt + ((size_t)g * kD + dr) * S_pad + kb * 64 + kc * 8) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -336,19 +594,56 @@ hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnLaunch& a, const AttnItems& items,
+hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
                             hipStream_t st) {
-  if (a.n_b == 0 || items.n == 0) return hipSuccess;
-  AttnParams p;
-  p.a = a;
-  p.c = a.scale * 1.4426950408889634f;
-  p.tau = 8.0f / p.c;
-  p.per_qb = items.n;
-  p.n_items = a.n_b * items.n;
-  p.chunk = items.n;
-  for (int i = 0; i < kMaxHeads; ++i) p.desc[i] = i < items.n ? items.desc[i] : 0;
-  prof_begin("attn", st);
-  hipLaunchKernelGGL(attn_kernel, dim3(p.n_items), dim3(256), 0, st, p);
+  if (a.n_b == 0) return hipSuccess;
+  const int Hq = a.G * a.Hkv;
+  const float c = a.scale * 1.4426950408889634f;
+  // window heads
+  WinParams wp;
+  wp.q = a.q; wp.k = a.k; wp.vt = a.vt; wp.out = a.out; wp.lse = a.lse;
+  wp.S = a.S; wp.S_pad = a.S_pad; wp.n_b = a.n_b; wp.Hkv = a.Hkv;
+  wp.window = a.window;
+  wp.c = c;
+  wp.tau = 8.0f / c;
+  int nl = 0, max_items = 0;
+  for (int g = 0; g < a.Hkv; ++g) {
+    wp.hoff[g] = (int16_t)nl;
+    int cnt = 0;
+    for (int h = g * a.G; h < (g + 1) * a.G; ++h)
+      if (!(is_ret && is_ret[h])) {
+        wp.hlist[nl++] = (uint8_t)h;
+        ++cnt;
+      }
+    max_items = max(max_items, (cnt * a.n_b + 3) / 4);
+  }
+  wp.hoff[a.Hkv] = (int16_t)nl;
+  for (int i = nl; i < kMaxHeads; ++i) wp.hlist[i] = 0;
+  if (nl > 0) {
+    prof_begin("attn_window", st);
+    hipLaunchKernelGGL(attn_window_kernel, dim3(max_items * a.Hkv), dim3(256), 0,
+                       st, wp);
+    prof_end(st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // retrieval heads
+  int n_ret = 0;
+  SparseParams sp;
+  for (int h = 0; h < Hq; ++h)
+    if (is_ret && is_ret[h]) sp.head_of_rho[n_ret++] = (uint8_t)h;
+  if (n_ret == 0) return hipSuccess;
+  for (int i = n_ret; i < kMaxHeads; ++i) sp.head_of_rho[i] = 0;
+  sp.q = a.q; sp.k = a.k; sp.vt = a.vt; sp.out = a.out; sp.lse = a.lse;
+  sp.sel = a.sel; sp.sel_cnt = a.sel_cnt; sp.sel_stride = a.sel_stride;
+  sp.S = a.S; sp.S_pad = a.S_pad; sp.n_b = a.n_b; sp.G = a.G;
+  sp.n_ret = n_ret;
+  sp.n_jobs = n_ret * a.n_b;
+  sp.c = c;
+  sp.tau = 8.0f / c;
+  prof_begin("attn_sparse", st);
+  hipLaunchKernelGGL(attn_sparse_kernel, dim3((sp.n_jobs + 3) / 4), dim3(256), 0,
+                     st, sp);
   prof_end(st);
   return hipGetLastError();
 }

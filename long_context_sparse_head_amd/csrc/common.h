@@ -42,24 +42,17 @@ void prof_end(hipStream_t st);
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
-struct AttnItems {
-  // One entry per work item of a query block: bits 0-1 kind (0 = SWA head
-  // pair, 1 = single SWA head, 2 = single retrieval head), bits 8-15 head a,
-  // bits 16-23 head b, bits 24-31 retrieval index of head a.
-  uint32_t desc[kMaxHeads];
-  int n;
-};
-
 struct AttnLaunch {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
   const int32_t* sel; const int32_t* sel_cnt; int sel_stride;
-  int S, S_pad, n_b, G, window;
+  int S, S_pad, n_b, G, Hkv, window;
   float scale;
 };
 
 hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
                               hipStream_t st);
-hipError_t launch_attention(const AttnLaunch& a, const AttnItems& items,
+// is_ret: host [Hq]; nullptr means every head is a window head.
+hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
                             hipStream_t st);
 
 struct IndexerLaunch {
