@@ -75,6 +75,7 @@ def load():
             raise RtpError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m long_context_sparse_head_amd.build`")
+        _warn_if_stale()
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)
@@ -82,6 +83,19 @@ def load():
             fn.argtypes = args
         _lib = lib
     return _lib
+
+
+def _warn_if_stale():
+    import warnings
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    try:
+        newest = max(os.path.getmtime(os.path.join(src, f))
+                     for f in os.listdir(src))
+    except (OSError, ValueError):
+        return
+    if newest > os.path.getmtime(LIB_PATH):
+        warnings.warn(f"{LIB_PATH} is older than its sources in {src}; "
+                      "rebuild with `python -m long_context_sparse_head_amd.build`")
 
 
 def version() -> str:

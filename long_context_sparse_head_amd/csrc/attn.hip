@@ -18,9 +18,9 @@
 //  * Key rows are placed so that the S^T accumulator is directly the B
 //    operand of the P.V MFMA (no shuffles), and V arrives pre-transposed (V^T)
 //    so its A operand is one 16-byte read.
-//  * Online softmax in base 2 with lazy rescaling: the running max moves only
-//    when a tile exceeds it by more than 8 (log2 units), so the O rescale is
-//    rare; exact because the final normalisation uses the same reference.
+//  * Softmax in base 2 against a fixed per-row reference taken from the
+//    row's diagonal key block, so O is never rescaled; a rare second pass
+//    covers rows whose scores climb far above that reference.
 //  * Software pipeline: the QK MFMAs of tile t+1 are issued next to the
 //    exp/pack VALU work of tile t, then P.V of tile t, so the matrix and vector
 //    units overlap.
@@ -68,7 +68,19 @@ __device__ __forceinline__ int perm_row(int r) {
 }
 
 // ------------------------------------------------------------ softmax core
-// One 32-key sub-tile x two 32-query tiles of scores.
+// Base-2 softmax with a fixed reference per query: m is the max score of the
+// query's own diagonal key half block (computed before the main pass), and
+// p = 2^(c s - c m) may exceed 1: fp32 and bf16 share the exponent range, so
+// values up to 2^64 lose nothing, and O and l share the reference, so O / l
+// is exact. The main pass only records whether a lane's partial sum of some
+// tile left that range (a score more than ~64 / c above m); if so (rare), a
+// max-only pass finds every row's true maximum and the job is recomputed
+// with it (then p <= 1). The O accumulator is touched only by MFMAs, which
+// keeps it resident in AGPRs with no per-tile rescale. Row sums use the
+// bf16-rounded p that also feeds the P.V MFMA.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
+
 struct Soft {
   float mref[2];
   float lsum[2];
@@ -85,51 +97,73 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NS][2], int j) {
   return fmaxf(m, __shfl_xor(m, 32));
 }
 
-// Lazy rescale: move the reference only when the tile max exceeds it by tau.
-template <int NS>
-__device__ __forceinline__ void rescale(const f32x16 (&s)[NS][2], Soft& sf,
-                                        f32x16 (&acc)[2][4], float c,
-                                        float tau) {
-  float alpha[2];
-  bool need = false;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float tm = tile_max<NS>(s, j);
-    const bool nj = tm > sf.mref[j] + tau;
-    alpha[j] = nj ? fast_exp2((sf.mref[j] - tm) * c) : 1.f;
-    sf.mref[j] = nj ? tm : sf.mref[j];
-    sf.lsum[j] *= alpha[j];
-    need |= nj;
-  }
-  if (__any(need)) {  // wave-uniform: rare after the first tiles
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][mt][i] *= alpha[j];
-  }
+// p = exp2(c s - c m) packed to bf16 (the B operand of P.V); ls = sum of the
+// packed values of this lane.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-// exp of one tile's scores against the current references; packs bf16 P
-// (the B operand of P.V) and adds the packed values to the row sums.
 template <int NS>
-__device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2], Soft& sf,
-                                         bf16x8 (&pb)[NS][2][2], float c) {
+__device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2],
+                                         const Soft& sf, bf16x8 (&pb)[NS][2][2],
+                                         float (&ls)[2], float c) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const float mc = sf.mref[j] * c;
-    float ls = 0.f;
+    float acc = 0.f;
 #pragma unroll
     for (int u = 0; u < NS; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[u][j][i], c, -mc));
-        ls += pv;
-        pb[u][j][i >> 3][i & 7] = (__bf16)pv;
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * h + 2 * e;
+          const float p0 = fast_exp2(fmaf(s[u][j][i], c, -mc));
+          const float p1 = fast_exp2(fmaf(s[u][j][i + 1], c, -mc));
+          w[e] = pack_bf16x2(p0, p1);
+          acc = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2, w[e]), one, acc, false);
+        }
+        const uint4 q4 = make_uint4(w[0], w[1], w[2], w[3]);
+        pb[u][j][h] = __builtin_bit_cast(bf16x8, q4);
       }
-    sf.lsum[j] += ls;
+    ls[j] = acc;
   }
+}
+
+// One tile against the current references: packs P, adds the row sums and
+// returns whether this lane's partial sum left the safe range. NaN (from NaN
+// inputs) does not count: raising the reference cannot remove it, so it just
+// propagates to the output.
+template <int NS>
+__device__ __forceinline__ bool softmax_step(const f32x16 (&s)[NS][2],
+                                             Soft& sf, bf16x8 (&pb)[NS][2][2],
+                                             float c) {
+  float ls[2];
+  exp_pack<NS>(s, sf, pb, ls, c);
+  sf.lsum[0] += ls[0];
+  sf.lsum[1] += ls[1];
+  return (ls[0] > kSumLimit) || (ls[1] > kSumLimit);
+}
+
+template <int NS>
+__device__ __forceinline__ void raise_refs(const f32x16 (&s)[NS][2],
+                                           Soft& sf) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sf.mref[j] = fmaxf(sf.mref[j], tile_max<NS>(s, j));
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[2][4]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x16 z = {};
+      acc[j][mt] = z;
+    }
 }
 
 // Mask scores of sub-tile starting at key kmin for query tiles with first
@@ -209,11 +243,13 @@ constexpr int STAGE_B = KTILE_B + VTILE_B;  // 35840
 constexpr int K_DMA = KTILE_B / 1024;       // 17 loads of 1 KB
 constexpr int V_DMA = VTILE_B / 1024;       // 18 loads of 1 KB
 constexpr int DMA_PER_WAVE = (K_DMA + V_DMA + 3) / 4;  // 9
+static_assert(K_DMA == 17 && V_DMA == 18 && DMA_PER_WAVE == 9,
+              "win_issue deals the loads for this split");
 
 struct WinParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
   int S, S_pad, n_b, Hkv, window;
-  float c, tau;
+  float c;
   uint8_t hlist[kMaxHeads];   // window heads grouped by KV head
   int16_t hoff[kMaxHeads + 1];
 };
@@ -260,6 +296,9 @@ __device__ __attribute__((noinline)) void win_issue_ragged_k(
   dma16(p.k + ((size_t)g * p.S + key) * kD + c * 8, stage + ld * 1024);
 }
 
+// Loads j = 0..3 of every wave are K rows, load 4 is K for wave 0 and V^T
+// for the others, loads 5..8 are V^T (wave 3 has no load 8). kt/vt: the
+// tile's first byte of K and of V^T.
 __device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
                                           char* stage, const WinLaneOffsets& o,
                                           int wave, int lane) {
@@ -267,20 +306,22 @@ __device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
                    ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
   const char* vt = reinterpret_cast<const char*>(p.vt) +
                    ((size_t)g * kD * p.S_pad + (size_t)kb * 64) * 2;
-  const bool ragged = (kb + 1) * 64 > p.S;  // last block of a ragged S
-#pragma unroll
-  for (int j = 0; j < DMA_PER_WAVE; ++j) {
-    const int ld = wave + 4 * j;  // wave-uniform
-    if (ld < K_DMA) {
-      if (!ragged) {
-        dma16(kt + o.off[j], stage + ld * 1024);
-      } else {  // rows past S re-read row S-1 (masked anyway)
-        win_issue_ragged_k(p, g, kb, stage, ld, lane);
-      }
-    } else if (ld < K_DMA + V_DMA) {
-      dma16(vt + o.off[j], stage + ld * 1024);
+  if ((kb + 1) * 64 > p.S) {  // last block of a ragged S: rows past S
+#pragma unroll 1                // re-read row S-1 (masked anyway)
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int ld = wave + 4 * j;
+      if (ld < K_DMA) win_issue_ragged_k(p, g, kb, stage, ld, lane);
+      else if (ld < K_DMA + V_DMA) dma16(vt + o.off[j], stage + ld * 1024);
     }
+    return;
   }
+  char* dst = stage + wave * 1024;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma16(kt + o.off[j], dst + j * 4096);
+  dma16((wave == 0 ? kt : vt) + o.off[4], dst + 4 * 4096);
+#pragma unroll
+  for (int j = 5; j < 8; ++j) dma16(vt + o.off[j], dst + j * 4096);
+  if (wave < 3) dma16(vt + o.off[8], dst + 8 * 4096);
 }
 
 // S^T for one 32-key sub-tile st of a staged tile: s[0][j], j = query tile
@@ -316,8 +357,64 @@ __device__ __forceinline__ void win_pv(const char* stage, int st,
     }
 }
 
+// K operand of a 32-key sub-tile straight from global memory: lane l holds
+// the row of MFMA row l%32 (key perm_row(l%32)), 8 d-chunks. koff is the
+// lane's byte offset inside a tile; rows past S (ragged last block) re-read
+// row S-1 (they are masked).
+__device__ __forceinline__ uint32_t k_lane_off(int lane) {
+  return (uint32_t)(perm_row(lane & 31) * 256 + 16 * (lane >> 5));
+}
+
+__device__ __forceinline__ void load_k_sub(const u16* kbase, int S, int k0,
+                                           uint32_t koff, bf16x8 (&kr)[8],
+                                           int lane) {
+  const char* kp;
+  if (k0 + 32 <= S) {
+    kp = reinterpret_cast<const char*>(kbase) + (size_t)k0 * 256 + koff;
+  } else {
+    int key = k0 + perm_row(lane & 31);
+    key = key < S ? key : S - 1;
+    kp = reinterpret_cast<const char*>(kbase + (size_t)key * kD) + 16 * (lane >> 5);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    kr[ks] = *reinterpret_cast<const bf16x8*>(kp + 32 * ks);
+}
+
+__device__ __forceinline__ void qk_regs(const bf16x8 (&kr)[8],
+                                        const bf16x8 (&qf)[2][8],
+                                        f32x16 (&s)[1][2]) {
+  f32x16 z = {};
+  s[0][0] = z;
+  s[0][1] = z;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s[0][0] = mfma32(kr[ks], qf[0][ks], s[0][0]);
+    s[0][1] = mfma32(kr[ks], qf[1][ks], s[0][1]);
+  }
+}
+
+// References of a 64-query block: each row's max over the keys it sees in its
+// own diagonal key block (it always sees its own key there).
+__device__ __forceinline__ void diag_refs(const u16* kbase, int S, int q0,
+                                          int window, const bf16x8 (&qf)[2][8],
+                                          Soft& sf, int lane) {
+  const uint32_t koff = k_lane_off(lane);
+  sf.mref[0] = sf.mref[1] = -INFINITY;
+#pragma unroll 1
+  for (int st = 0; st < 2; ++st) {
+    bf16x8 kr[8];
+    f32x16 s[1][2];
+    load_k_sub(kbase, S, q0 + 32 * st, koff, kr, lane);
+    qk_regs(kr, qf, s);
+    mask_sub(s[0], q0 + 32 * st, q0, window, lane);
+    raise_refs<1>(s, sf);
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[WSTAGES * STAGE_B];
+  __shared__ int over_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = blockIdx.x % p.Hkv;
@@ -332,7 +429,9 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   const int head = p.hlist[h0 + jl % nsw];
   const int q0 = qb * 64;
   const int w = p.window;
-  // union tile range of the workgroup's jobs (at most two query blocks)
+  // union tile range of the workgroup's jobs (up to four consecutive query
+  // blocks when a KV group has fewer than four window heads), walked from the
+  // top block down: tile t is key block qb_hi - t
   const int qb_hi = p.n_b - 1 - (4 * ig) / nsw;
   const int qb_lo = p.n_b - 1 - min(4 * ig + 3, njobs - 1) / nsw;
   const int lo = qb_lo * 64 - w + 1;
@@ -340,59 +439,82 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   const int nt = qb_hi - kt_lo + 1;
   // A 32-key sub-tile needs masking unless every key is inside every query's
   // window; sub-tiles entirely outside (edges only) are masked to nothing.
-  auto masked = [&](int kmin) -> bool {
+  auto mask = [&](f32x16 (&s)[1][2], int kmin) {
     const int kmax = kmin + 31, qmax = q0 + 63;
-    return !(kmax <= q0 && kmin > qmax - w);
+    if (!(kmax <= q0 && kmin > qmax - w)) mask_sub(s[0], kmin, q0, w, lane);
   };
   const WinLaneOffsets off = win_offsets(p.S_pad, wave, lane);
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, p.S, qf, lane);
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 z = {};
-      acc[j][mt] = z;
-    }
   Soft sf;
-  sf.mref[0] = sf.mref[1] = -1e30f;
-  sf.lsum[0] = sf.lsum[1] = 0.f;
-
-  win_issue(p, g, kt_lo, smem, off, wave, lane);
-  if (nt > 1) win_issue(p, g, kt_lo + 1, smem + STAGE_B, off, wave, lane);
-  wait_vm_all();
-  __syncthreads();
-  f32x16 s[1][2];
+  diag_refs(p.k + (size_t)g * p.S * kD, p.S, q0, w, qf, sf, lane);
+  if (tid == 0) over_flag = 0;  // published by the first barrier below
+  f32x16 acc[2][4];
+  f32x16 sa[1][2], sb[1][2];
   bf16x8 pb[1][2][2];
-  win_qk(smem, 0, qf, s, lane);
-  if (masked(kt_lo * 64)) mask_sub(s[0], kt_lo * 64, q0, w, lane);
-  rescale<1>(s, sf, acc, p.c, p.tau);
-  // step u works on 32-key sub-tile u (tile u/2, half u%2): the QK MFMAs of
-  // sub-tile u+1 run next to the exp/pack of sub-tile u, then P.V(u)
-  const int nu = 2 * nt;
-  for (int u = 0; u + 1 < nu; ++u) {
-    const int tn = (u + 1) >> 1;
-    if (u & 1) {  // sub-tile u+1 opens tile tn
+  for (int attempt = 0;; ++attempt) {
+    zero_acc(acc);
+    sf.lsum[0] = sf.lsum[1] = 0.f;
+    bool over = false;
+    // LDS ring: cur holds tile t, nxt tile t+1, spare the stage for t+2
+    char* cur = smem;
+    char* nxt = smem + STAGE_B;
+    char* spare = smem + 2 * STAGE_B;
+    win_issue(p, g, qb_hi, cur, off, wave, lane);
+    if (nt > 1) win_issue(p, g, qb_hi - 1, nxt, off, wave, lane);
+    wait_vm_all();
+    __syncthreads();
+    win_qk(cur, 0, qf, sa, lane);
+    mask(sa, qb_hi * 64);
+    // one tile per iteration, in two 32-key steps; each step runs the QK
+    // MFMAs of the next sub-tile next to the exp/pack of the current one,
+    // then the current one's P.V
+    for (int t = 0; t + 1 < nt; ++t) {
+      const int kb = qb_hi - t;
+      win_qk(cur, 1, qf, sb, lane);
+      over |= softmax_step<1>(sa, sf, pb, p.c);
+      win_pv(cur, 0, pb, acc, lane);
+      mask(sb, kb * 64 + 32);
       wait_vm_all();
-      __syncthreads();  // tile tn resident; stage of tile tn-2 free
-      if (tn + 1 < nt)
-        win_issue(p, g, kt_lo + tn + 1, smem + ((tn + 1) % WSTAGES) * STAGE_B,
-                  off, wave, lane);
+      __syncthreads();  // tile t+1 resident; spare (tile t-1) free
+      if (t + 2 < nt) win_issue(p, g, kb - 2, spare, off, wave, lane);
+      win_qk(nxt, 0, qf, sa, lane);
+      over |= softmax_step<1>(sb, sf, pb, p.c);
+      win_pv(cur, 1, pb, acc, lane);
+      mask(sa, (kb - 1) * 64);
+      char* const done = cur;
+      cur = nxt;
+      nxt = spare;
+      spare = done;
     }
-    f32x16 sn[1][2];
-    win_qk(smem + (tn % WSTAGES) * STAGE_B, (u + 1) & 1, qf, sn, lane);
-    exp_pack<1>(s, sf, pb, p.c);
-    win_pv(smem + ((u >> 1) % WSTAGES) * STAGE_B, u & 1, pb, acc, lane);
-    const int kn = (kt_lo + tn) * 64 + 32 * ((u + 1) & 1);
-    if (masked(kn)) mask_sub(sn[0], kn, q0, w, lane);
-    rescale<1>(sn, sf, acc, p.c, p.tau);
-    s[0][0] = sn[0][0];
-    s[0][1] = sn[0][1];
+    win_qk(cur, 1, qf, sb, lane);
+    over |= softmax_step<1>(sa, sf, pb, p.c);
+    win_pv(cur, 0, pb, acc, lane);
+    mask(sb, kt_lo * 64 + 32);
+    over |= softmax_step<1>(sb, sf, pb, p.c);
+    win_pv(cur, 1, pb, acc, lane);
+    if (attempt > 0) break;  // exact references: nothing can overflow
+    if (__any(over)) over_flag = 1;
+    __syncthreads();  // also: every wave is done with the LDS ring
+    if (!over_flag) break;
+    // Rare: some score lies far above its row's reference. Find every row's
+    // true maximum over the same tiles, then recompute with it.
+    sf.mref[0] = sf.mref[1] = -INFINITY;
+#pragma unroll 1
+    for (int t = 0; t < nt; ++t) {
+      win_issue(p, g, qb_hi - t, smem, off, wave, lane);
+      wait_vm_all();
+      __syncthreads();
+#pragma unroll 1
+      for (int st = 0; st < 2; ++st) {
+        win_qk(smem, st, qf, sa, lane);
+        mask(sa, (qb_hi - t) * 64 + 32 * st);
+        raise_refs<1>(sa, sf);
+      }
+      __syncthreads();
+    }
   }
-  exp_pack<1>(s, sf, pb, p.c);
-  win_pv(smem + ((nt - 1) % WSTAGES) * STAGE_B, 1, pb, acc, lane);
   if (active) store_out(acc, sf, p.c, p.out, p.lse, head, q0, p.S, lane);
 }
 
@@ -405,47 +527,24 @@ struct SparseParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
   const int32_t* sel; const int32_t* sel_cnt;
   int sel_stride, S, S_pad, n_b, G, n_ret, n_jobs;
-  float c, tau;
+  float c;
   uint8_t head_of_rho[kMaxHeads];
 };
 
 // V^T half tile (32 keys): row d x 4 chunks of 16 B, chunk c at
-// c ^ ((d >> 1) & 3).
+// c ^ ((d >> 1) & 3). Load ins (0..7) covers rows 16 ins .. 16 ins + 15; the
+// lane part of the global offset is the same for every load and tile.
+__device__ __forceinline__ uint32_t sp_v_lane_off(int S_pad, int lane) {
+  const int c = (lane & 3) ^ ((lane >> 3) & 3);
+  return (uint32_t)((lane >> 2) * S_pad * 2 + c * 16);
+}
+
 __device__ __forceinline__ void sp_issue_v(const u16* vbase, int S_pad, int k0,
-                                           char* slot, int lane) {
+                                           uint32_t voff, char* slot) {
+  const char* vb = reinterpret_cast<const char*>(vbase) + (size_t)k0 * 2;
 #pragma unroll
-  for (int ins = 0; ins < 8; ++ins) {
-    const int u = 64 * ins + lane;
-    const int d = u >> 2, cs = u & 3;
-    const int c = cs ^ ((d >> 1) & 3);
-    dma16(vbase + (size_t)d * S_pad + k0 + c * 8, slot + ins * 1024);
-  }
-}
-
-// K operand of a 32-key half tile straight from global memory: lane l holds
-// the row of MFMA row l%32 (key perm_row(l%32)), 8 d-chunks.
-__device__ __forceinline__ void sp_load_k(const u16* kbase, int S, int k0,
-                                          bf16x8 (&kr)[8], int lane) {
-  const int g = lane >> 5, n = lane & 31;
-  int key = k0 + perm_row(n);
-  key = key < S ? key : S - 1;
-  const u16* kp = kbase + (size_t)key * kD + 8 * g;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    kr[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
-}
-
-__device__ __forceinline__ void sp_qk(const bf16x8 (&kr)[8],
-                                      const bf16x8 (&qf)[2][8],
-                                      f32x16 (&s)[1][2]) {
-  f32x16 z = {};
-  s[0][0] = z;
-  s[0][1] = z;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    s[0][0] = mfma32(kr[ks], qf[0][ks], s[0][0]);
-    s[0][1] = mfma32(kr[ks], qf[1][ks], s[0][1]);
-  }
+  for (int ins = 0; ins < 8; ++ins)
+    dma16(vb + (size_t)ins * 16 * S_pad * 2 + voff, slot + ins * 1024);
 }
 
 __device__ __forceinline__ void sp_pv(const char* slot,
@@ -483,73 +582,88 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   char* slots = smem + wave * 2 * VHALF_B;
   const u16* kbase = p.k + (size_t)g * S * kD;
   const u16* vbase = p.vt + (size_t)g * kD * p.S_pad;
+  // blocks from the last (the diagonal) to the first, halves ascending: the
+  // first half tile holds every query's own key, which sets the reference
   auto tile_k0 = [&](int t) -> int {
-    int kb = list[t >> 1];
+    int kb = list[cnt - 1 - (t >> 1)];
     kb = kb < 0 ? 0 : (kb > qb ? qb : kb);  // memory-safe on bad input
     return kb * 64 + 32 * (t & 1);
   };
   // only half tiles of the diagonal block straddle the causal edge; a half
   // tile entirely after every query is masked to nothing
-  auto masked = [&](int k0) -> bool { return k0 + 31 > q0; };
+  auto mask = [&](f32x16 (&s)[1][2], int k0) {
+    if (k0 + 31 > q0) mask_sub(s[0], k0, q0, 1 << 30, lane);
+  };
+  const uint32_t koff = k_lane_off(lane);
+  const uint32_t voff = sp_v_lane_off(p.S_pad, lane);
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, S, qf, lane);
   f32x16 acc[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x16 z = {};
-      acc[j][mt] = z;
-    }
+  zero_acc(acc);
   Soft sf;
-  sf.mref[0] = sf.mref[1] = -1e30f;
+  sf.mref[0] = sf.mref[1] = -INFINITY;
   sf.lsum[0] = sf.lsum[1] = 0.f;
   if (nt == 0) {
     store_out(acc, sf, p.c, p.out, p.lse, head, q0, S, lane);
     return;
   }
 
-  // prologue: K(0), V(0), K(1), V(1) in flight
   bf16x8 kr[8];
-  int k0c = tile_k0(0);
-  sp_load_k(kbase, S, k0c, kr, lane);
-  sp_issue_v(vbase, p.S_pad, k0c, slots, lane);
-  int k0n = k0c;
-  if (nt > 1) {
-    k0n = tile_k0(1);
-    sp_issue_v(vbase, p.S_pad, k0n, slots + VHALF_B, lane);
-  }
-  wait_vm_all();
-  f32x16 s[1][2];
-  sp_qk(kr, qf, s);
-  if (masked(k0c)) mask_sub(s[0], k0c, q0, 1 << 30, lane);
-  rescale<1>(s, sf, acc, p.c, p.tau);
-  if (nt > 1) sp_load_k(kbase, S, k0n, kr, lane);
   bf16x8 pb[1][2][2];
-  for (int t = 0; t + 1 < nt; ++t) {
-    // K(t+1) registers and V(t) slot are ready once everything issued
-    // before V(t+1) has landed
-    wait_vm8();
-    f32x16 sn[1][2];
-    sp_qk(kr, qf, sn);
-    exp_pack<1>(s, sf, pb, p.c);
-    sp_pv(slots + (t & 1) * VHALF_B, pb, acc, lane);
-    const int k0cur = k0n;
-    if (t + 2 < nt) {  // prefetch tile t+2: K to registers, V^T to the slot
-      k0n = tile_k0(t + 2);
-      sp_load_k(kbase, S, k0n, kr, lane);
-      wait_lgkm0();  // this wave's reads of the slot are done
-      sp_issue_v(vbase, p.S_pad, k0n, slots + (t & 1) * VHALF_B, lane);
+  f32x16 s[1][2], sn[1][2];
+  for (int attempt = 0;; ++attempt) {
+    // prologue: K(0), V(0), K(1), V(1) in flight
+    const int k0f = tile_k0(0);
+    load_k_sub(kbase, S, k0f, koff, kr, lane);
+    sp_issue_v(vbase, p.S_pad, k0f, voff, slots);
+    int k0n = k0f;
+    if (nt > 1) {
+      k0n = tile_k0(1);
+      sp_issue_v(vbase, p.S_pad, k0n, voff, slots + VHALF_B);
     }
-    if (masked(k0cur)) mask_sub(sn[0], k0cur, q0, 1 << 30, lane);
-    rescale<1>(sn, sf, acc, p.c, p.tau);
-    s[0][0] = sn[0][0];
-    s[0][1] = sn[0][1];
+    wait_vm_all();
+    qk_regs(kr, qf, s);
+    mask(s, k0f);
+    if (attempt == 0) raise_refs<1>(s, sf);
+    if (nt > 1) load_k_sub(kbase, S, k0n, koff, kr, lane);
+    bool over = false;
+    for (int t = 0; t + 1 < nt; ++t) {
+      // K(t+1) registers and V(t) slot are ready once everything issued
+      // before V(t+1) has landed
+      wait_vm8();
+      qk_regs(kr, qf, sn);
+      over |= softmax_step<1>(s, sf, pb, p.c);
+      sp_pv(slots + (t & 1) * VHALF_B, pb, acc, lane);
+      const int k0cur = k0n;
+      if (t + 2 < nt) {  // prefetch tile t+2: K to registers, V^T to the slot
+        k0n = tile_k0(t + 2);
+        load_k_sub(kbase, S, k0n, koff, kr, lane);
+        wait_lgkm0();  // this wave's reads of the slot are done
+        sp_issue_v(vbase, p.S_pad, k0n, voff, slots + (t & 1) * VHALF_B);
+      }
+      mask(sn, k0cur);
+      s[0][0] = sn[0][0];
+      s[0][1] = sn[0][1];
+    }
+    wait_vm_all();
+    over |= softmax_step<1>(s, sf, pb, p.c);
+    sp_pv(slots + ((nt - 1) & 1) * VHALF_B, pb, acc, lane);
+    if (attempt > 0 || !__any(over)) break;
+    // Rare: a score far above its row's reference. Find every row's true
+    // maximum over the kept keys, then recompute with it.
+    wait_lgkm0();
+#pragma unroll 1
+    for (int t = 0; t < nt; ++t) {
+      const int k0 = tile_k0(t);
+      load_k_sub(kbase, S, k0, koff, kr, lane);
+      qk_regs(kr, qf, s);
+      mask(s, k0);
+      raise_refs<1>(s, sf);
+    }
+    zero_acc(acc);
+    sf.lsum[0] = sf.lsum[1] = 0.f;
   }
-  wait_vm_all();
-  exp_pack<1>(s, sf, pb, p.c);
-  sp_pv(slots + ((nt - 1) & 1) * VHALF_B, pb, acc, lane);
   store_out(acc, sf, p.c, p.out, p.lse, head, q0, S, lane);
 }
 
@@ -605,7 +719,6 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
   wp.S = a.S; wp.S_pad = a.S_pad; wp.n_b = a.n_b; wp.Hkv = a.Hkv;
   wp.window = a.window;
   wp.c = c;
-  wp.tau = 8.0f / c;
   int nl = 0, max_items = 0;
   for (int g = 0; g < a.Hkv; ++g) {
     wp.hoff[g] = (int16_t)nl;
@@ -640,7 +753,6 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
   sp.n_ret = n_ret;
   sp.n_jobs = n_ret * a.n_b;
   sp.c = c;
-  sp.tau = 8.0f / c;
   prof_begin("attn_sparse", st);
   hipLaunchKernelGGL(attn_sparse_kernel, dim3((sp.n_jobs + 3) / 4), dim3(256), 0,
                      st, sp);

@@ -8,10 +8,15 @@ Bars (the tolerances the method is held to):
   inputs with fp32 accumulation;
 * log-sum-exp: max-abs difference <= LSE_TOL.
 
-OUT_TOL comes from the arithmetic: P is rounded to bf16 (relative 2^-9) before
-the P.V product and the output is rounded to bf16 (relative 2^-9); with |v|
-below ~5 for N(0,1) data that bounds the error by ~1e-2, the figure the
-method's accuracy target states.
+OUT_TOL comes from the arithmetic: P is rounded to bf16 (relative <= 2^-8)
+before the P.V product and the output is rounded to bf16 (relative <= 2^-8);
+with |v| below ~5 for N(0,1) data that bounds the error by ~1e-2, the figure
+the method's accuracy target states.
+
+LSE_TOL: the kernels sum the same bf16-rounded probabilities that feed P.V
+(so the output is an exactly normalised average of its weights); each term
+carries a relative error <= 2^-8, so the sum is off by at most that factor
+and log-sum-exp by at most log(1 + 2^-8) = 3.9e-3.
 """
 import math
 
@@ -21,7 +26,7 @@ import oracle
 
 TIE_BAND = 1e-4
 OUT_TOL = 1e-2
-LSE_TOL = 2e-3
+LSE_TOL = 4e-3
 
 
 def sel_sets(sel, cnt):

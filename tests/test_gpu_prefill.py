@@ -220,3 +220,20 @@ def test_indexer_select_kth_scores_and_centroids(gpu_lib):
     assert rel.max() < 1e-4, rel.max()
     c_g, c_o = cent.cpu().numpy(), ora_sel["centroids"]
     assert np.abs(c_g - c_o).max() <= 1e-5 * np.abs(c_o).max() + 1e-6
+
+
+def test_reference_restart_when_an_early_key_dominates(gpu_lib):
+    # Every query equals u and key 0 is 60 u/|u|: its score exceeds the
+    # diagonal block's scores by far more than the kernels' no-rescale range,
+    # so window and retrieval heads must restart with a raised reference and
+    # still match the exact softmax.
+    S = 512
+    x = make_prefill(_wl(S, Hq=4, Hkv=1, ret=(1, 3), window=S, top_k=2))
+    g = torch.Generator().manual_seed(7)
+    u = torch.randn(128, generator=g)
+    q = u.to(torch.bfloat16).expand(4, S, 128).contiguous()
+    k = x["k"].clone()
+    k[0, 0] = (60.0 * u / u.norm()).to(torch.bfloat16)
+    x["q"], x["k"] = q, k
+    r = full_check(gpu_lib, x, "restart")
+    assert np.isfinite(r["out"].float().cpu().numpy()).all()
