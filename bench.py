@@ -34,6 +34,30 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA peak"
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) of
+#   bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-gib 1
+# each divided by what the same counter reads per byte of the run's 1 GiB
+# plain device copy. Valid only for the kernel source it was measured on
+# (sha256 below); after any change to it the figure is reported as null.
+TRAFFIC = {
+    "kernel": "attn_window_kernel",
+    "source": "long_context_sparse_head_amd/csrc/attn.hip",
+    "sha256": None,
+    "fetch_bytes": None,
+    "write_bytes": None,
+}
+
+
+def measured_traffic():
+    import hashlib
+    if TRAFFIC["sha256"] is None:
+        return None
+    with open(os.path.join(ROOT, TRAFFIC["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["sha256"]:
+            return None
+    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -321,6 +345,10 @@ def main():
                     help="time the 128K prefill only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="after the timed legs, run a plain device copy of "
+                         "this many GiB twice (calibrates HBM byte counters "
+                         "under rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU "
@@ -356,6 +384,15 @@ def main():
             f"ms/step")
         extra["speedup_vs_dense_128k"] = (extra["dense_128k"]["ms_per_step"] /
                                           main["ms_per_step"])
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * 2**30)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 2 x {n} bytes copied")
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(PREFILL_128K, main["attn_pairs"]["retrieval"],
@@ -384,7 +421,7 @@ def main():
                      "achieved": main["window_kernel_tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": main["window_kernel_tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "detail": {"prefill_128k": main, **extra},
     }

@@ -41,6 +41,8 @@
 // its block list in 32-key half tiles: K goes straight into registers in MFMA
 // operand layout (vector-memory path), V^T through a per-wave LDS slot (LDS
 // DMA path), so the gather traffic is split over both paths.
+#include <type_traits>
+
 #include "common.h"
 
 namespace rtp {
@@ -174,11 +176,12 @@ __device__ __forceinline__ void mask_sub(f32x16 (&s)[2], int kmin, int q0,
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int qi = q0 + 32 * j + n;
+    const int rel0 = qi - kmin - 8 * g;  // qi - key of element 0
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int key = kmin + 16 * (i >> 3) + 8 * g + (i & 7);
-      const bool ok = key <= qi && key > qi - window;
-      s[j][i] = ok ? s[j][i] : -INFINITY;
+      // key <= qi and key > qi - window, as one unsigned compare
+      const unsigned rel = (unsigned)(rel0 - 16 * (i >> 3) - (i & 7));
+      s[j][i] = rel < (unsigned)window ? s[j][i] : -INFINITY;
     }
   }
 }
@@ -412,6 +415,99 @@ __device__ __forceinline__ void diag_refs(const u16* kbase, int S, int q0,
   }
 }
 
+// One 32-key step with the work interleaved by hand: the QK MFMAs of the next
+// sub-tile (K from stage kst, half kh) and the P.V MFMAs of the current one
+// (V^T from stage vst, half vh) are issued in 8 groups of 4, each next to an
+// eighth of the exp/pack work of the current scores s and the LDS reads of
+// the next group's operands. sched_barrier keeps the compiler from
+// regrouping them (it otherwise issues all QK MFMAs, then all exps, then all
+// P.V MFMAs). Returns whether a row sum left the safe range.
+__device__ __forceinline__ bool win_step(const char* kst, int kh,
+                                         const char* vst, int vh,
+                                         const bf16x8 (&qf)[2][8],
+                                         const f32x16 (&s)[1][2],
+                                         f32x16 (&sn)[1][2], Soft& sf,
+                                         f32x16 (&acc)[2][4], float c,
+                                         int lane) {
+  const int g = lane >> 5, n = lane & 31;
+  const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
+  const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
+  auto kld = [&](int ks) {
+    return *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
+  };
+  auto vld = [&](int ks, int mt) {
+    return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B + 32 * ks);
+  };
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const float mc[2] = {sf.mref[0] * c, sf.mref[1] * c};
+  uint32_t w[2][2][4];  // packed P: [query tile j][key half h][pair]
+  float ls[2] = {0.f, 0.f};
+  // exp/pack of 4 scores (pairs e0, e0+1) of query tile j, key half h
+  auto expq = [&](int j, int h, int e0) {
+#pragma unroll
+    for (int e = e0; e < e0 + 2; ++e) {
+      const int i = 8 * h + 2 * e;
+      const float p0 = fast_exp2(fmaf(s[0][j][i], c, -mc[j]));
+      const float p1 = fast_exp2(fmaf(s[0][j][i + 1], c, -mc[j]));
+      w[j][h][e] = pack_bf16x2(p0, p1);
+      ls[j] = __builtin_amdgcn_fdot2_f32_bf16(
+          __builtin_bit_cast(bf16x2, w[j][h][e]), one, ls[j], false);
+    }
+  };
+  auto pb = [&](int j, int h) {
+    return __builtin_bit_cast(
+        bf16x8, make_uint4(w[j][h][0], w[j][h][1], w[j][h][2], w[j][h][3]));
+  };
+  f32x16 z = {};
+  sn[0][0] = z;
+  sn[0][1] = z;
+  bf16x8 k0 = kld(0), k1 = kld(1);
+  // groups 0-3: QK ks = 2q, 2q+1 | exp of (j, h=0) quarter q
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bf16x8 k2 = kld(q < 3 ? 2 * q + 2 : 0);
+    const bf16x8 k3 = kld(q < 3 ? 2 * q + 3 : 1);
+    sn[0][0] = mfma32(k0, qf[0][2 * q], sn[0][0]);
+    sn[0][1] = mfma32(k0, qf[1][2 * q], sn[0][1]);
+    sn[0][0] = mfma32(k1, qf[0][2 * q + 1], sn[0][0]);
+    sn[0][1] = mfma32(k1, qf[1][2 * q + 1], sn[0][1]);
+    expq(q >> 1, 0, 2 * (q & 1));
+    k0 = k2;
+    k1 = k3;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // groups 4-5: P.V h=0 (mt 2r, 2r+1) | exp of (j = r, h=1)
+  bf16x8 v0 = vld(0, 0), v1 = vld(0, 1);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const bf16x8 v2 = vld(r == 0 ? 0 : 1, r == 0 ? 2 : 0);
+    const bf16x8 v3 = vld(r == 0 ? 0 : 1, r == 0 ? 3 : 1);
+    const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
+    acc[0][2 * r] = mfma32(v0, p00, acc[0][2 * r]);
+    acc[1][2 * r] = mfma32(v0, p10, acc[1][2 * r]);
+    acc[0][2 * r + 1] = mfma32(v1, p00, acc[0][2 * r + 1]);
+    acc[1][2 * r + 1] = mfma32(v1, p10, acc[1][2 * r + 1]);
+    expq(r, 1, 0);
+    expq(r, 1, 2);
+    v0 = v2;
+    v1 = v3;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // groups 6-7: P.V h=1, query tile 0 then 1 (v0, v1 hold mt 0, 1)
+  const bf16x8 v2 = vld(1, 2), v3 = vld(1, 3);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x8 p = pb(j, 1);
+    acc[j][0] = mfma32(v0, p, acc[j][0]);
+    acc[j][1] = mfma32(v1, p, acc[j][1]);
+    acc[j][2] = mfma32(v2, p, acc[j][2]);
+    acc[j][3] = mfma32(v3, p, acc[j][3]);
+  }
+  sf.lsum[0] += ls[0];
+  sf.lsum[1] += ls[1];
+  return (ls[0] > kSumLimit) || (ls[1] > kSumLimit);
+}
+
 __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[WSTAGES * STAGE_B];
   __shared__ int over_flag;
@@ -452,7 +548,6 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   if (tid == 0) over_flag = 0;  // published by the first barrier below
   f32x16 acc[2][4];
   f32x16 sa[1][2], sb[1][2];
-  bf16x8 pb[1][2][2];
   for (int attempt = 0;; ++attempt) {
     zero_acc(acc);
     sf.lsum[0] = sf.lsum[1] = 0.f;
@@ -465,29 +560,52 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     if (nt > 1) win_issue(p, g, qb_hi - 1, nxt, off, wave, lane);
     wait_vm_all();
     __syncthreads();
+    // Sub-tile u = 32 keys (tile u/2, half u%2). Step u runs the QK MFMAs of
+    // sub-tile u+1 next to the exp/pack of sub-tile u, then P.V(u). One tile
+    // (two steps) per iteration; the barrier sits between the steps, when QK
+    // moves on to the next tile.
+    bf16x8 pb[1][2][2];
     win_qk(cur, 0, qf, sa, lane);
     mask(sa, qb_hi * 64);
-    // one tile per iteration, in two 32-key steps; each step runs the QK
-    // MFMAs of the next sub-tile next to the exp/pack of the current one,
-    // then the current one's P.V
-    for (int t = 0; t + 1 < nt; ++t) {
+    // iteration t: tile t's second half and tile t+1's first half are
+    // masked (edges) unless both tiles are clean for every wave
+    auto iter = [&](auto with_mask, int t) {
+      constexpr bool M = decltype(with_mask)::value;
       const int kb = qb_hi - t;
-      win_qk(cur, 1, qf, sb, lane);
-      over |= softmax_step<1>(sa, sf, pb, p.c);
-      win_pv(cur, 0, pb, acc, lane);
-      mask(sb, kb * 64 + 32);
+      if constexpr (M) {
+        win_qk(cur, 1, qf, sb, lane);
+        over |= softmax_step<1>(sa, sf, pb, p.c);
+        win_pv(cur, 0, pb, acc, lane);
+        mask(sb, kb * 64 + 32);
+      } else {
+        over |= win_step(cur, 1, cur, 0, qf, sa, sb, sf, acc, p.c, lane);
+      }
       wait_vm_all();
       __syncthreads();  // tile t+1 resident; spare (tile t-1) free
       if (t + 2 < nt) win_issue(p, g, kb - 2, spare, off, wave, lane);
-      win_qk(nxt, 0, qf, sa, lane);
-      over |= softmax_step<1>(sb, sf, pb, p.c);
-      win_pv(cur, 1, pb, acc, lane);
-      mask(sa, (kb - 1) * 64);
+      if constexpr (M) {
+        win_qk(nxt, 0, qf, sa, lane);
+        over |= softmax_step<1>(sb, sf, pb, p.c);
+        win_pv(cur, 1, pb, acc, lane);
+        mask(sa, (kb - 1) * 64);
+      } else {
+        over |= win_step(nxt, 0, cur, 1, qf, sb, sa, sf, acc, p.c, lane);
+      }
       char* const done = cur;
       cur = nxt;
       nxt = spare;
       spare = done;
-    }
+    };
+    // Tiles clean for every wave of the workgroup: below the lowest query
+    // block's diagonal and above the highest query block's window edge.
+    const int edge = qb_hi * 64 + 63 - w;
+    const int kc_lo = edge < 0 ? 0 : (edge >> 6) + 1;
+    const int t_a = min(qb_hi - qb_lo + 1, nt - 1);
+    const int t_b = min(max(qb_hi - kc_lo, t_a), nt - 1);
+    int t = 0;
+    for (; t < t_a; ++t) iter(std::true_type{}, t);
+    for (; t < t_b; ++t) iter(std::false_type{}, t);
+    for (; t < nt - 1; ++t) iter(std::true_type{}, t);
     win_qk(cur, 1, qf, sb, lane);
     over |= softmax_step<1>(sa, sf, pb, p.c);
     win_pv(cur, 0, pb, acc, lane);
