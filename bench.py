@@ -345,6 +345,9 @@ def main():
                     help="time the 128K prefill only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense"],
+                    help="run only this secondary leg and print its detail "
+                         "(for profiling); no bench line")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after the timed legs, run a plain device copy of "
                          "this many GiB twice (calibrates HBM byte counters "
@@ -361,6 +364,17 @@ def main():
     rtp.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.leg:
+        if args.leg == "decode":
+            res = bench_decode(rtp, torch, DECODE_32x256K, args.steps,
+                               args.warmup)
+        else:
+            w = {"1m": PREFILL_1M, "32k": PREFILL_32K,
+                 "dense": PREFILL_128K}[args.leg]
+            res = bench_prefill(rtp, torch, w, args.steps, args.warmup,
+                                dense=args.leg == "dense")
+        print(json.dumps({"leg": args.leg, **res}), flush=True)
+        return
     main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup)
     log(f"[bench] 128K: {main['ms_per_step']:.3f} ms/step, "
         f"{main['tokens_per_s']:.3e} tok/s, window kernel "

@@ -267,8 +267,7 @@ struct WinLaneOffsets {
   uint32_t off[DMA_PER_WAVE];
 };
 
-__device__ __forceinline__ uint32_t win_unit_offset(int ld, int lane,
-                                                    int S_pad) {
+__device__ __forceinline__ uint32_t win_unit_offset(int ld, int lane) {
   if (ld < K_DMA) {
     const int u = 64 * ld + lane;
     const int r = u / 17, c = min(u % 17, 15);
@@ -276,16 +275,15 @@ __device__ __forceinline__ uint32_t win_unit_offset(int ld, int lane,
   }
   const int u = 64 * (ld - K_DMA) + lane;
   const int d = u / 9, c = min(u % 9, 7);
-  return (uint32_t)(d * S_pad * 2 + c * 16);
+  return (uint32_t)(d * 128 + c * 16);  // V^T block row d: 64 keys, 128 B
 }
 
-__device__ __forceinline__ WinLaneOffsets win_offsets(int S_pad, int wave,
-                                                      int lane) {
+__device__ __forceinline__ WinLaneOffsets win_offsets(int wave, int lane) {
   WinLaneOffsets o;
 #pragma unroll
   for (int j = 0; j < DMA_PER_WAVE; ++j) {
     const int ld = wave + 4 * j;
-    o.off[j] = ld < K_DMA + V_DMA ? win_unit_offset(ld, lane, S_pad) : 0u;
+    o.off[j] = ld < K_DMA + V_DMA ? win_unit_offset(ld, lane) : 0u;
   }
   return o;
 }
@@ -307,8 +305,8 @@ __device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
                                           int wave, int lane) {
   const char* kt = reinterpret_cast<const char*>(p.k) +
                    ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
-  const char* vt = reinterpret_cast<const char*>(p.vt) +
-                   ((size_t)g * kD * p.S_pad + (size_t)kb * 64) * 2;
+  const char* vt = reinterpret_cast<const char*>(
+      p.vt + ((size_t)g * p.n_b + kb) * 64 * kD);
   if ((kb + 1) * 64 > p.S) {  // last block of a ragged S: rows past S
 #pragma unroll 1                // re-read row S-1 (masked anyway)
     for (int j = 0; j < DMA_PER_WAVE; ++j) {
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     const int kmax = kmin + 31, qmax = q0 + 63;
     if (!(kmax <= q0 && kmin > qmax - w)) mask_sub(s[0], kmin, q0, w, lane);
   };
-  const WinLaneOffsets off = win_offsets(p.S_pad, wave, lane);
+  const WinLaneOffsets off = win_offsets(wave, lane);
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, p.S, qf, lane);
@@ -652,17 +650,19 @@ struct SparseParams {
 // V^T half tile (32 keys): row d x 4 chunks of 16 B, chunk c at
 // c ^ ((d >> 1) & 3). Load ins (0..7) covers rows 16 ins .. 16 ins + 15; the
 // lane part of the global offset is the same for every load and tile.
-__device__ __forceinline__ uint32_t sp_v_lane_off(int S_pad, int lane) {
+__device__ __forceinline__ uint32_t sp_v_lane_off(int lane) {
   const int c = (lane & 3) ^ ((lane >> 3) & 3);
-  return (uint32_t)((lane >> 2) * S_pad * 2 + c * 16);
+  return (uint32_t)((lane >> 2) * 128 + c * 16);
 }
 
-__device__ __forceinline__ void sp_issue_v(const u16* vbase, int S_pad, int k0,
+// vbase: the KV group's first V^T block; k0: first key of the half tile
+__device__ __forceinline__ void sp_issue_v(const u16* vbase, int k0,
                                            uint32_t voff, char* slot) {
-  const char* vb = reinterpret_cast<const char*>(vbase) + (size_t)k0 * 2;
+  const char* vb = reinterpret_cast<const char*>(
+                       vbase + (size_t)(k0 >> 6) * 64 * kD) + (k0 & 63) * 2;
 #pragma unroll
   for (int ins = 0; ins < 8; ++ins)
-    dma16(vb + (size_t)ins * 16 * S_pad * 2 + voff, slot + ins * 1024);
+    dma16(vb + ins * 16 * 128 + voff, slot + ins * 1024);
 }
 
 __device__ __forceinline__ void sp_pv(const char* slot,
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   const int nt = 2 * cnt;  // 32-key half tiles
   char* slots = smem + wave * 2 * VHALF_B;
   const u16* kbase = p.k + (size_t)g * S * kD;
-  const u16* vbase = p.vt + (size_t)g * kD * p.S_pad;
+  const u16* vbase = p.vt + (size_t)g * p.n_b * 64 * kD;
   // blocks from the last (the diagonal) to the first, halves ascending: the
   // first half tile holds every query's own key, which sets the reference
   auto tile_k0 = [&](int t) -> int {
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     if (k0 + 31 > q0) mask_sub(s[0], k0, q0, 1 << 30, lane);
   };
   const uint32_t koff = k_lane_off(lane);
-  const uint32_t voff = sp_v_lane_off(p.S_pad, lane);
+  const uint32_t voff = sp_v_lane_off(lane);
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, S, qf, lane);
@@ -734,11 +734,11 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     // prologue: K(0), V(0), K(1), V(1) in flight
     const int k0f = tile_k0(0);
     load_k_sub(kbase, S, k0f, koff, kr, lane);
-    sp_issue_v(vbase, p.S_pad, k0f, voff, slots);
+    sp_issue_v(vbase, k0f, voff, slots);
     int k0n = k0f;
     if (nt > 1) {
       k0n = tile_k0(1);
-      sp_issue_v(vbase, p.S_pad, k0n, voff, slots + VHALF_B);
+      sp_issue_v(vbase, k0n, voff, slots + VHALF_B);
     }
     wait_vm_all();
     qk_regs(kr, qf, s);
@@ -758,7 +758,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
         k0n = tile_k0(t + 2);
         load_k_sub(kbase, S, k0n, koff, kr, lane);
         wait_lgkm0();  // this wave's reads of the slot are done
-        sp_issue_v(vbase, p.S_pad, k0n, voff, slots + (t & 1) * VHALF_B);
+        sp_issue_v(vbase, k0n, voff, slots + (t & 1) * VHALF_B);
       }
       mask(sn, k0cur);
       s[0][0] = sn[0][0];
@@ -786,7 +786,8 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
 }
 
 // =====================================================================
-// V transpose: V [Hkv,S,128] -> V^T [Hkv,128,S_pad], zero beyond S
+// V transpose: V [Hkv,S,128] -> V^T in 64-key blocks [Hkv][n_b][128][64]
+// (zero beyond S), so every key block's V^T is one contiguous 16 KiB read
 // =====================================================================
 constexpr int TSTR = 136;
 __global__ __launch_bounds__(256) void transpose_v_kernel(
@@ -811,7 +812,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
     for (int e = 0; e < 4; ++e)
       w[e] = (uint32_t)t[(kc * 8 + 2 * e) * TSTR + dr] |
              ((uint32_t)t[(kc * 8 + 2 * e + 1) * TSTR + dr] << 16);
-    *reinterpret_cast<uint4*>(vt + ((size_t)g * kD + dr) * S_pad + kb * 64 + kc * 8) =
+    *reinterpret_cast<uint4*>(
+        vt + (((size_t)g * (S_pad / 64) + kb) * kD + dr) * 64 + kc * 8) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
 }

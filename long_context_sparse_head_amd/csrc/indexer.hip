@@ -131,11 +131,14 @@ __global__ __launch_bounds__(64) void proj_qmeans_kernel(
   }
 }
 
-// ---- block scores: grid (ceil(n_b/KBC), ceil(n_b/128), n_ret), 4 waves.
+// ---- block scores: grid (ceil(n_b/128), ceil(n_b/KBC), n_ret), 4 waves.
 // Workgroup = 128 query blocks (32 per wave, along the MFMA N dimension) x a
 // chunk of KBC key blocks. For each key block the 64 projected keys are
 // staged in LDS and each wave computes the 64 x 32 dot products as two
-// 32x32 tiles (keys along M), then max-pools the 64 keys of the block.
+// 32x32 tiles (keys along M), then max-pools the 64 keys of the block. The
+// query tile is the fastest grid index, so the workgroups that share a key
+// chunk run together and read it from L2. Scores are collected in LDS and
+// written row by row, one contiguous run of up to KBC floats per row.
 constexpr int KBC = 64;
 
 template <int R16>
@@ -146,7 +149,8 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
   constexpr int r = 16 * R16;
   constexpr int RS = r + 8;  // LDS row stride (bf16), 16-byte pad
   __shared__ __attribute__((aligned(16))) u16 st[2][2][64 * RS];
-  const int kc = blockIdx.x, qt = blockIdx.y, rho = blockIdx.z;
+  __shared__ float scs[128][KBC + 1];
+  const int qt = blockIdx.x, kc = blockIdx.y, rho = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, n = lane & 31;
   const int qb0 = qt * 128;
@@ -171,7 +175,6 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
   }
   const int64_t tri = tri_rows(n_b);
   float* srow_base = scores + (size_t)rho * tri;
-  const int64_t rowoff = qb >= 2 ? (int64_t)(qb - 2) * (qb - 1) / 2 : 0;
 
   // staging: 64 rows x r bf16 (hi and lo) = 64*r*4 bytes = r*16 chunks of 16 B
   constexpr int CH_PER_ROW = r / 8;            // 16-byte chunks per row
@@ -229,10 +232,18 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (g == 0 && qb < n_b && kb <= qb - 1) srow_base[rowoff + kb - 1] = mx;
+      if (g == 0) scs[32 * wave + n][kb - kb_begin] = mx;
     }
     if (kb + 1 < kb_end) sstore(buf ^ 1);
     __syncthreads();
+  }
+  // write-out: row qb takes candidates kb_begin .. min(kb_end, qb) - 1
+  for (int i = 0; i < 32; ++i) {
+    const int row = 32 * wave + i, qbi = qb0 + row;
+    if (qbi >= n_b) break;
+    const int cnt = min(kb_end, qbi) - kb_begin;
+    const int64_t off = qbi >= 2 ? (int64_t)(qbi - 2) * (qbi - 1) / 2 : 0;
+    if (lane < cnt) srow_base[off + kb_begin + lane - 1] = scs[row][lane];
   }
 }
 
@@ -335,7 +346,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
                      a.q, a.p_q, pa, a.qhi, a.qlo);
   prof_end(st);
   if (a.n_b >= 3) {
-    dim3 grid((a.n_b + KBC - 1) / KBC, (a.n_b + 127) / 128, a.n_ret);
+    dim3 grid((a.n_b + 127) / 128, (a.n_b + KBC - 1) / KBC, a.n_ret);
     prof_begin("block_scores", st);
     switch (a.r / 16) {
 #define RTP_SCORE_CASE(R)                                                    \
