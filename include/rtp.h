@@ -125,7 +125,9 @@ int rtp_indexer_select(const void* q, const void* k, int S, int Hq, int Hkv,
  *  scale            softmax scale; <= 0 means 1/sqrt(d)
  *  sel_in, sel_count_in   (may both be NULL) a selection in the layout of
  *        rtp_indexer_select; when given, the indexer is skipped and these
- *        blocks are used (each row ascending, within 0..qb)
+ *        blocks are used (each row strictly ascending, within 0..qb;
+ *        rows that break this are read memory-safely but give undefined
+ *        outputs)
  *  out [Hq,S,d] bf16 (out)        attention output, rounded to nearest even
  *  lse [Hq,S] fp32 (out, may be NULL)   natural-log sum of exp of scaled
  *                                        logits over the attended keys

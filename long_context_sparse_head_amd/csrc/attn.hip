@@ -414,28 +414,18 @@ __device__ __forceinline__ void diag_refs(const u16* kbase, int S, int q0,
 }
 
 // One 32-key step with the work interleaved by hand: the QK MFMAs of the next
-// sub-tile (K from stage kst, half kh) and the P.V MFMAs of the current one
-// (V^T from stage vst, half vh) are issued in 8 groups of 4, each next to an
-// eighth of the exp/pack work of the current scores s and the LDS reads of
-// the next group's operands. sched_barrier keeps the compiler from
-// regrouping them (it otherwise issues all QK MFMAs, then all exps, then all
-// P.V MFMAs). Returns whether a row sum left the safe range.
-__device__ __forceinline__ bool win_step(const char* kst, int kh,
-                                         const char* vst, int vh,
-                                         const bf16x8 (&qf)[2][8],
-                                         const f32x16 (&s)[1][2],
-                                         f32x16 (&sn)[1][2], Soft& sf,
-                                         f32x16 (&acc)[2][4], float c,
-                                         int lane) {
-  const int g = lane >> 5, n = lane & 31;
-  const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
-  const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
-  auto kld = [&](int ks) {
-    return *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
-  };
-  auto vld = [&](int ks, int mt) {
-    return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B + 32 * ks);
-  };
+// sub-tile (K operand kop(ks), ks = 0..7) and the P.V MFMAs of the current
+// one (V^T operand vop(h, mt)) are issued in 8 groups of 4, each next to an
+// eighth of the exp/pack work of the current scores s and the operand reads
+// of the next group. sched_barrier keeps the compiler from regrouping them
+// (it otherwise issues all QK MFMAs, then all exps, then all P.V MFMAs).
+// Returns whether a row sum left the safe range.
+template <class KOp, class VOp>
+__device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
+                                          const bf16x8 (&qf)[2][8],
+                                          const f32x16 (&s)[1][2],
+                                          f32x16 (&sn)[1][2], Soft& sf,
+                                          f32x16 (&acc)[2][4], float c) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   const float mc[2] = {sf.mref[0] * c, sf.mref[1] * c};
   uint32_t w[2][2][4];  // packed P: [query tile j][key half h][pair]
@@ -459,12 +449,12 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
   f32x16 z = {};
   sn[0][0] = z;
   sn[0][1] = z;
-  bf16x8 k0 = kld(0), k1 = kld(1);
+  bf16x8 k0 = kop(0), k1 = kop(1);
   // groups 0-3: QK ks = 2q, 2q+1 | exp of (j, h=0) quarter q
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const bf16x8 k2 = kld(q < 3 ? 2 * q + 2 : 0);
-    const bf16x8 k3 = kld(q < 3 ? 2 * q + 3 : 1);
+    const bf16x8 k2 = kop(q < 3 ? 2 * q + 2 : 0);
+    const bf16x8 k3 = kop(q < 3 ? 2 * q + 3 : 1);
     sn[0][0] = mfma32(k0, qf[0][2 * q], sn[0][0]);
     sn[0][1] = mfma32(k0, qf[1][2 * q], sn[0][1]);
     sn[0][0] = mfma32(k1, qf[0][2 * q + 1], sn[0][0]);
@@ -475,11 +465,11 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
     __builtin_amdgcn_sched_barrier(0);
   }
   // groups 4-5: P.V h=0 (mt 2r, 2r+1) | exp of (j = r, h=1)
-  bf16x8 v0 = vld(0, 0), v1 = vld(0, 1);
+  bf16x8 v0 = vop(0, 0), v1 = vop(0, 1);
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const bf16x8 v2 = vld(r == 0 ? 0 : 1, r == 0 ? 2 : 0);
-    const bf16x8 v3 = vld(r == 0 ? 0 : 1, r == 0 ? 3 : 1);
+    const bf16x8 v2 = vop(r == 0 ? 0 : 1, r == 0 ? 2 : 0);
+    const bf16x8 v3 = vop(r == 0 ? 0 : 1, r == 0 ? 3 : 1);
     const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
     acc[0][2 * r] = mfma32(v0, p00, acc[0][2 * r]);
     acc[1][2 * r] = mfma32(v0, p10, acc[1][2 * r]);
@@ -492,7 +482,7 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
     __builtin_amdgcn_sched_barrier(0);
   }
   // groups 6-7: P.V h=1, query tile 0 then 1 (v0, v1 hold mt 0, 1)
-  const bf16x8 v2 = vld(1, 2), v3 = vld(1, 3);
+  const bf16x8 v2 = vop(1, 2), v3 = vop(1, 3);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const bf16x8 p = pb(j, 1);
@@ -504,6 +494,27 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
   sf.lsum[0] += ls[0];
   sf.lsum[1] += ls[1];
   return (ls[0] > kSumLimit) || (ls[1] > kSumLimit);
+}
+
+// The window kernel's step: K rows of stage kst (half kh) and V^T rows of
+// stage vst (half vh), both from the padded LDS tile.
+__device__ __forceinline__ bool win_step(const char* kst, int kh,
+                                         const char* vst, int vh,
+                                         const bf16x8 (&qf)[2][8],
+                                         const f32x16 (&s)[1][2],
+                                         f32x16 (&sn)[1][2], Soft& sf,
+                                         f32x16 (&acc)[2][4], float c,
+                                         int lane) {
+  const int g = lane >> 5, n = lane & 31;
+  const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
+  const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
+  return attn_step(
+      [&](int ks) { return *reinterpret_cast<const bf16x8*>(krow + 32 * ks); },
+      [&](int h, int mt) {
+        return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B +
+                                                32 * h);
+      },
+      qf, s, sn, sf, acc, c);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) {
@@ -638,6 +649,9 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
 // Sparse kernel
 // =====================================================================
 constexpr int VHALF_B = 8192;  // V^T of 32 keys: 128 d x 64 B
+constexpr int KHALF_B = 8192;  // K of 32 keys: 32 rows x 256 B
+// per wave: a ring of 2 K and 3 V^T half tiles (4 waves: 160 KiB of LDS)
+constexpr int SP_WAVE_B = 2 * KHALF_B + 3 * VHALF_B;
 
 struct SparseParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
@@ -665,24 +679,50 @@ __device__ __forceinline__ void sp_issue_v(const u16* vbase, int k0,
     dma16(vb + ins * 16 * 128 + voff, slot + ins * 1024);
 }
 
-__device__ __forceinline__ void sp_pv(const char* slot,
-                                      const bf16x8 (&pb)[1][2][2],
-                                      f32x16 (&acc)[2][4], int lane) {
-  const int g = lane >> 5, n = lane & 31;
+// s_waitcnt vmcnt(24), other counters at their maximum (gfx9 encoding)
+__device__ __forceinline__ void wait_vm24() {
+  __builtin_amdgcn_s_waitcnt((24 & 15) | (7 << 4) | (15 << 8) | ((24 >> 4) << 14));
+}
+
+// K half tile (32 keys) in LDS: row r = key r, 16 chunks of 16 B, chunk c at
+// position c ^ (r & 15) (16 consecutive lanes of an operand read then hit 16
+// distinct bank groups). DMA ins (0..7), lane i fills position i & 15 of row
+// 4 ins + i / 16; its global offset inside the half tile repeats every 4
+// loads (+4 KiB), so 4 per-lane offsets cover all 8.
+__device__ __forceinline__ void sp_k_lane_offs(int lane, uint32_t (&o)[4]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ins = 0; ins < 4; ++ins) {
+    const int r = 4 * ins + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    o[ins] = (uint32_t)(r * 256 + c * 16);
+  }
+}
+
+__device__ __attribute__((noinline)) void sp_issue_k_ragged(
+    const u16* kbase, int S, int k0, char* slot, int lane) {
+  for (int ins = 0; ins < 8; ++ins) {
+    const int r = 4 * ins + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const int key = k0 + r < S ? k0 + r : S - 1;  // rows past S: masked
+    dma16(kbase + (size_t)key * kD + c * 8, slot + ins * 1024);
+  }
+}
+
+__device__ __forceinline__ void sp_issue_k(const u16* kbase, int S, int k0,
+                                           const uint32_t (&o)[4], char* slot,
+                                           int lane) {
+  if (k0 + 32 > S) {
+    sp_issue_k_ragged(kbase, S, k0, slot, lane);
+    return;
+  }
+  const char* kb = reinterpret_cast<const char*>(kbase + (size_t)k0 * kD);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int d = 32 * mt + n;
-      const int c = (2 * ks + g) ^ ((d >> 1) & 3);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + d * 64 + c * 16);
-      acc[0][mt] = mfma32(a, pb[0][0][ks], acc[0][mt]);
-      acc[1][mt] = mfma32(a, pb[0][1][ks], acc[1][mt]);
-    }
+  for (int ins = 0; ins < 8; ++ins)
+    dma16(kb + (ins >> 2) * 4096 + o[ins & 3], slot + ins * 1024);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * 2 * VHALF_B];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * SP_WAVE_B];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int job = 4 * blockIdx.x + wave;
@@ -693,27 +733,53 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   const int g = head / p.G;
   const int q0 = qb * 64;
   const int S = p.S;
-  const int32_t* list = p.sel + ((size_t)rho * p.n_b + qb) * p.sel_stride;
-  int cnt = p.sel_cnt[(size_t)rho * p.n_b + qb];
+  // The list is read-only here: reading it through the constant address
+  // space lets the compiler use scalar loads, which leave vmcnt (the K/V
+  // prefetch accounting) alone.
+  typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+  const const_i32_ptr list =
+      (const_i32_ptr)(p.sel + ((size_t)rho * p.n_b + qb) * p.sel_stride);
+  int cnt = __builtin_amdgcn_readfirstlane(p.sel_cnt[(size_t)rho * p.n_b + qb]);
   cnt = cnt < 0 ? 0 : (cnt > p.sel_stride ? p.sel_stride : cnt);
-  const int nt = 2 * cnt;  // 32-key half tiles
-  char* slots = smem + wave * 2 * VHALF_B;
+  const int nt = 2 * cnt;  // 32-key half tiles (even)
+  char* const kslots = smem + wave * SP_WAVE_B;
+  char* const vslots = kslots + 2 * KHALF_B;
   const u16* kbase = p.k + (size_t)g * S * kD;
   const u16* vbase = p.vt + (size_t)g * p.n_b * 64 * kD;
-  // blocks from the last (the diagonal) to the first, halves ascending: the
-  // first half tile holds every query's own key, which sets the reference
+  // Half tile t: blocks from the last (the diagonal) to the first, halves
+  // ascending, so the first half tile holds every query's own key and sets
+  // the reference. Indices past the end re-read the last half tile, so every
+  // step issues the same loads (fixed wait counts); those are never used.
   auto tile_k0 = [&](int t) -> int {
-    int kb = list[cnt - 1 - (t >> 1)];
+    t = t < nt ? t : nt - 1;
+    int kb = list[__builtin_amdgcn_readfirstlane(cnt - 1 - (t >> 1))];
     kb = kb < 0 ? 0 : (kb > qb ? qb : kb);  // memory-safe on bad input
     return kb * 64 + 32 * (t & 1);
   };
-  // only half tiles of the diagonal block straddle the causal edge; a half
-  // tile entirely after every query is masked to nothing
-  auto mask = [&](f32x16 (&s)[1][2], int k0) {
-    if (k0 + 31 > q0) mask_sub(s[0], k0, q0, 1 << 30, lane);
+  // only half tiles of the diagonal block straddle the causal edge
+  auto mask = [&](f32x16 (&sc)[1][2], int k0) {
+    if (k0 + 31 > q0) mask_sub(sc[0], k0, q0, 1 << 30, lane);
   };
-  const uint32_t koff = k_lane_off(lane);
+  uint32_t koffs[4];
+  sp_k_lane_offs(lane, koffs);
   const uint32_t voff = sp_v_lane_off(lane);
+  // this lane's operand rows: K row perm_row(n) (chunk 2 ks + g, swizzled),
+  // V^T row 32 mt + n (chunk 2 h + g, swizzled)
+  const int g2 = lane >> 5, n32 = lane & 31;
+  const int kr_row = perm_row(n32);
+  auto kop_at = [=](const char* slot) {
+    return [=](int ks) {
+      const int c = (2 * ks + g2) ^ (kr_row & 15);
+      return *reinterpret_cast<const bf16x8*>(slot + kr_row * 256 + c * 16);
+    };
+  };
+  auto vop_at = [=](const char* slot) {
+    return [=](int h, int mt) {
+      const int d = 32 * mt + n32;
+      const int c = (2 * h + g2) ^ ((d >> 1) & 3);
+      return *reinterpret_cast<const bf16x8*>(slot + d * 64 + c * 16);
+    };
+  };
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, S, qf, lane);
@@ -726,58 +792,78 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     store_out(acc, sf, p.c, p.out, p.lse, head, q0, S, lane);
     return;
   }
+  auto qk_lds = [&](const char* slot, f32x16 (&sc)[1][2]) {
+    const auto kop = kop_at(slot);
+    f32x16 z = {};
+    sc[0][0] = z;
+    sc[0][1] = z;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a = kop(ks);
+      sc[0][0] = mfma32(a, qf[0][ks], sc[0][0]);
+      sc[0][1] = mfma32(a, qf[1][ks], sc[0][1]);
+    }
+  };
 
-  bf16x8 kr[8];
-  bf16x8 pb[1][2][2];
-  f32x16 s[1][2], sn[1][2];
+  // K of half tile t lives in K slot t % 2, V^T in V slot t % 3, both
+  // staged by LDS DMA; every step issues one half tile (8 + 8 loads), three
+  // ahead of the half tile whose P.V it runs.
+  f32x16 sa[1][2], sb[1][2];
   for (int attempt = 0;; ++attempt) {
-    // prologue: K(0), V(0), K(1), V(1) in flight
-    const int k0f = tile_k0(0);
-    load_k_sub(kbase, S, k0f, koff, kr, lane);
-    sp_issue_v(vbase, k0f, voff, slots);
-    int k0n = k0f;
-    if (nt > 1) {
-      k0n = tile_k0(1);
-      sp_issue_v(vbase, k0n, voff, slots + VHALF_B);
-    }
-    wait_vm_all();
-    qk_regs(kr, qf, s);
-    mask(s, k0f);
-    if (attempt == 0) raise_refs<1>(s, sf);
-    if (nt > 1) load_k_sub(kbase, S, k0n, koff, kr, lane);
+    const int k0_0 = tile_k0(0), k0_1 = tile_k0(1), k0_2 = tile_k0(2);
+    sp_issue_k(kbase, S, k0_0, koffs, kslots, lane);
+    sp_issue_v(vbase, k0_0, voff, vslots);
+    sp_issue_k(kbase, S, k0_1, koffs, kslots + KHALF_B, lane);
+    sp_issue_v(vbase, k0_1, voff, vslots + VHALF_B);
+    wait_vm24();  // K(0) resident
+    qk_lds(kslots, sa);
+    mask(sa, k0_0);
+    if (attempt == 0) raise_refs<1>(sa, sf);
+    wait_lgkm0();  // reads of K slot 0 done
+    sp_issue_k(kbase, S, k0_2, koffs, kslots, lane);
+    sp_issue_v(vbase, k0_2, voff, vslots + 2 * VHALF_B);
+    char* vcur = vslots;  // V slot of the current half tile t
+    char* vn1 = vslots + VHALF_B;
+    char* vn2 = vslots + 2 * VHALF_B;
     bool over = false;
-    for (int t = 0; t + 1 < nt; ++t) {
-      // K(t+1) registers and V(t) slot are ready once everything issued
-      // before V(t+1) has landed
-      wait_vm8();
-      qk_regs(kr, qf, sn);
-      over |= softmax_step<1>(s, sf, pb, p.c);
-      sp_pv(slots + (t & 1) * VHALF_B, pb, acc, lane);
-      const int k0cur = k0n;
-      if (t + 2 < nt) {  // prefetch tile t+2: K to registers, V^T to the slot
-        k0n = tile_k0(t + 2);
-        load_k_sub(kbase, S, k0n, koff, kr, lane);
-        wait_lgkm0();  // this wave's reads of the slot are done
-        sp_issue_v(vbase, k0n, voff, slots + (t & 1) * VHALF_B);
-      }
-      mask(sn, k0cur);
-      s[0][0] = sn[0][0];
-      s[0][1] = sn[0][1];
+    // step t: S(t) in sc -> P.V with V^T(t); QK(t+1) from K slot (t+1) % 2
+    // -> sn; then the loads of half tile t+3 (K into that K slot, V^T into
+    // t's V slot)
+    auto step = [&](int t, char* kslot, f32x16 (&sc)[1][2],
+                    f32x16 (&sn)[1][2]) {
+      wait_vm24();  // K(t+1) and V^T(t) resident
+      over |= attn_step(kop_at(kslot), vop_at(vcur), qf, sc, sn, sf, acc, p.c);
+      const int k0f = tile_k0(t + 3);
+      wait_lgkm0();  // this wave's reads of both slots are done
+      sp_issue_k(kbase, S, k0f, koffs, kslot, lane);
+      sp_issue_v(vbase, k0f, voff, vcur);
+      char* const done = vcur;
+      vcur = vn1;
+      vn1 = vn2;
+      vn2 = done;
+    };
+    // Rows are strictly ascending, so only the first block processed can be
+    // the diagonal one: step 0 masks S(1), later steps need no masks.
+    step(0, kslots + KHALF_B, sa, sb);
+    mask(sb, k0_1);
+    for (int t = 1; t + 1 < nt; t += 2) {
+      step(t, kslots, sb, sa);
+      step(t + 1, kslots + KHALF_B, sa, sb);
     }
-    wait_vm_all();
-    over |= softmax_step<1>(s, sf, pb, p.c);
-    sp_pv(slots + ((nt - 1) & 1) * VHALF_B, pb, acc, lane);
+    step(nt - 1, kslots, sb, sa);
+    wait_vm_all();  // no DMA may still target this wave's LDS slots
     if (attempt > 0 || !__any(over)) break;
     // Rare: a score far above its row's reference. Find every row's true
     // maximum over the kept keys, then recompute with it.
-    wait_lgkm0();
 #pragma unroll 1
     for (int t = 0; t < nt; ++t) {
       const int k0 = tile_k0(t);
-      load_k_sub(kbase, S, k0, koff, kr, lane);
-      qk_regs(kr, qf, s);
-      mask(s, k0);
-      raise_refs<1>(s, sf);
+      sp_issue_k(kbase, S, k0, koffs, kslots, lane);
+      wait_vm_all();
+      qk_lds(kslots, sa);
+      mask(sa, k0);
+      raise_refs<1>(sa, sf);
+      wait_lgkm0();
     }
     zero_acc(acc);
     sf.lsum[0] = sf.lsum[1] = 0.f;

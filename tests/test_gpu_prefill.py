@@ -131,8 +131,10 @@ def test_hybrid_with_full_budget_equals_dense(gpu_lib):
     assert diff <= 2 * 2 ** -8, diff
 
 
-def test_selection_override_is_used(gpu_lib):
-    # an explicit selection skips the indexer; outputs follow it exactly
+@pytest.mark.parametrize("with_diag", [True, False])
+def test_selection_override_is_used(gpu_lib, with_diag):
+    # an explicit selection skips the indexer; outputs follow it exactly,
+    # also when a row leaves out its own diagonal block
     S = 640
     x = make_prefill(_wl(S, Hq=2, Hkv=1, ret=(0,), window=32, top_k=2))
     d = _to_dev(x)
@@ -141,7 +143,8 @@ def test_selection_override_is_used(gpu_lib):
     cnt = np.zeros((1, n_b), dtype=np.int32)
     override = {0: {}}
     for qb in range(n_b):
-        s = sorted({0, qb} | ({qb // 2} if qb >= 2 else set()))
+        keep = {0, qb} if with_diag or qb == 0 else {0}
+        s = sorted(keep | ({qb // 2} if qb >= 2 else set()))
         sel[0, qb, :len(s)] = s
         cnt[0, qb] = len(s)
         override[0][qb] = np.array(s)
