@@ -415,11 +415,11 @@ __device__ __forceinline__ void diag_refs(const u16* kbase, int S, int q0,
 
 // One 32-key step with the work interleaved by hand: the QK MFMAs of the next
 // sub-tile (K operand kop(ks), ks = 0..7) and the P.V MFMAs of the current
-// one (V^T operand vop(h, mt)) are issued in 8 groups of 4, each next to an
-// eighth of the exp/pack work of the current scores s and the operand reads
-// of the next group. sched_barrier keeps the compiler from regrouping them
-// (it otherwise issues all QK MFMAs, then all exps, then all P.V MFMAs).
-// Returns whether a row sum left the safe range.
+// one (V^T operand vop(h, mt)) are issued in groups of 4, next to the
+// exp/pack work of the current scores s and the operand reads of the next
+// group. sched_barrier keeps the compiler from regrouping them (it otherwise
+// issues all QK MFMAs, then all exps, then all P.V MFMAs). Returns whether a
+// row sum left the safe range.
 template <class KOp, class VOp>
 __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
                                           const bf16x8 (&qf)[2][8],
@@ -449,47 +449,80 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   f32x16 z = {};
   sn[0][0] = z;
   sn[0][1] = z;
-  bf16x8 k0 = kop(0), k1 = kop(1);
-  // groups 0-3: QK ks = 2q, 2q+1 | exp of (j, h=0) quarter q
+  // Group g's MFMAs use operands read in group g-1, and each of groups 0-7
+  // carries a quarter of one (query tile, key half) of exp/pack work:
+  //   g0      read K ks 0,1                 | exp (j0,h0) and (j1,h0): q0
+  //   g1-g3   read K 2g,2g+1; QK ks 2g-2,2g-1 | exp q1..q3 of h0
+  //   g4      read V h0 mt0,1; QK ks 6,7    | exp (j0,h1) first half
+  //   g5      read V h0 mt2,3; PV h0 mt0,1  | exp (j0,h1) second half
+  //   g6      read V h1 mt0-3; PV h0 mt2,3  | exp (j1,h1) first half
+  //   g7      PV h1 j0                      | exp (j1,h1) second half
+  //   g8      PV h1 j1
+  // Group 0 has no MFMA of its own: the previous step's last ones drain
+  // while it runs.
+  bf16x8 ka = kop(0), kb = kop(1);
+  expq(0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const bf16x8 k2 = kop(q < 3 ? 2 * q + 2 : 0);
-    const bf16x8 k3 = kop(q < 3 ? 2 * q + 3 : 1);
-    sn[0][0] = mfma32(k0, qf[0][2 * q], sn[0][0]);
-    sn[0][1] = mfma32(k0, qf[1][2 * q], sn[0][1]);
-    sn[0][0] = mfma32(k1, qf[0][2 * q + 1], sn[0][0]);
-    sn[0][1] = mfma32(k1, qf[1][2 * q + 1], sn[0][1]);
+  for (int q = 1; q < 4; ++q) {
+    const bf16x8 kc = kop(2 * q), kd = kop(2 * q + 1);
+    sn[0][0] = mfma32(ka, qf[0][2 * q - 2], sn[0][0]);
+    sn[0][1] = mfma32(ka, qf[1][2 * q - 2], sn[0][1]);
+    sn[0][0] = mfma32(kb, qf[0][2 * q - 1], sn[0][0]);
+    sn[0][1] = mfma32(kb, qf[1][2 * q - 1], sn[0][1]);
     expq(q >> 1, 0, 2 * (q & 1));
-    k0 = k2;
-    k1 = k3;
+    ka = kc;
+    kb = kd;
     __builtin_amdgcn_sched_barrier(0);
   }
-  // groups 4-5: P.V h=0 (mt 2r, 2r+1) | exp of (j = r, h=1)
-  bf16x8 v0 = vop(0, 0), v1 = vop(0, 1);
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const bf16x8 v2 = vop(r == 0 ? 0 : 1, r == 0 ? 2 : 0);
-    const bf16x8 v3 = vop(r == 0 ? 0 : 1, r == 0 ? 3 : 1);
+  // g4
+  bf16x8 va = vop(0, 0), vb = vop(0, 1);
+  sn[0][0] = mfma32(ka, qf[0][6], sn[0][0]);
+  sn[0][1] = mfma32(ka, qf[1][6], sn[0][1]);
+  sn[0][0] = mfma32(kb, qf[0][7], sn[0][0]);
+  sn[0][1] = mfma32(kb, qf[1][7], sn[0][1]);
+  expq(0, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // g5
+  const bf16x8 vc = vop(0, 2), vd = vop(0, 3);
+  {
     const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
-    acc[0][2 * r] = mfma32(v0, p00, acc[0][2 * r]);
-    acc[1][2 * r] = mfma32(v0, p10, acc[1][2 * r]);
-    acc[0][2 * r + 1] = mfma32(v1, p00, acc[0][2 * r + 1]);
-    acc[1][2 * r + 1] = mfma32(v1, p10, acc[1][2 * r + 1]);
-    expq(r, 1, 0);
-    expq(r, 1, 2);
-    v0 = v2;
-    v1 = v3;
-    __builtin_amdgcn_sched_barrier(0);
+    acc[0][0] = mfma32(va, p00, acc[0][0]);
+    acc[1][0] = mfma32(va, p10, acc[1][0]);
+    acc[0][1] = mfma32(vb, p00, acc[0][1]);
+    acc[1][1] = mfma32(vb, p10, acc[1][1]);
   }
-  // groups 6-7: P.V h=1, query tile 0 then 1 (v0, v1 hold mt 0, 1)
-  const bf16x8 v2 = vop(1, 2), v3 = vop(1, 3);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const bf16x8 p = pb(j, 1);
-    acc[j][0] = mfma32(v0, p, acc[j][0]);
-    acc[j][1] = mfma32(v1, p, acc[j][1]);
-    acc[j][2] = mfma32(v2, p, acc[j][2]);
-    acc[j][3] = mfma32(v3, p, acc[j][3]);
+  expq(0, 1, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  // g6
+  const bf16x8 v10 = vop(1, 0), v11 = vop(1, 1), v12 = vop(1, 2),
+               v13 = vop(1, 3);
+  {
+    const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
+    acc[0][2] = mfma32(vc, p00, acc[0][2]);
+    acc[1][2] = mfma32(vc, p10, acc[1][2]);
+    acc[0][3] = mfma32(vd, p00, acc[0][3]);
+    acc[1][3] = mfma32(vd, p10, acc[1][3]);
+  }
+  expq(1, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // g7
+  {
+    const bf16x8 p = pb(0, 1);
+    acc[0][0] = mfma32(v10, p, acc[0][0]);
+    acc[0][1] = mfma32(v11, p, acc[0][1]);
+    acc[0][2] = mfma32(v12, p, acc[0][2]);
+    acc[0][3] = mfma32(v13, p, acc[0][3]);
+  }
+  expq(1, 1, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  // g8
+  {
+    const bf16x8 p = pb(1, 1);
+    acc[1][0] = mfma32(v10, p, acc[1][0]);
+    acc[1][1] = mfma32(v11, p, acc[1][1]);
+    acc[1][2] = mfma32(v12, p, acc[1][2]);
+    acc[1][3] = mfma32(v13, p, acc[1][3]);
   }
   sf.lsum[0] += ls[0];
   sf.lsum[1] += ls[1];
@@ -662,10 +695,11 @@ struct SparseParams {
 };
 
 // V^T half tile (32 keys): row d x 4 chunks of 16 B, chunk c at
-// c ^ ((d >> 1) & 3). Load ins (0..7) covers rows 16 ins .. 16 ins + 15; the
-// lane part of the global offset is the same for every load and tile.
+// c ^ ((d >> 2) & 3), so the 16 rows that 16 consecutive lanes read hit 16
+// distinct bank groups. Load ins (0..7) covers rows 16 ins .. 16 ins + 15;
+// the lane part of the global offset is the same for every load and tile.
 __device__ __forceinline__ uint32_t sp_v_lane_off(int lane) {
-  const int c = (lane & 3) ^ ((lane >> 3) & 3);
+  const int c = (lane & 3) ^ ((lane >> 4) & 3);
   return (uint32_t)((lane >> 2) * 128 + c * 16);
 }
 
@@ -776,7 +810,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   auto vop_at = [=](const char* slot) {
     return [=](int h, int mt) {
       const int d = 32 * mt + n32;
-      const int c = (2 * h + g2) ^ ((d >> 1) & 3);
+      const int c = (2 * h + g2) ^ ((d >> 2) & 3);
       return *reinterpret_cast<const bf16x8*>(slot + d * 64 + c * 16);
     };
   };
