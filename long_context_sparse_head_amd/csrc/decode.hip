@@ -154,7 +154,8 @@ struct DecAttnArgs {
 };
 
 // grid (n_split, n_units, B), 256 threads. Each wave takes 32-key tiles in
-// turn; S^T = K Q^T on MFMA (heads along N), P.V on the vector ALU.
+// turn, independently of the other waves until the final merge; S^T = K Q^T
+// on MFMA (heads along N), P.V on the vector ALU.
 __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
   __shared__ float Pw[4][32][33];     // p[key row][head], per wave
   __shared__ float alw[4][32];        // per-head rescale of this tile
@@ -171,7 +172,10 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
 
   // key tiles of this split
   int nt = 0, k_begin = 0, k_end = 0, blk0 = 0;
-  const int32_t* list = nullptr;
+  // The selection is read-only here: the constant address space lets the
+  // compiler use scalar loads, which leave the K/V prefetch waits alone.
+  typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+  const_i32_ptr list = nullptr;
   if (kind == 0) {
     const int lo = max(0, L - a.window);
     const int nk = L - lo;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
   } else {
     const int rho = a.rho[u];
     const int nsel = a.sel_cnt[(size_t)b * a.n_ret + rho];
-    list = a.sel + ((size_t)b * a.n_ret + rho) * a.sel_width;
+    list = (const_i32_ptr)(a.sel + ((size_t)b * a.n_ret + rho) * a.sel_width);
     const int bps = (nsel + a.n_split - 1) / a.n_split;
     blk0 = min(s * bps, nsel);
     const int blk1 = min(blk0 + bps, nsel);
@@ -214,27 +218,50 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
     for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
   const int kg = lane >> 4, dc = lane & 15;
 
-  const int iters = (nt + 3) / 4;
-  for (int it = 0; it < iters; ++it) {
-    const int t = it * 4 + wave;
-    int base = 0, nvalid = 0;
+  // Wave w takes tiles w, w + 4, ... Loads are issued for every iteration
+  // (an empty tile re-reads row 0), so each iteration has the same loads:
+  // the K rows of the next tile are fetched during this tile's P.V, the V
+  // rows of this tile during its QK and softmax.
+  auto tile_at = [&](int t, int& base, int& nvalid) {
+    base = 0;
+    nvalid = 0;
     if (t < nt) {
       if (kind == 0) {
         base = k_begin + 32 * t;
         nvalid = min(32, k_end - base);
       } else {
-        const int blk = list[blk0 + (t >> 1)];
+        const int blk = list[__builtin_amdgcn_readfirstlane(blk0 + (t >> 1))];
         base = blk * 64 + 32 * (t & 1);
         nvalid = max(0, min(32, L - base));
+        if (nvalid == 0) base = 0;
       }
     }
-    if (t < nt && nvalid > 0) {
-      f32x16 sacc = {};
-      const int krow = n < nvalid ? base + n : base;
-      const u16* kp = kbase + (size_t)krow * kD + 8 * g;
+  };
+  auto load_k = [&](int base, int nvalid, bf16x8 (&kq)[8]) {
+    const int krow = n < nvalid ? base + n : base;
+    const u16* kp = kbase + (size_t)krow * kD + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(kp + 16 * ks), qf[ks], sacc);
+    for (int ks = 0; ks < 8; ++ks)
+      kq[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+  };
+  int base, nvalid;
+  tile_at(wave, base, nvalid);
+  bf16x8 kq[8];
+  load_k(base, nvalid, kq);
+  const int iters = (nt + 3) / 4;
+  for (int it = 0; it < iters; ++it) {
+    uint4 vr[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int row = 4 * jj + kg;
+      const int vrow = row < nvalid ? base + row : base;
+      vr[jj] = *reinterpret_cast<const uint4*>(vbase + (size_t)vrow * kD + 8 * dc);
+    }
+    const bool live = nvalid > 0;  // wave-uniform
+    if (live) {
+      f32x16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(kq[ks], qf[ks], sacc);
       // accumulator element i: key row 8*(i/4) + 4*g + i%4, head n
       float tmax = -INFINITY;
 #pragma unroll
@@ -254,13 +281,16 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
         const int row = 8 * (i >> 2) + 4 * g + (i & 3);
         const float pv = fast_exp2(fmaf(sacc[i], a.c, -mc));
         ls += pv;
-        Pw[wave][row][n] = pv;
+        Pw[wave][row][n] = pv;  // this wave's slice only: no barrier
       }
       l_run = l_run * alpha + ls;
       if (g == 0) alw[wave][n] = alpha;
     }
-    __syncthreads();
-    if (t < nt && nvalid > 0) {
+    // next tile's K rows, in flight during this tile's P.V
+    int nbase, nnvalid;
+    tile_at((it + 1) * 4 + wave, nbase, nnvalid);
+    load_k(nbase, nnvalid, kq);
+    if (live) {
 #pragma unroll
       for (int j = 0; j < kDecMaxUnitHeads; ++j) {
         if (j < nh) {
@@ -273,9 +303,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
       for (int jj = 0; jj < 8; ++jj) {
         const int row = 4 * jj + kg;
         if (row < nvalid) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(
-              vbase + (size_t)(base + row) * kD + 8 * dc);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+          const uint32_t w[4] = {vr[jj].x, vr[jj].y, vr[jj].z, vr[jj].w};
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -293,7 +321,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
         }
       }
     }
-    __syncthreads();
+    base = nbase;
+    nvalid = nnvalid;
   }
 
   // wave-level totals: PV over the 4 key groups, l over the lane pair
