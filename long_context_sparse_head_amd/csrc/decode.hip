@@ -118,12 +118,32 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   const float* cb = cent + row_id * a.nbmax * a.r;
   float* srow = cscores + row_id * a.nbmax;
   const bool in_lds = n_c <= TK_LDS;
-  for (int e = tid; e < n_c; e += 256) {
-    const float* c = cb + (size_t)(e + 1) * a.r;
-    float s = 0.f;
-    for (int rr = 0; rr < a.r; ++rr) s = fmaf(qt[rr], c[rr], s);
-    if (in_lds) keys[e + (e >> 5)] = order_key(s);
-    else srow[e] = s;
+  // four candidates per thread in flight; each centroid row is r floats
+  // read as float4 (consecutive lanes read consecutive rows)
+  for (int e0 = tid; e0 < n_c; e0 += 4 * 256) {
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < a.r; rr += 4) {
+      float4 cv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = min(e0 + 256 * u, n_c - 1);
+        cv[u] = *reinterpret_cast<const float4*>(cb + (size_t)(e + 1) * a.r + rr);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc[u] = fmaf(qt[rr], cv[u].x, sc[u]);
+        sc[u] = fmaf(qt[rr + 1], cv[u].y, sc[u]);
+        sc[u] = fmaf(qt[rr + 2], cv[u].z, sc[u]);
+        sc[u] = fmaf(qt[rr + 3], cv[u].w, sc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + 256 * u;
+      if (e >= n_c) break;
+      if (in_lds) keys[e + (e >> 5)] = order_key(sc[u]);
+      else srow[e] = sc[u];
+    }
   }
   __syncthreads();
   auto getk = [&](int e) -> uint32_t {

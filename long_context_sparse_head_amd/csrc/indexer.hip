@@ -294,7 +294,17 @@ __global__ __launch_bounds__(256) void topk_kernel(
   // 1 <= top_k < n_c
   const bool in_lds = n_c <= TK_LDS;
   if (in_lds) {
-    for (int e = tid; e < n_c; e += 256) keys[e + (e >> 5)] = order_key(row[e]);
+    // eight loads per thread in flight
+    for (int e0 = tid; e0 < n_c; e0 += 8 * 256) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = row[min(e0 + 256 * u, n_c - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < n_c) keys[e + (e >> 5)] = order_key(v[u]);
+      }
+    }
     __syncthreads();
   }
   auto getk = [&](int e) -> uint32_t {

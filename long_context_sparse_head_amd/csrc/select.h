@@ -2,10 +2,12 @@
 // indexer and the decode block choice.
 //
 // The k largest of n candidate scores (ties: lower candidate index first) are
-// found by a 4-pass, 8-bit radix select on order-preserving 32-bit keys, then
-// written in ascending index order by a prefix sum over thread-contiguous
-// chunks. The result is exact and deterministic (LDS atomics only build
-// histograms, whose totals do not depend on order).
+// found on order-preserving 32-bit keys (a value histogram locates the bin
+// of the threshold, an exact radix select inside it finds the threshold),
+// then written in ascending index order by a prefix sum over
+// thread-contiguous chunks. The result is exact and deterministic (LDS
+// atomics only build histograms and a candidate set whose order does not
+// matter).
 #pragma once
 #include "common.h"
 
@@ -60,10 +62,14 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t v, int* tmp) {
   return r;
 }
 
+constexpr int TK_CAND = 2048;  // keys of the threshold bin held in LDS
+
 struct TopkShared {
   int hist[256];
   int tmp[8];
   int bcast[4];
+  int ncand;
+  uint32_t cand[TK_CAND];
 };
 
 struct TopkResult {
@@ -71,24 +77,22 @@ struct TopkResult {
   int count_ge;     // candidates with key >= T (block-uniform)
 };
 
-// Requires 1 <= k < n. getk(e) returns the key of candidate e (0 <= e < n).
-// Writes out[0..k-1] = idx_base + chosen e, ascending. Every thread of the
-// block must call it.
-template <class GetK>
-__device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
-                                 int idx_base, TopkShared& sh) {
+// The kk-th largest (1 <= kk <= count) of the keys key(i), i < m, for which
+// pred(i) holds: a 4-pass, 8-bit radix select. Every thread of the block
+// must call it; the result is block-uniform.
+template <class Key, class Pred>
+__device__ uint32_t radix_kth(Key key, Pred pred, int m, int kk,
+                              TopkShared& sh) {
   const int tid = threadIdx.x;
-  const int C = (n + 255) / 256;
-  const int e0 = min(tid * C, n), e1 = min(e0 + C, n);
   uint32_t prefix = 0, pmask = 0;
-  int kk = k;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     sh.hist[tid] = 0;
     __syncthreads();
-    for (int e = e0; e < e1; ++e) {
-      const uint32_t key = getk(e);
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255], 1);
+    for (int i = tid; i < m; i += 256) {
+      if (!pred(i)) continue;
+      const uint32_t x = key(i);
+      if ((x & pmask) == prefix) atomicAdd(&sh.hist[(x >> shift) & 255], 1);
     }
     __syncthreads();
     const int b = 255 - tid;  // thread t covers bin 255-t: scan from the top
@@ -105,15 +109,109 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
     kk -= sh.bcast[1];
     __syncthreads();
   }
-  const uint32_t T = prefix;  // kk = how many keys equal to T are taken
+  return prefix;
+}
+
+// Requires 1 <= k < n. getk(e) returns the key of candidate e (0 <= e < n).
+// Writes out[0..k-1] = idx_base + chosen e, ascending (ties: lower e first).
+// Every thread of the block must call it.
+//
+// The threshold T (the k-th largest key) is found in two steps: keys are
+// histogrammed into 256 bins of a linear quantisation of their values
+// between the row's minimum and maximum (order-preserving, and spread even
+// when the values share a few exponents, unlike the top bits of the key),
+// which fixes the bin holding T; the keys of that bin alone are then
+// gathered in LDS and searched exactly. A bin too large to gather is
+// searched in place.
+template <class GetK>
+__device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
+                                 int idx_base, TopkShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int C = (n + 255) / 256;
+  const int e0 = min(tid * C, n), e1 = min(e0 + C, n);
+  // range of the non-NaN keys (NaN keys lie above +inf or below -inf)
+  auto is_nan_key = [](uint32_t x) {
+    return x > 0xff800000u || x < 0x007fffffu;
+  };
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int e = e0; e < e1; ++e) {
+    const uint32_t x = getk(e);
+    if (!is_nan_key(x)) {
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  lo = block_min_u32(lo, sh.tmp);
+  hi = block_max_u32(hi, sh.tmp);
+  float flo = 0.f, scale = 0.f;
+  if (lo <= hi) {
+    flo = order_key_inv(lo);
+    const float span = order_key_inv(hi) - flo;
+    if (span > 0.f) scale = 255.99f / span;
+    if (!(scale < 1e30f)) scale = 0.f;  // inf span or tiny span: one bin
+  }
+  auto bin = [&](uint32_t x) -> int {
+    if (x > 0xff800000u) return 255;  // +NaN keys
+    if (x < 0x007fffffu) return 0;    // -NaN keys
+    float f = (order_key_inv(x) - flo) * scale;
+    f = fminf(fmaxf(f, 0.f), 255.f);  // NaN (inf * 0) -> 0
+    return (int)f;
+  };
+  sh.hist[tid] = 0;
+  __syncthreads();
+  for (int e = e0; e < e1; ++e) atomicAdd(&sh.hist[bin(getk(e))], 1);
+  __syncthreads();
+  {
+    const int b = 255 - tid;
+    const int h = sh.hist[b];
+    const int incl = block_incl_scan(h, sh.tmp);
+    const int gt = incl - h;
+    if (h > 0 && gt < k && k <= incl) {
+      sh.bcast[0] = b;
+      sh.bcast[1] = gt;
+      sh.bcast[2] = h;
+    }
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+  }
+  const int bstar = sh.bcast[0], kk = k - sh.bcast[1], nbin = sh.bcast[2];
+  uint32_t T;
+  if (nbin <= TK_CAND) {
+    // gather the bin's keys (wave-aggregated appends)
+    for (int i = 0; i < C; ++i) {
+      const int e = e0 + i;
+      const uint32_t x = e < e1 ? getk(e) : 0u;
+      const bool in = e < e1 && bin(x) == bstar;
+      const uint64_t bal = __ballot(in);
+      if (bal) {
+        int base = 0;
+        if (lane == __builtin_ctzll(bal))
+          base = atomicAdd(&sh.ncand, (int)__builtin_popcountll(bal));
+        base = __shfl(base, (int)__builtin_ctzll(bal));
+        const uint64_t below = lane ? (bal & ((1ull << lane) - 1)) : 0ull;
+        if (in) sh.cand[base + __builtin_popcountll(below)] = x;
+      }
+    }
+    __syncthreads();
+    T = radix_kth([&](int i) { return sh.cand[i]; }, [](int) { return true; },
+                  nbin, kk, sh);
+  } else {
+    T = radix_kth(getk, [&](int e) { return bin(getk(e)) == bstar; }, n, kk,
+                  sh);
+  }
+  // take every key above T and the first (by index) keys equal to T
   int ngt = 0, neq = 0;
   for (int e = e0; e < e1; ++e) {
-    const uint32_t key = getk(e);
-    ngt += key > T;
-    neq += key == T;
+    const uint32_t x = getk(e);
+    ngt += x > T;
+    neq += x == T;
   }
+  const int gt_incl = block_incl_scan(ngt, sh.tmp);
+  if (tid == 255) sh.bcast[3] = gt_incl;
+  __syncthreads();
+  const int keq = k - sh.bcast[3];  // keys equal to T to take
   const int eq_incl = block_incl_scan(neq, sh.tmp);
-  const int take_eq = max(0, min(kk - (eq_incl - neq), neq));
+  const int take_eq = max(0, min(keq - (eq_incl - neq), neq));
   const int ntake = ngt + take_eq;
   const int pos_incl = block_incl_scan(ntake, sh.tmp);
   const int ge_incl = block_incl_scan(ngt + neq, sh.tmp);
@@ -121,9 +219,9 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
   int pos = pos_incl - ntake;
   int eq_seen = 0;
   for (int e = e0; e < e1; ++e) {
-    const uint32_t key = getk(e);
-    bool t = key > T;
-    if (key == T) {
+    const uint32_t x = getk(e);
+    bool t = x > T;
+    if (x == T) {
       t = eq_seen < take_eq;
       ++eq_seen;
     }

@@ -123,3 +123,19 @@ def test_decode_deterministic(gpu_lib):
     b = run_gpu(gpu_lib, y)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_decode_equal_centroid_scores_keep_the_lowest_blocks(gpu_lib):
+    # constant keys => equal centroids => the kept blocks are the sink, the
+    # lowest-index top_k candidates and the recent blocks; 4093 candidates
+    # per row also exceed the selection's LDS gather size
+    y = make_decode(_wl(2, 1 << 18, Hq=4, Hkv=1, ret=(2,), window=64,
+                        top_k=64))
+    y["k_cache"] = torch.full_like(y["k_cache"], -0.25)
+    out, lse, sel, cent = run_gpu(gpu_lib, y)
+    sel = sel.cpu().numpy()
+    for b in range(2):
+        n_b = int(y["cache_len"][b]) // 64
+        want = [0] + list(range(1, 65)) + [n_b - 2, n_b - 1]
+        got = [int(v) for v in sel[b, 0] if v >= 0]
+        assert got == want, (b, got[:5], got[-5:])

@@ -240,3 +240,27 @@ def test_reference_restart_when_an_early_key_dominates(gpu_lib):
     x["q"], x["k"] = q, k
     r = full_check(gpu_lib, x, "restart")
     assert np.isfinite(r["out"].float().cpu().numpy()).all()
+
+
+def test_indexer_equal_scores_keep_the_lowest_blocks(gpu_lib):
+    # Every key equal => every candidate block of a row scores the same, so
+    # the kept set is fixed by the tie rule alone: blocks 1..k (lower index
+    # first), plus the sink and the diagonal. Rows longer than 2048
+    # candidates put more keys in the threshold's value bin than the
+    # selection gathers in LDS, which exercises its in-place search.
+    S, k = 2200 * 64, 37
+    x = make_prefill(_wl(S, Hq=2, Hkv=1, ret=(1,), window=64, top_k=k))
+    kc = torch.full_like(x["k"], 0.5)
+    d = _to_dev(dict(x, k=kc))
+    sel, cnt, kth, _ = gpu_lib.indexer_select(
+        d["q"], d["k"], x["is_retrieval"], d["p_q_t"], d["p_k_t"], k, kth=True)
+    torch.cuda.synchronize()
+    sel, cnt, kth = sel.cpu().numpy()[0], cnt.cpu().numpy()[0], kth.cpu().numpy()[0]
+    n_b = S // 64
+    for qb in range(n_b):
+        cand = list(range(1, qb))[:k]
+        want = sorted({0, qb} | set(cand))
+        assert int(cnt[qb]) == len(want), qb
+        assert list(sel[qb][:cnt[qb]]) == want, qb
+        if qb - 1 > k:  # s_k and s_{k+1} both exist and are equal
+            assert kth[qb][0] == kth[qb][1], qb
