@@ -373,7 +373,7 @@ int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
   return RTP_OK;
 }
 
-static const int kDecSplit = 16;
+static const int kDecSplit = 8;
 
 struct DecodeLayout {
   size_t cs, sel, po, pml, total;

@@ -176,9 +176,9 @@ struct DecAttnArgs {
 // grid (n_split, n_units, B), 256 threads. Each wave takes 32-key tiles in
 // turn, independently of the other waves until the final merge; S^T = K Q^T
 // on MFMA (heads along N), P.V on the vector ALU.
-__global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
-  __shared__ float Pw[4][32][33];     // p[key row][head], per wave
-  __shared__ float alw[4][32];        // per-head rescale of this tile
+__global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float Pw[4][32][kDecMaxUnitHeads];
+  __shared__ __attribute__((aligned(16))) float alw[4][kDecMaxUnitHeads];
   __shared__ float red_o[4][kDecMaxUnitHeads][kD];
   __shared__ float red_ml[4][kDecMaxUnitHeads][2];
   const int s = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
@@ -231,12 +231,10 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
   }
 
   float m_run = -1e30f, l_run = 0.f;  // softmax state of head n (lane pair)
-  float o[kDecMaxUnitHeads][8];       // PV lanes: key group kg, d chunk dc
+  // P.V: lane l accumulates d = 2l, 2l+1 of every head of the unit
+  float o[kDecMaxUnitHeads][2];
 #pragma unroll
-  for (int j = 0; j < kDecMaxUnitHeads; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
-  const int kg = lane >> 4, dc = lane & 15;
+  for (int j = 0; j < kDecMaxUnitHeads; ++j) o[j][0] = o[j][1] = 0.f;
 
   // Wave w takes tiles w, w + 4, ... Loads are issued for every iteration
   // (an empty tile re-reads row 0), so each iteration has the same loads:
@@ -270,12 +268,12 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
   load_k(base, nvalid, kq);
   const int iters = (nt + 3) / 4;
   for (int it = 0; it < iters; ++it) {
-    uint4 vr[8];
+    uint32_t vr[32];  // V[row][2 lane, 2 lane + 1], rows past nvalid re-read
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int row = 4 * jj + kg;
+    for (int row = 0; row < 32; ++row) {
       const int vrow = row < nvalid ? base + row : base;
-      vr[jj] = *reinterpret_cast<const uint4*>(vbase + (size_t)vrow * kD + 8 * dc);
+      vr[row] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)vrow * kD +
+                                                   2 * lane);
     }
     const bool live = nvalid > 0;  // wave-uniform
     if (live) {
@@ -301,42 +299,36 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
         const int row = 8 * (i >> 2) + 4 * g + (i & 3);
         const float pv = fast_exp2(fmaf(sacc[i], a.c, -mc));
         ls += pv;
-        Pw[wave][row][n] = pv;  // this wave's slice only: no barrier
+        if (n < kDecMaxUnitHeads) Pw[wave][row][n] = pv;  // own slice only
       }
       l_run = l_run * alpha + ls;
-      if (g == 0) alw[wave][n] = alpha;
+      if (g == 0 && n < kDecMaxUnitHeads) alw[wave][n] = alpha;
     }
     // next tile's K rows, in flight during this tile's P.V
     int nbase, nnvalid;
     tile_at((it + 1) * 4 + wave, nbase, nnvalid);
     load_k(nbase, nnvalid, kq);
     if (live) {
+      const float4 al0 = *reinterpret_cast<const float4*>(&alw[wave][0]);
+      const float4 al1 = *reinterpret_cast<const float4*>(&alw[wave][4]);
+      const float al[8] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
 #pragma unroll
       for (int j = 0; j < kDecMaxUnitHeads; ++j) {
-        if (j < nh) {
-          const float al = alw[wave][j];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[j][e] *= al;
-        }
+        o[j][0] *= al[j];
+        o[j][1] *= al[j];
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int row = 4 * jj + kg;
-        if (row < nvalid) {
-          const uint32_t w[4] = {vr[jj].x, vr[jj].y, vr[jj].z, vr[jj].w};
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(w[e] << 16);
-            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-          }
+      for (int row = 0; row < 32; ++row) {
+        if (row < nvalid) {  // wave-uniform
+          const float v0 = __uint_as_float(vr[row] << 16);
+          const float v1 = __uint_as_float(vr[row] & 0xffff0000u);
+          const float4 p0 = *reinterpret_cast<const float4*>(&Pw[wave][row][0]);
+          const float4 p1 = *reinterpret_cast<const float4*>(&Pw[wave][row][4]);
+          const float pj[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
           for (int j = 0; j < kDecMaxUnitHeads; ++j) {
-            if (j < nh) {
-              const float pj = Pw[wave][row][j];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) o[j][e] = fmaf(pj, v[e], o[j][e]);
-            }
+            o[j][0] = fmaf(pj[j], v0, o[j][0]);
+            o[j][1] = fmaf(pj[j], v1, o[j][1]);
           }
         }
       }
@@ -345,22 +337,12 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecAttnArgs a) {
     nvalid = nnvalid;
   }
 
-  // wave-level totals: PV over the 4 key groups, l over the lane pair
-#pragma unroll
-  for (int j = 0; j < kDecMaxUnitHeads; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float x = o[j][e];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      o[j][e] = x;
-    }
+  // wave-level totals: l over the lane pair
   l_run += __shfl_xor(l_run, 32);
-  if (kg == 0) {
 #pragma unroll
-    for (int j = 0; j < kDecMaxUnitHeads; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_o[wave][j][8 * dc + e] = o[j][e];
+  for (int j = 0; j < kDecMaxUnitHeads; ++j) {
+    red_o[wave][j][2 * lane] = o[j][0];
+    red_o[wave][j][2 * lane + 1] = o[j][1];
   }
   if (g == 0 && n < kDecMaxUnitHeads) {
     red_ml[wave][n][0] = m_run;
