@@ -174,6 +174,29 @@ int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
                         const uint8_t* is_retrieval, const float* p_k, int r,
                         int block, float* centroids, rtp_stream_t stream);
 
+/*
+ * rtp_decode_append - appends one token per sequence to the decode cache and
+ * keeps the centroids of rtp_build_centroids current (RTPurboV2: the K
+ * cache stays clustered in the low-rank space during decode; here a block's
+ * centroid is added when its last token arrives):
+ *   k_cache[b,g,L_b,:] = k_new[b,g,:], v_cache[b,g,L_b,:] = v_new[b,g,:]
+ *   with L_b = cache_len[b]; if L_b + 1 is a multiple of block, the
+ *   centroids of block L_b / block are computed for every retrieval head
+ *   exactly as rtp_build_centroids would; then cache_len[b] = L_b + 1.
+ *
+ *  k_cache, v_cache [B,Hkv,Lmax,d] bf16 (in/out); cache_len [B] int32
+ *  DEVICE array (in/out); k_new, v_new [B,Hkv,d] bf16;
+ *  p_k [n_ret,r,d] fp32 and centroids [B,n_ret,Lmax/block,r] fp32 (in/out;
+ *  both may be NULL when no head is a retrieval head).
+ *  The caller keeps cache_len[b] < Lmax; a sequence whose cache is full is
+ *  left unchanged. Two kernels on `stream`, nothing allocated.
+ */
+int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
+                      const void* k_new, const void* v_new, int B, int Lmax,
+                      int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                      const float* p_k, int r, int block, float* centroids,
+                      rtp_stream_t stream);
+
 /* Workspace bytes for rtp_hybrid_attn_decode. */
 size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
                                   const uint8_t* is_retrieval, int r,

@@ -24,7 +24,7 @@ __all__ = [
     "load", "LIB_PATH", "RtpError", "prefill_workspace_bytes",
     "dense_workspace_bytes", "decode_workspace_bytes", "indexer_select",
     "hybrid_attn_prefill", "dense_attn_prefill", "build_centroids",
-    "hybrid_attn_decode", "version", "KernelTimer",
+    "hybrid_attn_decode", "decode_append", "version", "KernelTimer",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
@@ -57,6 +57,8 @@ _SIGS = {
                                     _P, _Z, _P]),
     "rtp_build_centroids": (_I, [_P, _P, _I, _I, _I, _I, _I, _U8P, _P, _I, _I,
                                  _P, _P]),
+    "rtp_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U8P,
+                               _P, _I, _I, _P, _P]),
     "rtp_hybrid_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _U8P,
                                     _I, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                     _P, _Z, _P]),
@@ -319,6 +321,32 @@ def build_centroids(k_cache, cache_len, is_retrieval, p_k, r: int = 16,
         _ptr(k_cache), _ptr(cache_len), B, Lmax, Hq, Hkv, d, mp, _ptr(p_k), r,
         block, _ptr(out), _stream(k_cache.device)), "rtp_build_centroids")
     return out
+
+
+def decode_append(k_cache, v_cache, cache_len, k_new, v_new, is_retrieval,
+                  p_k=None, centroids=None, r: int = 16, block: int = 64):
+    """Appends k_new/v_new [B,Hkv,d] at cache_len (in place), adds the
+    centroid of each block the token completes, increments cache_len."""
+    lib = load()
+    B, Hkv, Lmax, d = k_cache.shape
+    Hq = len(is_retrieval)
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(v_cache, torch.bfloat16, "v_cache", (B, Hkv, Lmax, d))
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    _dev(k_new, torch.bfloat16, "k_new", (B, Hkv, d))
+    _dev(v_new, torch.bfloat16, "v_new", (B, Hkv, d))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    if n_ret:
+        _proj(p_k, n_ret, r, d, "p_k")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, Lmax // block, r))
+    _check(lib.rtp_decode_append(
+        _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(k_new),
+        _ptr(v_new), B, Lmax, Hq, Hkv, d, mp,
+        _ptr(p_k) if n_ret else None, r, block,
+        _ptr(centroids) if n_ret else None, _stream(k_cache.device)),
+        "rtp_decode_append")
 
 
 def hybrid_attn_decode(q, k_cache, v_cache, cache_len, is_retrieval,

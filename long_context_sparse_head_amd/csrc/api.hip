@@ -373,6 +373,32 @@ int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
   return RTP_OK;
 }
 
+int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
+                      const void* k_new, const void* v_new, int B, int Lmax,
+                      int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                      const float* p_k, int r, int block, float* centroids,
+                      rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(0, Hq, Hkv, d)) return e;
+  if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, 0)) return e;
+  if (B == 0) return RTP_OK;
+  if (!k_cache || !v_cache || !cache_len || !k_new || !v_new)
+    return fail(RTP_EINVAL, "cache, cache_len and new-token pointers must be non-NULL");
+  if (hi.n_ret > 0 && (!p_k || !centroids))
+    return fail(RTP_EINVAL, "p_k and centroids must be non-NULL with retrieval heads");
+  hipError_t e = rtp::launch_decode_append(
+      static_cast<rtp::u16*>(k_cache), static_cast<rtp::u16*>(v_cache),
+      cache_len, static_cast<const rtp::u16*>(k_new),
+      static_cast<const rtp::u16*>(v_new), p_k, centroids, B, Lmax, Hkv,
+      hi.n_ret, r, Hq / Hkv, hi.ret_heads.data(),
+      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return RTP_OK;
+}
+
 static const int kDecSplit = 8;
 
 struct DecodeLayout {

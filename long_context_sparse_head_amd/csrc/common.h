@@ -81,6 +81,12 @@ hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
                                   int Lmax, int Hkv, int n_ret, int r, int G,
                                   const uint8_t* ret_heads, hipStream_t st);
 
+hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
+                                const u16* k_new, const u16* v_new,
+                                const float* p_k, float* cent, int B,
+                                int Lmax, int Hkv, int n_ret, int r, int G,
+                                const uint8_t* ret_heads, hipStream_t st);
+
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 __host__ __device__ inline int64_t tri_rows(int64_t n_b) {  // candidates of rows 2..n_b-1
   return n_b >= 3 ? (n_b - 2) * (n_b - 1) / 2 : 0;

@@ -28,19 +28,15 @@ struct CentArgs {
   uint8_t kvh_of_rho[kMaxHeads];
 };
 
-// grid (nbmax, n_ret, B), one wave: mean of the block's keys, then projected
-// (equal to the mean of the projected keys by linearity). Full blocks only.
-__global__ __launch_bounds__(64) void build_centroids_kernel(
-    const u16* __restrict__ kc, const int32_t* __restrict__ cache_len,
-    const float* __restrict__ p_k, const CentArgs ca, float* __restrict__ cent) {
-  __shared__ float mean[kD];
-  const int kb = blockIdx.x, rho = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
-  int L = cache_len[b];
-  L = L < 0 ? 0 : (L > ca.Lmax ? ca.Lmax : L);
-  if ((kb + 1) * 64 > L) return;
-  const int g = ca.kvh_of_rho[rho];
-  const uint32_t* rows = reinterpret_cast<const uint32_t*>(
-      kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD) + lane;
+// Centroid of one full key block for one retrieval head, by one wave: the
+// mean of the block's 64 keys (summed key by key, two dims per lane), then
+// projected with P_k[rho] (equal to the mean of the projected keys by
+// linearity). rows: the block's first key row; mean: kD floats of LDS.
+__device__ __forceinline__ void block_centroid(const u16* rows_base,
+                                               const float* prow0, int r,
+                                               float* mean, float* out,
+                                               int lane) {
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(rows_base) + lane;
   float s0 = 0.f, s1 = 0.f;
   for (int i = 0; i < 64; ++i) {
     const uint32_t w = rows[(size_t)i * (kD / 2)];
@@ -50,12 +46,94 @@ __global__ __launch_bounds__(64) void build_centroids_kernel(
   mean[2 * lane] = s0 * (1.f / 64.f);
   mean[2 * lane + 1] = s1 * (1.f / 64.f);
   __syncthreads();
-  for (int rr = lane; rr < ca.r; rr += 64) {
-    const float* prow = p_k + ((size_t)rho * ca.r + rr) * kD;
+  for (int rr = lane; rr < r; rr += 64) {
+    const float* prow = prow0 + (size_t)rr * kD;
     float acc = 0.f;
     for (int d = 0; d < kD; ++d) acc = fmaf(prow[d], mean[d], acc);
-    cent[(((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r + rr] = acc;
+    out[rr] = acc;
   }
+  __syncthreads();  // mean may be reused
+}
+
+// grid (nbmax, n_ret, B), one wave. Full blocks only.
+__global__ __launch_bounds__(64) void build_centroids_kernel(
+    const u16* __restrict__ kc, const int32_t* __restrict__ cache_len,
+    const float* __restrict__ p_k, const CentArgs ca, float* __restrict__ cent) {
+  __shared__ float mean[kD];
+  const int kb = blockIdx.x, rho = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  int L = cache_len[b];
+  L = L < 0 ? 0 : (L > ca.Lmax ? ca.Lmax : L);
+  if ((kb + 1) * 64 > L) return;
+  const int g = ca.kvh_of_rho[rho];
+  block_centroid(kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD,
+                 p_k + (size_t)rho * ca.r * kD, ca.r, mean,
+                 cent + (((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r,
+                 lane);
+}
+
+// ------------------------------------------------------------- cache append
+// grid (B, Hkv), one wave: k_new / v_new row of (b, g) -> position
+// cache_len[b] of the cache (full caches are left unchanged).
+__global__ __launch_bounds__(64) void append_kv_kernel(
+    u16* __restrict__ kc, u16* __restrict__ vc,
+    const int32_t* __restrict__ cache_len, const u16* __restrict__ k_new,
+    const u16* __restrict__ v_new, int Hkv, int Lmax) {
+  const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
+  const int L = cache_len[b];
+  if (L < 0 || L >= Lmax) return;
+  const size_t src = ((size_t)b * Hkv + g) * kD;
+  const size_t dst = (((size_t)b * Hkv + g) * Lmax + L) * kD;
+  reinterpret_cast<uint32_t*>(kc + dst)[lane] =
+      reinterpret_cast<const uint32_t*>(k_new + src)[lane];
+  reinterpret_cast<uint32_t*>(vc + dst)[lane] =
+      reinterpret_cast<const uint32_t*>(v_new + src)[lane];
+}
+
+// grid (B), one wave: when the appended token completes a block, that
+// block's centroid for every retrieval head; then cache_len[b] += 1.
+__global__ __launch_bounds__(64) void append_centroids_kernel(
+    const u16* __restrict__ kc, int32_t* __restrict__ cache_len,
+    const float* __restrict__ p_k, const CentArgs ca, float* __restrict__ cent) {
+  __shared__ float mean[kD];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int L = cache_len[b];  // before the append
+  if (L < 0 || L >= ca.Lmax) return;
+  if ((L + 1) % 64 == 0) {
+    const int kb = L / 64;
+    for (int rho = 0; rho < ca.n_ret; ++rho) {
+      const int g = ca.kvh_of_rho[rho];
+      block_centroid(
+          kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD,
+          p_k + (size_t)rho * ca.r * kD, ca.r, mean,
+          cent + (((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r, lane);
+    }
+  }
+  if (lane == 0) cache_len[b] = L + 1;
+}
+
+hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
+                                const u16* k_new, const u16* v_new,
+                                const float* p_k, float* cent, int B,
+                                int Lmax, int Hkv, int n_ret, int r, int G,
+                                const uint8_t* ret_heads, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  CentArgs ca;
+  ca.Hkv = Hkv;
+  ca.Lmax = Lmax;
+  ca.n_ret = n_ret;
+  ca.r = r;
+  ca.nbmax = Lmax / 64;
+  for (int i = 0; i < kMaxHeads; ++i)
+    ca.kvh_of_rho[i] = i < n_ret ? ret_heads[i] / G : 0;
+  prof_begin("append_kv", st);
+  hipLaunchKernelGGL(append_kv_kernel, dim3(B, Hkv), dim3(64), 0, st, kc, vc,
+                     cache_len, k_new, v_new, Hkv, Lmax);
+  prof_end(st);
+  prof_begin("append_centroids", st);
+  hipLaunchKernelGGL(append_centroids_kernel, dim3(B), dim3(64), 0, st, kc,
+                     cache_len, p_k, ca, cent);
+  prof_end(st);
+  return hipGetLastError();
 }
 
 hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,

@@ -132,6 +132,19 @@ def test_decode_and_centroid_validation():
     st = lib.rtp_build_centroids(P(1), P(1), 2, 4096, 2, 1, 128, mp, P(1), 16,
                                  48, P(1), None)
     assert st == -2
+    # append: retrieval head without p_k / centroids, bad d, bad block
+    st = lib.rtp_decode_append(P(1), P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                               128, mp, None, 16, 64, None, None)
+    assert st == -1
+    st = lib.rtp_decode_append(P(1), P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                               64, mp, P(1), 16, 64, P(1), None)
+    assert st == -2
+    st = lib.rtp_decode_append(P(1), P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                               128, mp, P(1), 16, 32, P(1), None)
+    assert st == -2
+    st = lib.rtp_decode_append(None, P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                               128, mp, P(1), 16, 64, P(1), None)
+    assert st == -1
 
 
 def test_binding_rejects_cpu_tensors():

@@ -139,3 +139,39 @@ def test_decode_equal_centroid_scores_keep_the_lowest_blocks(gpu_lib):
         want = [0] + list(range(1, 65)) + [n_b - 2, n_b - 1]
         got = [int(v) for v in sel[b, 0] if v >= 0]
         assert got == want, (b, got[:5], got[-5:])
+
+
+def test_decode_append_matches_rebuild_and_oracle(gpu_lib):
+    # Ragged caches, two of them one token short of a full block and one
+    # already full. After an append the new rows sit at the old lengths,
+    # cache_len grows by one (the full cache is left unchanged), the blocks
+    # the token completed get centroids bitwise equal to a full rebuild, and
+    # a decode step on the grown cache matches the oracle.
+    Lmax = 64 * 40
+    lens = [63, 64 * 7 + 63, 100, 64 * 12, Lmax]
+    y = make_decode(_wl(len(lens), Lmax, Hq=8, Hkv=2, ret=(1, 6), window=200,
+                        top_k=5), cache_len=lens, Lmax=Lmax)
+    dev = "cuda"
+    kc, vc = y["k_cache"].to(dev), y["v_cache"].to(dev)
+    cl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    cent = gpu_lib.build_centroids(kc, cl, y["is_retrieval"], pk)
+    gen = torch.Generator().manual_seed(5)
+    kn = torch.randn(len(lens), 2, 128, generator=gen).to(torch.bfloat16).to(dev)
+    vn = torch.randn(len(lens), 2, 128, generator=gen).to(torch.bfloat16).to(dev)
+    k_before = kc.clone()
+    gpu_lib.decode_append(kc, vc, cl, kn, vn, y["is_retrieval"], pk, cent)
+    torch.cuda.synchronize()
+    grown = [L + 1 if L < Lmax else L for L in lens]
+    assert cl.cpu().tolist() == grown
+    for b, L in enumerate(lens):
+        if L < Lmax:
+            assert torch.equal(kc[b, :, L], kn[b]) and torch.equal(vc[b, :, L], vn[b])
+        else:
+            assert torch.equal(kc[b], k_before[b])
+    rebuilt = gpu_lib.build_centroids(kc, cl, y["is_retrieval"], pk)
+    torch.cuda.synchronize()
+    assert torch.equal(cent, rebuilt)
+    y2 = dict(y, k_cache=kc.cpu(), v_cache=vc.cpu(),
+              cache_len=np.array(grown, dtype=np.int32))
+    check(gpu_lib, y2, "after append")
