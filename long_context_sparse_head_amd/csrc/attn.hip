@@ -33,9 +33,8 @@
 //
 // Window kernel: 4 waves = 4 (head, query block) jobs of one KV group share
 // one stream of 64-key tiles, staged by direct global->LDS loads
-// (global_load_lds_dwordx4) into a 3-deep LDS ring with an XOR swizzle.
-// Workgroups are interleaved over KV groups, so with round-robin placement
-// each XCD serves one KV group from its own L2.
+// (global_load_lds_dwordx4) into a 3-deep LDS ring of padded rows. Each XCD
+// takes a contiguous, equal share of all KV groups' work items.
 //
 // Sparse kernel: each wave runs its own (retrieval head, query block) job over
 // its block list in 32-key half tiles: K goes straight into registers in MFMA
@@ -249,12 +248,24 @@ constexpr int DMA_PER_WAVE = (K_DMA + V_DMA + 3) / 4;  // 9
 static_assert(K_DMA == 17 && V_DMA == 18 && DMA_PER_WAVE == 9,
               "win_issue deals the loads for this split");
 
+// Workgroups are dealt round-robin to the chip's 8 XCDs (each with its own
+// L2). The work items of all KV groups are laid end to end and cut into 8
+// contiguous ranges of equal estimated cost (tiles walked plus a per-item
+// constant); XCD x runs range x. So the XCDs stay balanced when KV groups
+// have different numbers of window heads or items differ in length (causal
+// dense), and each XCD's concurrent workgroups cover neighbouring query
+// blocks of one group.
+constexpr int kXcds = 8;
+
 struct WinParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
   int S, S_pad, n_b, Hkv, window;
   float c;
+  int per_xcd, n_items;
+  int32_t xcd_begin[kXcds + 1];     // item range of each XCD
   uint8_t hlist[kMaxHeads];   // window heads grouped by KV head
   int16_t hoff[kMaxHeads + 1];
+  int32_t item_off[kMaxHeads + 1];  // first work item of each KV group
 };
 
 // The 35 DMA loads of a tile (17 K, 18 V^T) are dealt round-robin to the 4
@@ -555,8 +566,12 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   __shared__ int over_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = blockIdx.x % p.Hkv;
-  const int ig = blockIdx.x / p.Hkv;
+  const int xcd = blockIdx.x % kXcds;
+  const int item = p.xcd_begin[xcd] + blockIdx.x / kXcds;
+  if (item >= p.xcd_begin[xcd + 1]) return;  // whole workgroup
+  int g = 0;
+  while (item >= p.item_off[g + 1]) ++g;
+  const int ig = item - p.item_off[g];
   const int h0 = p.hoff[g], nsw = p.hoff[g + 1] - h0;
   const int njobs = nsw * p.n_b;
   if (nsw == 0 || 4 * ig >= njobs) return;  // whole workgroup
@@ -959,23 +974,58 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
   wp.S = a.S; wp.S_pad = a.S_pad; wp.n_b = a.n_b; wp.Hkv = a.Hkv;
   wp.window = a.window;
   wp.c = c;
-  int nl = 0, max_items = 0;
+  int nl = 0, n_items = 0;
   for (int g = 0; g < a.Hkv; ++g) {
     wp.hoff[g] = (int16_t)nl;
+    wp.item_off[g] = n_items;
     int cnt = 0;
     for (int h = g * a.G; h < (g + 1) * a.G; ++h)
       if (!(is_ret && is_ret[h])) {
         wp.hlist[nl++] = (uint8_t)h;
         ++cnt;
       }
-    max_items = max(max_items, (cnt * a.n_b + 3) / 4);
+    n_items += (cnt * a.n_b + 3) / 4;
   }
   wp.hoff[a.Hkv] = (int16_t)nl;
+  wp.item_off[a.Hkv] = n_items;
   for (int i = nl; i < kMaxHeads; ++i) wp.hlist[i] = 0;
+  wp.n_items = n_items;
+  // cost-balanced contiguous item ranges per XCD (the tile count of an item
+  // follows the kernel's own range computation)
+  {
+    const int w = a.window;
+    auto item_cost = [&](int g, int ig) -> int64_t {
+      const int nsw = wp.hoff[g + 1] - wp.hoff[g];
+      const int njobs = nsw * a.n_b;
+      const int qb_hi = a.n_b - 1 - (4 * ig) / nsw;
+      const int qb_lo = a.n_b - 1 - min(4 * ig + 3, njobs - 1) / nsw;
+      const int64_t lo = (int64_t)qb_lo * 64 - w + 1;
+      const int64_t kt_lo = lo > 0 ? (lo >> 6) : 0;
+      return (qb_hi - kt_lo + 1) + 9;  // + per-item prologue/epilogue
+    };
+    int64_t total = 0;
+    for (int g = 0; g < a.Hkv; ++g)
+      for (int ig = 0; ig < wp.item_off[g + 1] - wp.item_off[g]; ++ig)
+        total += item_cost(g, ig);
+    int x = 0, item = 0;
+    int64_t run = 0;
+    wp.xcd_begin[0] = 0;
+    for (int g = 0; g < a.Hkv; ++g)
+      for (int ig = 0; ig < wp.item_off[g + 1] - wp.item_off[g]; ++ig, ++item) {
+        run += item_cost(g, ig);
+        while (x + 1 < kXcds && run * kXcds >= total * (x + 1))
+          wp.xcd_begin[++x] = item + 1;
+      }
+    while (x < kXcds) wp.xcd_begin[++x] = n_items;
+    int longest = 0;
+    for (int i = 0; i < kXcds; ++i)
+      longest = max(longest, wp.xcd_begin[i + 1] - wp.xcd_begin[i]);
+    wp.per_xcd = longest;
+  }
   if (nl > 0) {
     prof_begin("attn_window", st);
-    hipLaunchKernelGGL(attn_window_kernel, dim3(max_items * a.Hkv), dim3(256), 0,
-                       st, wp);
+    hipLaunchKernelGGL(attn_window_kernel, dim3(wp.per_xcd * kXcds), dim3(256),
+                       0, st, wp);
     prof_end(st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
