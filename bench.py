@@ -43,9 +43,9 @@ METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA p
 TRAFFIC = {
     "kernel": "attn_window_kernel",
     "source": "long_context_sparse_head_amd/csrc/attn.hip",
-    "sha256": "b8dfb0fea692fcfc6d4a4a8700085b2348cbb0dbb07b6aad2ac0cd243a93a809",
-    "fetch_bytes": 3158317638,
-    "write_bytes": 905969811,
+    "sha256": "f0bb8610ec43d1c545a9262ec8298c8ab59d8015605fb912e36c97f627f1172b",
+    "fetch_bytes": 2935032827,
+    "write_bytes": 906010592,
 }
 
 
