@@ -706,6 +706,11 @@ struct SparseParams {
   const int32_t* sel; const int32_t* sel_cnt;
   int sel_stride, S, S_pad, n_b, G, n_ret, n_jobs;
   float c;
+  // Retrieval heads are numbered in ascending head order, so those of one KV
+  // group are consecutive: group slot i holds rho in [rho_begin[i],
+  // rho_begin[i+1]) (only groups with retrieval heads get a slot).
+  int n_grp;
+  int16_t rho_begin[kMaxHeads + 1];
   uint8_t head_of_rho[kMaxHeads];
 };
 
@@ -776,8 +781,16 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int job = 4 * blockIdx.x + wave;
   if (job >= p.n_jobs) return;  // waves are independent: no block barriers
-  const int rho = job % p.n_ret;
-  const int qb = p.n_b - 1 - job / p.n_ret;
+  // Jobs run KV-group by KV-group (query blocks descending, the group's
+  // heads interleaved), so the jobs in flight gather from one group's K/V
+  // and share its frequently chosen blocks (sink, recent and strongly
+  // scored ones) in L2.
+  int gs = 0;
+  while (job >= p.n_b * p.rho_begin[gs + 1]) ++gs;
+  const int r0 = p.rho_begin[gs], nr = p.rho_begin[gs + 1] - r0;
+  const int jj = job - p.n_b * r0;
+  const int rho = r0 + jj % nr;
+  const int qb = p.n_b - 1 - jj / nr;
   const int head = p.head_of_rho[rho];
   const int g = head / p.G;
   const int q0 = qb * 64;
@@ -1037,6 +1050,11 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
     if (is_ret && is_ret[h]) sp.head_of_rho[n_ret++] = (uint8_t)h;
   if (n_ret == 0) return hipSuccess;
   for (int i = n_ret; i < kMaxHeads; ++i) sp.head_of_rho[i] = 0;
+  sp.n_grp = 0;
+  for (int rho = 0; rho < n_ret; ++rho)
+    if (rho == 0 || sp.head_of_rho[rho] / a.G != sp.head_of_rho[rho - 1] / a.G)
+      sp.rho_begin[sp.n_grp++] = (int16_t)rho;
+  for (int i = sp.n_grp; i <= kMaxHeads; ++i) sp.rho_begin[i] = (int16_t)n_ret;
   sp.q = a.q; sp.k = a.k; sp.vt = a.vt; sp.out = a.out; sp.lse = a.lse;
   sp.sel = a.sel; sp.sel_cnt = a.sel_cnt; sp.sel_stride = a.sel_stride;
   sp.S = a.S; sp.S_pad = a.S_pad; sp.n_b = a.n_b; sp.G = a.G;
