@@ -39,6 +39,8 @@
  *    stream). The library allocates no device memory: scratch space comes
  *    from the caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned),
  *    sized by the matching *_workspace_bytes query. Calls never synchronise.
+ *    (rtp_hybrid_attn_decode also uses a library-owned auxiliary stream;
+ *    see there.)
  *  - Arguments are validated on the host before anything is enqueued. On an
  *    error nothing is launched, outputs are untouched, and a negative status
  *    is returned; rtp_last_error() gives a thread-local message.
@@ -223,6 +225,15 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
  *  out [B,Hq,d] bf16 (out); lse [B,Hq] fp32 (out, may be NULL);
  *  sel_out [B,n_ret,top_k+1+n_recent] int32 (out, may be NULL): kept blocks
  *  ascending, -1 padded.
+ *
+ *  Streams: when both kinds of head are present, the streaming-head
+ *  attention runs on an auxiliary stream that the library creates once per
+ *  device (default priority), concurrently with the block choice on
+ *  `stream`. Events order it after the work enqueued on `stream` before the
+ *  call, and the rest of the call after it, so the step as a whole is
+ *  ordered on `stream` like any other asynchronous call; the host never
+ *  waits. If the auxiliary stream cannot be created, everything runs on
+ *  `stream`.
  */
 int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* cache_len,

@@ -46,28 +46,6 @@
 
 namespace rtp {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
-// s_waitcnt vmcnt(8), other counters at their maximum (gfx9 encoding)
-__device__ __forceinline__ void wait_vm8() {
-  __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
-}
-
-// Row of a 32-key sub-tile that MFMA row m reads: swap bits 2 and 3. Then
-// accumulator element i of lane l of S^T holds key 16*(i/8) + 8*(l/32) + i%8
-// of the sub-tile, i.e. the 8 values a lane feeds to one P.V step are 8
-// consecutive keys.
-__device__ __forceinline__ int perm_row(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
 // ------------------------------------------------------------ softmax core
 // Base-2 softmax with a fixed reference per query: m is the max score of the
 // query's own diagonal key half block (computed before the main pass), and
@@ -79,7 +57,6 @@ __device__ __forceinline__ int perm_row(int r) {
 // with it (then p <= 1). The O accumulator is touched only by MFMAs, which
 // keeps it resident in AGPRs with no per-tile rescale. Row sums use the
 // bf16-rounded p that also feeds the P.V MFMA.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
 struct Soft {
@@ -100,10 +77,6 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NS][2], int j) {
 
 // p = exp2(c s - c m) packed to bf16 (the B operand of P.V); ls = sum of the
 // packed values of this lane.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 template <int NS>
 __device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2],

@@ -34,6 +34,37 @@ __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {  // RNE
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// LDS DMA: lane i's 16 bytes from g land at lds_base + 16 i.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
+// s_waitcnt vmcnt(N), other counters at their maximum (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vm8() { wait_vm<8>(); }
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));  // lgkmcnt(0)
+}
+
+// Row of a 32-key sub-tile that MFMA row m reads: swap bits 2 and 3. Then
+// accumulator element i of lane l of S^T holds key 16*(i/8) + 8*(l/32) + i%8
+// of the sub-tile, i.e. the 8 values a lane feeds to one P.V step are 8
+// consecutive keys.
+__device__ __forceinline__ int perm_row(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
 // Optional per-kernel timing (off unless rtp_profile(1) was called): HIP
 // events recorded on the launch stream right before and after a kernel.
 void prof_begin(const char* name, hipStream_t st);

@@ -18,6 +18,8 @@
 #include "common.h"
 #include "select.h"
 
+#include <mutex>
+
 namespace rtp {
 
 constexpr int kDecMaxUnitHeads = 8;
@@ -172,6 +174,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   __shared__ uint32_t keys[TK_LDS + TK_LDS / 32];
   __shared__ float qt[kD];
   __shared__ TopkShared sh;
+  __shared__ WaveTopkShared wsh;
   const int rho = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = cache_len[b];
   L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
@@ -186,48 +189,98 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   }
   const int h = a.head_of_rho[rho];
   const u16* qrow = q + ((size_t)b * a.Hq + h) * kD;
-  if (tid < a.r) {
-    const float* prow = p_q + ((size_t)rho * a.r + tid) * kD;
+  // q~ = P_q q: thread (j, c) takes d = 8c .. 8c+7 of row j, 16 lanes sum
+  // a row (r is a multiple of 16)
+  for (int j0 = 0; j0 < a.r; j0 += 16) {
+    const int j = j0 + (tid >> 4), c = tid & 15;
     float acc = 0.f;
-    for (int d = 0; d < kD; ++d) acc = fmaf(prow[d], bf2f(qrow[d]), acc);
-    qt[tid] = acc;
+    if (j < a.r) {
+      const float4* pp =
+          reinterpret_cast<const float4*>(p_q + ((size_t)rho * a.r + j) * kD + 8 * c);
+      const float4 p0 = pp[0], p1 = pp[1];
+      const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+      acc = p0.x * bf2f(qv.x & 0xffffu);
+      acc = fmaf(p0.y, bf2f(qv.x >> 16), acc);
+      acc = fmaf(p0.z, bf2f(qv.y & 0xffffu), acc);
+      acc = fmaf(p0.w, bf2f(qv.y >> 16), acc);
+      acc = fmaf(p1.x, bf2f(qv.z & 0xffffu), acc);
+      acc = fmaf(p1.y, bf2f(qv.z >> 16), acc);
+      acc = fmaf(p1.z, bf2f(qv.w & 0xffffu), acc);
+      acc = fmaf(p1.w, bf2f(qv.w >> 16), acc);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (c == 0 && j < a.r) qt[j] = acc;
   }
   __syncthreads();
   const float* cb = cent + row_id * a.nbmax * a.r;
   float* srow = cscores + row_id * a.nbmax;
   const bool in_lds = n_c <= TK_LDS;
-  // four candidates per thread in flight; each centroid row is r floats
-  // read as float4 (consecutive lanes read consecutive rows)
-  for (int e0 = tid; e0 < n_c; e0 += 4 * 256) {
-    float sc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int rr = 0; rr < a.r; rr += 4) {
-      float4 cv[4];
+  // Candidate scores, several candidates per thread in flight; a centroid
+  // row is r floats read as float4 (consecutive lanes read consecutive
+  // rows). For r = 16 every load of a group of candidates is issued before
+  // the first is used, so the row costs a few memory latencies, not one per
+  // float4.
+  auto put = [&](int e, float v) {
+    if (in_lds) keys[e + (e >> 5)] = order_key(v);
+    else srow[e] = v;
+  };
+  if (a.r == 16) {
+    constexpr int U = 8;
+    for (int e0 = tid; e0 < n_c; e0 += U * 256) {
+      float4 cv[U][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int e = min(e0 + 256 * u, n_c - 1);
-        cv[u] = *reinterpret_cast<const float4*>(cb + (size_t)(e + 1) * a.r + rr);
+        const float4* crow = reinterpret_cast<const float4*>(cb + (size_t)(e + 1) * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cv[u][i] = crow[i];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sc[u] = fmaf(qt[rr], cv[u].x, sc[u]);
-        sc[u] = fmaf(qt[rr + 1], cv[u].y, sc[u]);
-        sc[u] = fmaf(qt[rr + 2], cv[u].z, sc[u]);
-        sc[u] = fmaf(qt[rr + 3], cv[u].w, sc[u]);
+      for (int u = 0; u < U; ++u) {
+        float sc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sc = fmaf(qt[4 * i], cv[u][i].x, sc);
+          sc = fmaf(qt[4 * i + 1], cv[u][i].y, sc);
+          sc = fmaf(qt[4 * i + 2], cv[u][i].z, sc);
+          sc = fmaf(qt[4 * i + 3], cv[u][i].w, sc);
+        }
+        const int e = e0 + 256 * u;
+        if (e < n_c) put(e, sc);
       }
     }
+  } else {
+    for (int e0 = tid; e0 < n_c; e0 += 4 * 256) {
+      float sc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < a.r; rr += 4) {
+        float4 cv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + 256 * u;
-      if (e >= n_c) break;
-      if (in_lds) keys[e + (e >> 5)] = order_key(sc[u]);
-      else srow[e] = sc[u];
+        for (int u = 0; u < 4; ++u) {
+          const int e = min(e0 + 256 * u, n_c - 1);
+          cv[u] = *reinterpret_cast<const float4*>(cb + (size_t)(e + 1) * a.r + rr);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          sc[u] = fmaf(qt[rr], cv[u].x, sc[u]);
+          sc[u] = fmaf(qt[rr + 1], cv[u].y, sc[u]);
+          sc[u] = fmaf(qt[rr + 2], cv[u].z, sc[u]);
+          sc[u] = fmaf(qt[rr + 3], cv[u].w, sc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < n_c) put(e, sc[u]);
+      }
     }
   }
   __syncthreads();
   auto getk = [&](int e) -> uint32_t {
     return in_lds ? keys[e + (e >> 5)] : order_key(srow[e]);
   };
-  radix_topk(getk, n_c, a.top_k, out + 1, 1, sh);
+  if (a.top_k > kWaveTopkMax) radix_topk(getk, n_c, a.top_k, out + 1, 1, sh);
+  else if (a.top_k > 0) wave_topk(getk, n_c, a.top_k, out + 1, 1, wsh);
   const int n_rec = n_b - 1 - n_c;  // = n_recent here
   if (tid == 0) {
     out[0] = 0;
@@ -242,6 +295,7 @@ struct DecAttnArgs {
   const int32_t* sel; const int32_t* sel_cnt;
   float* part_o; float* part_ml;
   int Hq, Hkv, Lmax, n_ret, window, n_split, sel_width, n_units;
+  int unit_base;  // the launch covers units unit_base .. unit_base + gridDim.y - 1
   float c;  // scale * log2(e)
   // unit u: bits 0-1 kind (0 window heads of one KV group, 1 retrieval
   // head), bits 8-15 KV head, bits 16-23 head count, bits 24-31 first index
@@ -251,16 +305,33 @@ struct DecAttnArgs {
   uint8_t hlist[kMaxHeads];
 };
 
+// K and V tiles of 32 keys in a wave's LDS, 256 B per key row in 16 chunks
+// of 16 B. Both come from global memory in whole rows (load ins, 0..7, covers
+// rows 4 ins .. 4 ins + 3: lane i takes position i & 15 of row 4 ins + i / 16,
+// so each load and each LDS write is 1 KiB contiguous) and are stored
+// swizzled so the MFMA operand reads hit distinct banks:
+//  K: position p of row r holds d-chunk p ^ (r & 15) (an operand read takes
+//     one chunk of 16 consecutive rows);
+//  V: position p of row r holds d-chunk p ^ (4 ((r >> 3) & 1)) (a P.V operand
+//     read takes one d of rows 8 apart).
+constexpr int kDecTile = 32 * kD * 2;
+
 // grid (n_split, n_units, B), 256 threads. Each wave takes 32-key tiles in
-// turn, independently of the other waves until the final merge; S^T = K Q^T
-// on MFMA (heads along N), P.V on the vector ALU.
-__global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) float Pw[4][32][kDecMaxUnitHeads];
-  __shared__ __attribute__((aligned(16))) float alw[4][kDecMaxUnitHeads];
-  __shared__ float red_o[4][kDecMaxUnitHeads][kD];
+// turn (tiles wave, wave + 4, ...), independently of the other waves until
+// the final merge. Both products run on MFMA with the unit's heads along N
+// (so up to 8 heads share every K/V byte): S^T = K Q^T with K rows read in
+// perm_row order, which makes the accumulator of S^T the B operand of
+// O^T += V^T P; that product wants 8 consecutive keys of one d per lane, so V
+// is read transposed from LDS. The next tile's K and V are loaded into
+// registers (a whole iteration ahead) and written to LDS at the start of
+// the next iteration; plain loads, not LDS DMA, keep the compiler's wait
+// counts exact.
+__global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kvbuf[4][2][kDecTile];
   __shared__ float red_ml[4][kDecMaxUnitHeads][2];
-  const int s = blockIdx.x, u = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, u = a.unit_base + blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, n = lane & 31;
   const uint32_t desc = a.desc[u];
   const int kind = desc & 3, kvh = (desc >> 8) & 255, nh = (desc >> 16) & 255,
@@ -295,7 +366,7 @@ __global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
   const u16* kbase = a.kc + kv_off;
   const u16* vbase = a.vc + kv_off;
 
-  // B operand: Q^T, column n = head n of the unit (zero beyond nh)
+  // B operand of S^T: Q^T, column n = head n of the unit (zero beyond nh)
   bf16x8 qf[8];
   {
     const int h = n < nh ? a.hlist[first + n] : a.hlist[first];
@@ -308,16 +379,7 @@ __global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
     }
   }
 
-  float m_run = -1e30f, l_run = 0.f;  // softmax state of head n (lane pair)
-  // P.V: lane l accumulates d = 2l, 2l+1 of every head of the unit
-  float o[kDecMaxUnitHeads][2];
-#pragma unroll
-  for (int j = 0; j < kDecMaxUnitHeads; ++j) o[j][0] = o[j][1] = 0.f;
-
-  // Wave w takes tiles w, w + 4, ... Loads are issued for every iteration
-  // (an empty tile re-reads row 0), so each iteration has the same loads:
-  // the K rows of the next tile are fetched during this tile's P.V, the V
-  // rows of this tile during its QK and softmax.
+  // tile t: first key and number of keys (0: past this wave's work)
   auto tile_at = [&](int t, int& base, int& nvalid) {
     base = 0;
     nvalid = 0;
@@ -333,94 +395,159 @@ __global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
       }
     }
   };
-  auto load_k = [&](int base, int nvalid, bf16x8 (&kq)[8]) {
-    const int krow = n < nvalid ? base + n : base;
-    const u16* kp = kbase + (size_t)krow * kD + 8 * g;
+  // whole-row loads of one tile (K or V, by swizzle); rows past nvalid
+  // re-read the tile's first row (never NaN garbage: their P is exactly 0)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // Full tiles: one uniform tile address plus per-lane offsets (the
+  // swizzle of row 4 ins + lane / 16 repeats every 4 loads for K and every
+  // 2 for V, and each load is 1 KiB further on).
+  uint32_t koff[4], voff[2];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kq[ks] = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    koff[j] = (uint32_t)(r * 256 + (((lane & 15) ^ (r & 15)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    voff[j] = (uint32_t)((lane >> 4) * 256 + (((lane & 15) ^ (4 * j)) << 4));
+  auto load_rows = [&](const u16* src, int base, int nvalid, bool kswz,
+                       u32x4 (&st)[8]) {
+    if (nvalid == 32) {  // wave-uniform
+      const char* t = reinterpret_cast<const char*>(src + (size_t)base * kD);
+#pragma unroll
+      for (int ins = 0; ins < 8; ++ins) {
+        const uint32_t off = kswz ? koff[ins & 3] + (ins >> 2) * 4096
+                                  : voff[(ins >> 1) & 1] + (ins >> 1) * 2048 +
+                                        (ins & 1) * 1024;
+        st[ins] = *reinterpret_cast<const u32x4*>(t + off);
+      }
+    } else {
+#pragma unroll
+      for (int ins = 0; ins < 8; ++ins) {
+        const int r = 4 * ins + (lane >> 4);
+        const int chunk = (lane & 15) ^ (kswz ? (r & 15) : 4 * ((r >> 3) & 1));
+        const u16* p = src + (size_t)(r < nvalid ? base + r : base) * kD + chunk * 8;
+        st[ins] = *reinterpret_cast<const u32x4*>(p);
+      }
+    }
   };
+  char* const ktile = kvbuf[wave][0];
+  char* const vtile = kvbuf[wave][1];
+  auto store_rows = [&](char* tile, const u32x4 (&st)[8]) {
+#pragma unroll
+    for (int ins = 0; ins < 8; ++ins)
+      *reinterpret_cast<u32x4*>(tile + ins * 1024 + lane * 16) = st[ins];
+  };
+  // A operand of S^T, step ks: lane (g, n) holds K[perm_row(n)][16 ks + 8 g
+  // .. + 7]
+  auto k_frag = [&](int ks) {
+    const int r = perm_row(n);
+    return *reinterpret_cast<const bf16x8*>(ktile + r * 256 +
+                                            (((2 * ks + g) ^ (r & 15)) << 4));
+  };
+  // A operand of O^T += V^T P for keys 16 c .. 16 c + 15 and d 32 mt ..
+  // 32 mt + 31: lane (g, n) holds V[16 c + 8 g + e][32 mt + n], e = 0..7
+  auto v_frag = [&](const char* buf, int c, int mt) {
+    const int d = 32 * mt + n;
+    const char* p = buf + (16 * c + 8 * g) * 256 + (((d >> 3) ^ (4 * g)) << 4) +
+                    (d & 7) * 2;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)*reinterpret_cast<const u16*>(p + 2 * e * 256) |
+             ((uint32_t)*reinterpret_cast<const u16*>(p + (2 * e + 1) * 256) << 16);
+    return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  };
+
+  float m_run = -1e30f, l_run = 0.f;  // softmax state of head n (lane pair)
+  f32x16 o[4];  // O^T: element i of o[mt] is d = 32 mt + 8 (i/4) + 4 g + i%4
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) o[mt] = f32x16{};
+
   int base, nvalid;
   tile_at(wave, base, nvalid);
-  bf16x8 kq[8];
-  load_k(base, nvalid, kq);
+  u32x4 kst[8], vst[8];
+  load_rows(kbase, base, nvalid, true, kst);
+  load_rows(vbase, base, nvalid, false, vst);
   const int iters = (nt + 3) / 4;
   for (int it = 0; it < iters; ++it) {
-    uint32_t vr[32];  // V[row][2 lane, 2 lane + 1], rows past nvalid re-read
-#pragma unroll
-    for (int row = 0; row < 32; ++row) {
-      const int vrow = row < nvalid ? base + row : base;
-      vr[row] = *reinterpret_cast<const uint32_t*>(vbase + (size_t)vrow * kD +
-                                                   2 * lane);
-    }
-    const bool live = nvalid > 0;  // wave-uniform
-    if (live) {
-      f32x16 sacc = {};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(kq[ks], qf[ks], sacc);
-      // accumulator element i: key row 8*(i/4) + 4*g + i%4, head n
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * g + (i & 3);
-        if (row >= nvalid) sacc[i] = -INFINITY;
-        tmax = fmaxf(tmax, sacc[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = fast_exp2((m_run - m_new) * a.c);
-      m_run = m_new;
-      const float mc = m_new * a.c;
-      float ls = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * g + (i & 3);
-        const float pv = fast_exp2(fmaf(sacc[i], a.c, -mc));
-        ls += pv;
-        if (n < kDecMaxUnitHeads) Pw[wave][row][n] = pv;  // own slice only
-      }
-      l_run = l_run * alpha + ls;
-      if (g == 0 && n < kDecMaxUnitHeads) alw[wave][n] = alpha;
-    }
-    // next tile's K rows, in flight during this tile's P.V
+    // this tile to LDS (the previous tile's reads are done: a wave's LDS
+    // operations complete in order), then the next tile into the registers,
+    // in flight for the whole iteration. Past the wave's last tile the loads
+    // re-read one row (cache hits), so every iteration issues the same loads.
+    store_rows(ktile, kst);
+    store_rows(vtile, vst);
     int nbase, nnvalid;
     tile_at((it + 1) * 4 + wave, nbase, nnvalid);
-    load_k(nbase, nnvalid, kq);
-    if (live) {
-      const float4 al0 = *reinterpret_cast<const float4*>(&alw[wave][0]);
-      const float4 al1 = *reinterpret_cast<const float4*>(&alw[wave][4]);
-      const float al[8] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+    load_rows(kbase, nbase, nnvalid, true, kst);
+    load_rows(vbase, nbase, nnvalid, false, vst);
+    if (nvalid > 0) {  // wave-uniform
+      f32x16 sacc = {};
 #pragma unroll
-      for (int j = 0; j < kDecMaxUnitHeads; ++j) {
-        o[j][0] *= al[j];
-        o[j][1] *= al[j];
+      for (int ks = 0; ks < 8; ++ks) sacc = mfma32(k_frag(ks), qf[ks], sacc);
+      // element i: key 16 (i/8) + 8 g + i%8 of the tile, head n
+      if (nvalid < 32) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (16 * (i >> 3) + 8 * g + (i & 7) >= nvalid) sacc[i] = -INFINITY;
       }
+      float tmax = sacc[0];
 #pragma unroll
-      for (int row = 0; row < 32; ++row) {
-        if (row < nvalid) {  // wave-uniform
-          const float v0 = __uint_as_float(vr[row] << 16);
-          const float v1 = __uint_as_float(vr[row] & 0xffff0000u);
-          const float4 p0 = *reinterpret_cast<const float4*>(&Pw[wave][row][0]);
-          const float4 p1 = *reinterpret_cast<const float4*>(&Pw[wave][row][4]);
-          const float pj[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, sacc[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      if (__any(m_new > m_run)) {  // rescale only when some head's max rose
+        const float alpha = fast_exp2((m_run - m_new) * a.c);
+        l_run *= alpha;
 #pragma unroll
-          for (int j = 0; j < kDecMaxUnitHeads; ++j) {
-            o[j][0] = fmaf(pj[j], v0, o[j][0]);
-            o[j][1] = fmaf(pj[j], v1, o[j][1]);
-          }
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[mt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * a.c;
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      bf16x8 pb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 8 * c + 2 * e;
+          w[e] = pack_bf16x2(fast_exp2(fmaf(sacc[i], a.c, -mc)),
+                             fast_exp2(fmaf(sacc[i + 1], a.c, -mc)));
+          // l sums the rounded weights that P.V uses
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2, w[e]), one, l_run, false);
         }
+        pb[c] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          o[mt] = mfma32(v_frag(vtile, c, mt), pb[c], o[mt]);
     }
     base = nbase;
     nvalid = nnvalid;
   }
 
-  // wave-level totals: l over the lane pair
+  // wave-level totals: l over the lane pair; O^T columns of the unit's heads
+  // go to this wave's own (now idle) V tile
   l_run += __shfl_xor(l_run, 32);
+  float* const red_o = reinterpret_cast<float*>(ktile);  // [head][d]
+  if (n < nh) {
 #pragma unroll
-  for (int j = 0; j < kDecMaxUnitHeads; ++j) {
-    red_o[wave][j][2 * lane] = o[j][0];
-    red_o[wave][j][2 * lane + 1] = o[j][1];
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 w;
+        w.x = o[mt][4 * q + 0];
+        w.y = o[mt][4 * q + 1];
+        w.z = o[mt][4 * q + 2];
+        w.w = o[mt][4 * q + 3];
+        *reinterpret_cast<float4*>(red_o + n * kD + 32 * mt + 8 * q + 4 * g) = w;
+      }
   }
   if (g == 0 && n < kDecMaxUnitHeads) {
     red_ml[wave][n][0] = m_run;
@@ -435,7 +562,7 @@ __global__ __launch_bounds__(256, 3) void dec_attn_kernel(const DecAttnArgs a) {
     float acc = 0.f, lsum = 0.f;
     for (int w = 0; w < 4; ++w) {
       const float f = fast_exp2((red_ml[w][j][0] - M) * a.c);
-      acc += f * red_o[w][j][d];
+      acc += f * reinterpret_cast<const float*>(kvbuf[w][0])[j * kD + d];
       lsum += f * red_ml[w][j][1];
     }
     const int h = a.hlist[first + j];
@@ -468,28 +595,56 @@ __global__ __launch_bounds__(128) void dec_merge_kernel(
     lse[(size_t)b * Hq + h] = (M * c + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
+// Streaming-head attention needs no block choice, so it runs on a
+// library-owned auxiliary stream of the device, concurrently with the block
+// choice and the retrieval-head attention on the caller's stream. Events
+// order it after the caller's earlier work and the merge after it, so the
+// call keeps plain stream semantics (and no host synchronisation).
+namespace {
+struct AuxStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;
+AuxStream g_aux[kMaxDevices];
+
+// Creates the device's auxiliary stream on first use; nullptr if that is
+// impossible (the caller then runs everything on its own stream).
+AuxStream* aux_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream& x = g_aux[dev];
+  if (x.failed) return nullptr;
+  if (!x.s) {
+    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+      x.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  return &x;
+}
+}  // namespace
+
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
   const int nbmax = a.Lmax / 64;
   const int width = a.top_k + 1 + a.n_recent;
-  if (a.n_ret > 0) {
-    DecSelArgs sa;
-    sa.Hq = a.Hq;
-    sa.Lmax = a.Lmax;
-    sa.n_ret = a.n_ret;
-    sa.r = a.r;
-    sa.nbmax = nbmax;
-    sa.top_k = a.top_k;
-    sa.n_recent = a.n_recent;
-    sa.width = width;
-    for (int i = 0; i < kMaxHeads; ++i) sa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
-    prof_begin("dec_select", st);
-    hipLaunchKernelGGL(dec_select_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st,
-                       a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
-                       a.sel + (size_t)a.B * a.n_ret * width);
-    prof_end(st);
-  }
+  DecSelArgs sa;
+  sa.Hq = a.Hq;
+  sa.Lmax = a.Lmax;
+  sa.n_ret = a.n_ret;
+  sa.r = a.r;
+  sa.nbmax = nbmax;
+  sa.top_k = a.top_k;
+  sa.n_recent = a.n_recent;
+  sa.width = width;
+  for (int i = 0; i < kMaxHeads; ++i) sa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
   DecAttnArgs da;
   da.q = a.q;
   da.kc = a.kc;
@@ -507,6 +662,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   da.n_split = a.n_split;
   da.sel_width = width;
   da.c = a.scale * 1.4426950408889634f;
+  // units: window heads of each KV group (up to kDecMaxUnitHeads per unit)
+  // first, then one unit per retrieval head
   int nu = 0, nl = 0, rho = 0;
   for (int g = 0; g < a.Hkv; ++g) {
     int cnt = 0, start = nl;
@@ -525,6 +682,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
       da.rho[nu++] = 0;
     }
   }
+  const int n_win_units = nu;
   for (int h = 0; h < a.Hq; ++h) {
     if (!a.is_ret[h]) continue;
     da.hlist[nl] = (uint8_t)h;
@@ -533,9 +691,46 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     ++nl;
   }
   da.n_units = nu;
-  prof_begin("dec_attn", st);
-  hipLaunchKernelGGL(dec_attn_kernel, dim3(a.n_split, nu, a.B), dim3(256), 0, st, da);
-  prof_end(st);
+  const int n_ret_units = nu - n_win_units;
+
+  auto select = [&]() {
+    prof_begin("dec_select", st);
+    hipLaunchKernelGGL(dec_select_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st,
+                       a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
+                       a.sel + (size_t)a.B * a.n_ret * width);
+    prof_end(st);
+  };
+  auto attend = [&](const char* name, int base, int n, hipStream_t on) {
+    DecAttnArgs d = da;
+    d.unit_base = base;
+    prof_begin(name, on);
+    hipLaunchKernelGGL(dec_attn_kernel, dim3(a.n_split, n, a.B), dim3(256), 0, on, d);
+    prof_end(on);
+  };
+  hipError_t e = hipSuccess;
+  {
+    std::lock_guard<std::mutex> lk(g_aux_mu);
+    AuxStream* aux = n_win_units > 0 && n_ret_units > 0 ? aux_stream() : nullptr;
+    if (aux) {
+      e = hipEventRecord(aux->fork, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
+      if (e != hipSuccess) return e;
+      attend("dec_attn_window", 0, n_win_units, aux->s);
+      e = hipGetLastError();
+      if (e == hipSuccess) e = hipEventRecord(aux->join, aux->s);
+      if (e != hipSuccess) return e;
+      select();
+      attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
+      e = hipStreamWaitEvent(st, aux->join, 0);
+      if (e != hipSuccess) return e;
+    } else {
+      if (a.n_ret > 0) select();
+      if (n_win_units > 0) attend("dec_attn_window", 0, n_win_units, st);
+      if (n_ret_units > 0) attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   prof_begin("dec_merge", st);
   hipLaunchKernelGGL(dec_merge_kernel, dim3(a.Hq, a.B), dim3(kD), 0, st,
                      a.part_o, a.part_ml, a.Hq, a.n_split, da.c, a.out, a.lse);

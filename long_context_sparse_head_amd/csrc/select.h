@@ -234,4 +234,140 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
   return res;
 }
 
+// ------------------------------------------------- wave-synchronous top-k
+// For small k: each wave of the block selects in its own range with no block
+// barriers (a wave's LDS operations complete in order), then one wave
+// selects among the survivors. Used by the decode block choice (k <= 64).
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// The kk-th largest (1 <= kk <= m) of key(i), i < m, found by one wave: a
+// 4-pass, 8-bit radix select on a 256-bin histogram of its own.
+template <class Key>
+__device__ uint32_t wave_kth(Key key, int m, int kk, int* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane + 64 * j] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < m; i += 64) {
+      const uint32_t x = key(i);
+      if ((x & pmask) == prefix) atomicAdd(&hist[(x >> shift) & 255], 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane l covers bins 255 - 4l .. 252 - 4l, from the top
+    int h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = hist[255 - 4 * lane - j];
+      sum += h[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int incl = wave_incl_scan(sum);
+    const int excl = incl - sum;
+    const bool mine = excl < kk && kk <= incl;  // exactly one lane
+    int bin = 0, above = excl;
+    if (mine) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above + h[j] >= kk) {
+          bin = 255 - 4 * lane - j;
+          break;
+        }
+        above += h[j];
+      }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(mine));
+    bin = __shfl(bin, src);
+    above = __shfl(above, src);
+    prefix |= (uint32_t)bin << shift;
+    pmask |= 0xffu << shift;
+    kk -= above;
+  }
+  return prefix;
+}
+
+// Hands the k largest of key(i), i < m (1 <= k <= m; ties: lower i first)
+// to emit(p, i, key) with p = 0..k-1 in ascending i. One wave.
+template <class Key, class Emit>
+__device__ void wave_take(Key key, int m, int k, Emit emit, int* hist) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t T = wave_kth(key, m, k, hist);
+  int gt = 0;
+  for (int i = lane; i < m; i += 64) gt += key(i) > T;
+  gt = __shfl(wave_incl_scan(gt), 63);
+  const int take_eq = k - gt;  // keys equal to T to take, lowest i first
+  const uint64_t below = lanes_below();
+  int pos = 0, eq_seen = 0;
+  for (int i0 = 0; i0 < m; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t x = i < m ? key(i) : 0u;
+    const bool is_gt = i < m && x > T, is_eq = i < m && x == T;
+    const uint64_t beq = __ballot(is_eq);
+    const bool t =
+        is_gt || (is_eq && eq_seen + __builtin_popcountll(beq & below) < take_eq);
+    const uint64_t bt = __ballot(t);
+    if (t) emit(pos + __builtin_popcountll(bt & below), i, x);
+    pos += __builtin_popcountll(bt);
+    eq_seen += __builtin_popcountll(beq);
+  }
+}
+
+constexpr int kWaveTopkMax = 64;
+
+struct WaveTopkShared {
+  int hist[4][256];
+  uint32_t ckey[4 * kWaveTopkMax];
+  int cidx[4 * kWaveTopkMax];
+};
+
+// Requires 1 <= k <= kWaveTopkMax and k < n; 256 threads. Writes out[0..k)
+// = idx_base + chosen e, ascending (ties: lower e first). The four waves
+// take consecutive quarters of [0, n); every member of the final top k is
+// in its quarter's top k, and the survivors are stored in quarter order,
+// i.e. in ascending e, so the last selection keeps the tie order.
+template <class GetK>
+__device__ void wave_topk(GetK getk, int n, int k, int32_t* out, int idx_base,
+                          WaveTopkShared& sh) {
+  const int wave = threadIdx.x >> 6;
+  const int C = (n + 3) / 4;
+  auto kw_of = [&](int w) {
+    return min(k, max(0, min(n, (w + 1) * C) - w * C));
+  };
+  const int lo = min(wave * C, n), m = min(n, lo + C) - lo;
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += kw_of(w);
+  const int kw = kw_of(wave);
+  if (kw > 0)
+    wave_take([&](int i) { return getk(lo + i); }, m, kw,
+              [&](int p, int i, uint32_t x) {
+                sh.ckey[off + p] = x;
+                sh.cidx[off + p] = lo + i;
+              },
+              sh.hist[wave]);
+  __syncthreads();
+  if (wave == 0) {
+    const int M = kw_of(0) + kw_of(1) + kw_of(2) + kw_of(3);
+    wave_take([&](int i) { return sh.ckey[i]; }, M, k,
+              [&](int p, int i, uint32_t) { out[p] = idx_base + sh.cidx[i]; },
+              sh.hist[0]);
+  }
+  __syncthreads();
+}
+
 }  // namespace rtp

@@ -87,6 +87,16 @@ def test_decode_ragged_batch(gpu_lib):
     check(gpu_lib, y, "ragged")
 
 
+@pytest.mark.parametrize("top_k", [0, 1, 37, 64, 65])
+def test_decode_budgets_across_selection_paths(gpu_lib, top_k):
+    # budgets up to 64 use the per-wave selection, larger ones the block-wide
+    # radix select; 0 keeps only the sink and the recent blocks. The caches
+    # hold 300-odd candidates, ragged, so the four quarters differ in size.
+    y = make_decode(_wl(3, 64 * 300 + 17, Hq=8, Hkv=2, ret=(0, 5), window=256,
+                        top_k=top_k), cache_len=[64 * 300 + 17, 64 * 71, 64 * 67 + 1])
+    check(gpu_lib, y, f"budget{top_k}")
+
+
 def test_decode_short_caches_keep_every_block(gpu_lib):
     y = make_decode(_wl(4, 200, Hq=4, Hkv=1, ret=(0, 2), window=64, top_k=8),
                     cache_len=[1, 63, 64, 130])
@@ -114,6 +124,33 @@ def test_decode_many_heads_per_group(gpu_lib):
     y = make_decode(_wl(2, 3000, Hq=16, Hkv=1, ret=(3,), window=700,
                         top_k=4), cache_len=[3000, 1800])
     check(gpu_lib, y, "gqa16")
+
+
+def test_decode_runs_after_earlier_work_on_the_callers_stream(gpu_lib):
+    # Streaming heads run on a stream of the library's own; they must still
+    # see what the caller's stream wrote just before the call. V = 1 is made
+    # by a kernel on a side stream right before decoding on that stream, so
+    # every output is exactly 1 only if the whole step waited for it.
+    y = make_decode(_wl(4, 20000, Hq=8, Hkv=2, ret=(1, 6), window=4096,
+                        top_k=16), cache_len=[20000, 15000, 9000, 4097])
+    dev = "cuda"
+    kc = y["k_cache"].to(dev)
+    cl = torch.from_numpy(y["cache_len"]).to(dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    pq = torch.from_numpy(y["p_q"]).to(dev)
+    cent = gpu_lib.build_centroids(kc, cl, y["is_retrieval"], pk)
+    q = y["q"].to(dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            v1 = torch.empty_like(kc)
+            v1.copy_(kc).mul_(0).add_(1)
+            out = gpu_lib.hybrid_attn_decode(
+                q, kc, v1, cl, y["is_retrieval"], y["window"], pq, cent,
+                y["top_k"], n_recent=y["n_recent"])
+            ones = bool((out == 1).all().item())
+            assert ones, out.float().sub(1).abs().max().item()
 
 
 def test_decode_deterministic(gpu_lib):
