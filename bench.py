@@ -43,9 +43,9 @@ METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA p
 TRAFFIC = {
     "kernel": "attn_window_kernel",
     "source": "long_context_sparse_head_amd/csrc/attn.hip",
-    "sha256": "f0bb8610ec43d1c545a9262ec8298c8ab59d8015605fb912e36c97f627f1172b",
-    "fetch_bytes": 2935032827,
-    "write_bytes": 906010592,
+    "sha256": "63f328adc0651f28c74feb8710487508fd6b41b2c102ad70cc5df1e50c639575",
+    "fetch_bytes": 2934394379,
+    "write_bytes": 906019155,
 }
 
 
