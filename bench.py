@@ -95,7 +95,10 @@ def kernel_stats(records, steps):
 
 
 # ------------------------------------------------------------ GPU legs
-def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
+def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False):
+    """dense: every head causal-full (rtp_dense_attn_prefill); full:
+    retrieval heads causal-full, streaming heads windowed, with the decode
+    centroids as an epilogue (rtp_headwise_prefill, RTP_RETRIEVAL_FULL)."""
     from workloads import make_prefill
     dev = "cuda"
     t0 = time.time()
@@ -113,6 +116,17 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
                          device=dev)
         call = lambda: rtp.dense_attn_prefill(x["q"], x["k"], x["v"], ws=ws,
                                               out=out)
+    elif full:
+        wins = [w.window] * Hq
+        ws = torch.empty(rtp.headwise_prefill_workspace_bytes(
+            S, Hq, Hkv, x["is_retrieval"], "full", w.r, w.top_k),
+            dtype=torch.uint8, device=dev)
+
+        def call():
+            return rtp.headwise_prefill(
+                x["q"], x["k"], x["v"], x["is_retrieval"], wins, None, pk,
+                w.top_k, retrieval="full", r=w.r, want_centroids=True, ws=ws,
+                out=out)
     else:
         ws = torch.empty(rtp.prefill_workspace_bytes(S, Hq, Hkv,
                                                      x["is_retrieval"], w.r,
@@ -124,7 +138,8 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
                 x["q"], x["k"], x["v"], x["is_retrieval"], w.window, pq, pk,
                 w.top_k, r=w.r, ws=ws, out=out)
     torch.cuda.synchronize()
-    log(f"[bench] {w.name}{' dense' if dense else ''}: inputs ready in "
+    tag = ' dense' if dense else (' full-retrieval' if full else '')
+    log(f"[bench] {w.name}{tag}: inputs ready in "
         f"{time.time() - t0:.1f}s, workspace {ws.numel() / 2**30:.2f} GiB")
     for _ in range(warmup):
         call()
@@ -140,6 +155,13 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
     if dense:
         i = np.arange(S, dtype=np.int64)
         swa_pairs, ret_pairs = Hq * int((i + 1).sum()), 0
+    elif full:
+        # every head runs in the window kernel; retrieval heads causal-full
+        i = np.arange(S, dtype=np.int64)
+        swa_pairs, _ = prefill_pairs(S, Hq, x["is_retrieval"], w.window,
+                                     np.zeros((0, n_b), dtype=np.int32))
+        swa_pairs += n_ret * int((i + 1).sum())
+        ret_pairs = 0
     else:
         # the selection of one more call, for exact pair counts
         _, _, s2, c2 = rtp.hybrid_attn_prefill(
@@ -169,7 +191,7 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False):
         res["sparse_kernel_tflops"] = (4 * 128 * ret_pairs /
                                        (spa["ms_per_launch"] / 1e3) / 1e12)
     res["attn_frac_bf16_peak"] = res["attn_tflops"] / PEAK_BF16_TFLOPS
-    if not dense and n_ret:
+    if not dense and not full and n_ret:
         # indexer figures (algorithmic): scores are 2r flops per (query
         # block, candidate key); projections read K and Q once
         cand_keys = 64 * sum(max(q - 1, 0) for q in range(n_b))
@@ -349,7 +371,7 @@ def main():
                     help="time the 128K prefill only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense"],
+    ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense", "full"],
                     help="run only this secondary leg and print its detail "
                          "(for profiling); no bench line")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -374,9 +396,10 @@ def main():
                                args.warmup)
         else:
             w = {"1m": PREFILL_1M, "32k": PREFILL_32K,
-                 "dense": PREFILL_128K}[args.leg]
+                 "dense": PREFILL_128K, "full": PREFILL_128K}[args.leg]
             res = bench_prefill(rtp, torch, w, args.steps, args.warmup,
-                                dense=args.leg == "dense")
+                                dense=args.leg == "dense",
+                                full=args.leg == "full")
         print(json.dumps({"leg": args.leg, **res}), flush=True)
         return
     main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup)
@@ -402,6 +425,10 @@ def main():
             f"ms/step")
         extra["speedup_vs_dense_128k"] = (extra["dense_128k"]["ms_per_step"] /
                                           main["ms_per_step"])
+        extra["full_retrieval_128k"] = bench_prefill(
+            rtp, torch, PREFILL_128K, max(2, args.steps // 2), 1, full=True)
+        log(f"[bench] 128K with full retrieval heads: "
+            f"{extra['full_retrieval_128k']['ms_per_step']:.2f} ms/step")
     if args.copy_probe_gib > 0:
         n = int(args.copy_probe_gib * 2**30)
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

@@ -146,6 +146,52 @@ int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
                             int32_t* sel_count_out, void* ws, size_t ws_bytes,
                             rtp_stream_t stream);
 
+/* Retrieval-head modes of rtp_headwise_prefill. */
+#define RTP_RETRIEVAL_SPARSE 0  /* indexer selection + exact attention on it */
+#define RTP_RETRIEVAL_FULL 1    /* causal full attention */
+
+/* Workspace bytes for rtp_headwise_prefill (0 on invalid arguments). In
+ * RTP_RETRIEVAL_FULL mode no selection workspace is needed. */
+size_t rtp_headwise_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
+                                            const uint8_t* is_retrieval,
+                                            int retrieval, int r, int block,
+                                            int top_k);
+
+/*
+ * rtp_headwise_prefill - rtp_hybrid_attn_prefill with a window per head, a
+ * per-call choice of how retrieval heads attend, and the decode centroids
+ * as an epilogue. This follows the RTPurboV2 article's paragraph on the
+ * Qwen3-Coder-30B-A3B deployment: retrieval heads use full attention in
+ * prefill together with K-cache clustering and run sparse only in decode;
+ * streaming heads use SWA with windows that may differ (8192 for some).
+ *
+ *  windows [Hq] int32, HOST (each >= 1): streaming head h attends keys
+ *        i - windows[h] < j <= i (windows[h] >= S: causal full attention).
+ *        Entries of retrieval heads are not used.
+ *  retrieval  RTP_RETRIEVAL_SPARSE: retrieval heads select blocks as in
+ *        rtp_hybrid_attn_prefill (p_q, p_k, top_k, sel_in/sel_count_in and
+ *        sel_out/sel_count_out as there);
+ *        RTP_RETRIEVAL_FULL: retrieval heads attend every key j <= i;
+ *        p_q and top_k are not used and sel_in/sel_out must be NULL.
+ *  centroids [n_ret,n_b,r] fp32 (out, may be NULL): per-block mean of the
+ *        projected keys P_k k_j of each retrieval head (as in
+ *        rtp_indexer_select; a ragged last block averages its tokens). For a
+ *        decode cache holding this sequence, the full blocks' rows equal
+ *        what rtp_build_centroids computes, up to fp32 rounding. Needs p_k.
+ *  Other arguments as in rtp_hybrid_attn_prefill; ws is sized by
+ *  rtp_headwise_prefill_workspace_bytes. A NULL `windows` or an unknown
+ *  mode is RTP_EINVAL.
+ */
+int rtp_headwise_prefill(const void* q, const void* k, const void* v, int S,
+                         int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                         const int32_t* windows, int retrieval,
+                         const float* p_q, const float* p_k, int r, int block,
+                         int top_k, float scale, const int32_t* sel_in,
+                         const int32_t* sel_count_in, void* out, float* lse,
+                         int32_t* sel_out, int32_t* sel_count_out,
+                         float* centroids, void* ws, size_t ws_bytes,
+                         rtp_stream_t stream);
+
 /* Workspace bytes for rtp_dense_attn_prefill. */
 size_t rtp_dense_workspace_bytes(int S, int Hq, int Hkv, int d);
 

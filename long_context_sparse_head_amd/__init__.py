@@ -22,8 +22,10 @@ import torch
 
 __all__ = [
     "load", "LIB_PATH", "RtpError", "prefill_workspace_bytes",
+    "headwise_prefill_workspace_bytes",
     "dense_workspace_bytes", "decode_workspace_bytes", "indexer_select",
-    "hybrid_attn_prefill", "dense_attn_prefill", "build_centroids",
+    "hybrid_attn_prefill", "headwise_prefill", "dense_attn_prefill",
+    "build_centroids",
     "hybrid_attn_decode", "decode_append", "version", "KernelTimer",
 ]
 
@@ -36,6 +38,7 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _Z = ctypes.c_size_t
 _U8P = ctypes.POINTER(ctypes.c_uint8)
+_I32P = ctypes.POINTER(ctypes.c_int32)
 
 _SIGS = {
     "rtp_status_string": (ctypes.c_char_p, [_I]),
@@ -55,6 +58,11 @@ _SIGS = {
                                      _P, _P, _Z, _P]),
     "rtp_dense_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _F, _P, _P,
                                     _P, _Z, _P]),
+    "rtp_headwise_prefill_workspace_bytes": (_Z, [_I, _I, _I, _I, _U8P, _I,
+                                                  _I, _I, _I]),
+    "rtp_headwise_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _U8P, _I32P, _I,
+                                  _P, _P, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _Z, _P]),
     "rtp_build_centroids": (_I, [_P, _P, _I, _I, _I, _I, _I, _U8P, _P, _I, _I,
                                  _P, _P]),
     "rtp_decode_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _U8P,
@@ -187,6 +195,15 @@ def prefill_workspace_bytes(S: int, Hq: int, Hkv: int, is_retrieval,
                                                   top_k))
 
 
+def headwise_prefill_workspace_bytes(S: int, Hq: int, Hkv: int, is_retrieval,
+                                     retrieval: str = "sparse", r: int = 16,
+                                     top_k: int = 64, d: int = 128,
+                                     block: int = 64) -> int:
+    m, mp = _mask(is_retrieval, Hq)
+    return int(load().rtp_headwise_prefill_workspace_bytes(
+        S, Hq, Hkv, d, mp, RETRIEVAL_MODES[retrieval], r, block, top_k))
+
+
 def dense_workspace_bytes(S: int, Hq: int, Hkv: int, d: int = 128) -> int:
     return int(load().rtp_dense_workspace_bytes(S, Hq, Hkv, d))
 
@@ -279,6 +296,68 @@ def hybrid_attn_prefill(q, k, v, is_retrieval, window: int, p_q, p_k,
         _stream(dev)), "rtp_hybrid_attn_prefill")
     if want_lse or want_sel:
         return out, lse, so, co
+    return out
+
+
+RETRIEVAL_MODES = {"sparse": 0, "full": 1}
+
+
+def headwise_prefill(q, k, v, is_retrieval, windows, p_q, p_k, top_k: int,
+                     retrieval: str = "sparse", r: int = 16, block: int = 64,
+                     scale: float = 0.0, sel=None, sel_count=None,
+                     want_lse: bool = False, want_sel: bool = False,
+                     want_centroids: bool = False, ws=None, out=None):
+    """Prefill with a window per head (host int sequence of length Hq) and
+    retrieval heads either "sparse" (indexer selection) or "full" (causal
+    full attention). Returns out, or a tuple (out, lse, sel, sel_count,
+    centroids) with None for the parts not asked for."""
+    lib = load()
+    Hq, S, d = q.shape
+    Hkv = k.shape[0]
+    _dev(q, torch.bfloat16, "q", (Hq, S, d))
+    _dev(k, torch.bfloat16, "k", (Hkv, S, d))
+    _dev(v, torch.bfloat16, "v", (Hkv, S, d))
+    if retrieval not in RETRIEVAL_MODES:
+        raise ValueError(f"retrieval must be one of {sorted(RETRIEVAL_MODES)}")
+    mode = RETRIEVAL_MODES[retrieval]
+    m, mp = _mask(is_retrieval, Hq)
+    win = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
+    if win.shape != (Hq,):
+        raise ValueError(f"windows must have {Hq} entries")
+    wp = win.ctypes.data_as(_I32P)
+    n_ret = int(m.astype(bool).sum())
+    n_b = -(-S // block)
+    dev = q.device
+    if sel is not None:
+        _dev(sel, torch.int32, "sel", (n_ret, n_b, top_k + 2))
+        _dev(sel_count, torch.int32, "sel_count", (n_ret, n_b))
+    elif mode == 0:
+        _proj(p_q, n_ret, r, d, "p_q")
+    if (mode == 0 and sel is None) or want_centroids:
+        _proj(p_k, n_ret, r, d, "p_k")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev(out, torch.bfloat16, "out", (Hq, S, d))
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    so = co = None
+    if want_sel:
+        so = torch.full((n_ret, n_b, top_k + 2), -1, dtype=torch.int32,
+                        device=dev)
+        co = torch.zeros((n_ret, n_b), dtype=torch.int32, device=dev)
+    cent = torch.zeros((n_ret, n_b, r), dtype=torch.float32, device=dev) \
+        if want_centroids else None
+    nb = lib.rtp_headwise_prefill_workspace_bytes(S, Hq, Hkv, d, mp, mode, r,
+                                                  block, top_k)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_headwise_prefill(
+        _ptr(q), _ptr(k), _ptr(v), S, Hq, Hkv, d, mp, wp, mode, _ptr(p_q),
+        _ptr(p_k), r, block, top_k, float(scale), _ptr(sel), _ptr(sel_count),
+        _ptr(out), _ptr(lse), _ptr(so), _ptr(co), _ptr(cent), _ptr(w),
+        w.numel(), _stream(dev)), "rtp_headwise_prefill")
+    if want_lse or want_sel or want_centroids:
+        return out, lse, so, co, cent
     return out
 
 

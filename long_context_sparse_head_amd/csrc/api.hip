@@ -61,7 +61,9 @@ struct PrefillLayout {
   size_t vt, khi, klo, qhi, qlo, sc, sel, cnt, total;
 };
 
-PrefillLayout prefill_layout(int S, int Hkv, int n_ret, int r, int top_k) {
+// n_sel: retrieval heads that select (0 when none runs the indexer)
+PrefillLayout prefill_layout(int S, int Hkv, int n_ret, int r, int top_k,
+                             int n_sel) {
   using rtp::align256;
   const size_t n_b = (size_t)(S + 63) / 64, S_pad = n_b * 64;
   PrefillLayout L;
@@ -69,11 +71,11 @@ PrefillLayout prefill_layout(int S, int Hkv, int n_ret, int r, int top_k) {
   L.vt = off;  off += align256((size_t)Hkv * rtp::kD * S_pad * 2);
   L.khi = off; off += align256((size_t)n_ret * S_pad * r * 2);
   L.klo = off; off += align256((size_t)n_ret * S_pad * r * 2);
-  L.qhi = off; off += align256((size_t)n_ret * n_b * r * 2);
-  L.qlo = off; off += align256((size_t)n_ret * n_b * r * 2);
-  L.sc = off;  off += align256((size_t)n_ret * rtp::tri_rows((int64_t)n_b) * 4);
-  L.sel = off; off += align256((size_t)n_ret * n_b * (top_k + 2) * 4);
-  L.cnt = off; off += align256((size_t)n_ret * n_b * 4);
+  L.qhi = off; off += align256((size_t)n_sel * n_b * r * 2);
+  L.qlo = off; off += align256((size_t)n_sel * n_b * r * 2);
+  L.sc = off;  off += align256((size_t)n_sel * rtp::tri_rows((int64_t)n_b) * 4);
+  L.sel = off; off += align256((size_t)n_sel * n_b * (top_k + 2) * 4);
+  L.cnt = off; off += align256((size_t)n_sel * n_b * 4);
   L.total = off;
   return L;
 }
@@ -177,19 +179,20 @@ size_t rtp_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
   if (check_shape(S, Hq, Hkv, d) || !is_retrieval) return 0;
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
-  return prefill_layout(S, Hkv, hi.n_ret, r, top_k).total;
+  return prefill_layout(S, Hkv, hi.n_ret, r, top_k, hi.n_ret).total;
 }
 
 size_t rtp_dense_workspace_bytes(int S, int Hq, int Hkv, int d) {
   if (check_shape(S, Hq, Hkv, d)) return 0;
-  return prefill_layout(S, Hkv, 0, 16, 0).total;
+  return prefill_layout(S, Hkv, 0, 16, 0, 0).total;
 }
 
 static int run_indexer(const void* q, const void* k, int S, int Hq, int Hkv,
                        const HeadInfo& hi, const float* p_q, const float* p_k,
                        int r, int top_k, int32_t* sel, int32_t* sel_count,
                        float* kth, float* cent, char* ws,
-                       const PrefillLayout& L, hipStream_t st) {
+                       const PrefillLayout& L, hipStream_t st,
+                       bool keys_only) {
   rtp::IndexerLaunch a;
   a.q = static_cast<const rtp::u16*>(q);
   a.k = static_cast<const rtp::u16*>(k);
@@ -213,6 +216,7 @@ static int run_indexer(const void* q, const void* k, int S, int Hq, int Hkv,
   a.sel_cnt = sel_count;
   a.kth = kth;
   a.centroids = cent;
+  a.keys_only = keys_only;
   hipError_t e = rtp::launch_indexer(a, st);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
   return RTP_OK;
@@ -232,38 +236,56 @@ int rtp_indexer_select(const void* q, const void* k, int S, int Hq, int Hkv,
   if (S == 0 || hi.n_ret == 0) return RTP_OK;
   if (!q || !k || !p_q || !p_k || !sel || !sel_count)
     return fail(RTP_EINVAL, "q, k, p_q, p_k, sel and sel_count must be non-NULL");
-  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k);
+  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k, hi.n_ret);
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
   return run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, sel, sel_count,
                      kth_scores, centroids, static_cast<char*>(ws), L,
-                     reinterpret_cast<hipStream_t>(stream));
+                     reinterpret_cast<hipStream_t>(stream), false);
 }
 
-int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
-                            int S, int Hq, int Hkv, int d,
-                            const uint8_t* is_retrieval, int window,
-                            const float* p_q, const float* p_k, int r,
-                            int block, int top_k, float scale,
-                            const int32_t* sel_in,
-                            const int32_t* sel_count_in, void* out,
-                            float* lse, int32_t* sel_out,
-                            int32_t* sel_count_out, void* ws, size_t ws_bytes,
-                            rtp_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+// Shared body of rtp_hybrid_attn_prefill (one window, sparse retrieval
+// heads) and rtp_headwise_prefill (a window per head, retrieval heads
+// sparse or full, optional centroids).
+int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
+                 int Hkv, int d, const uint8_t* is_retrieval, int window,
+                 const int32_t* windows, int mode, const float* p_q,
+                 const float* p_k, int r, int block, int top_k, float scale,
+                 const int32_t* sel_in, const int32_t* sel_count_in,
+                 void* out, float* lse, int32_t* sel_out,
+                 int32_t* sel_count_out, float* centroids, void* ws,
+                 size_t ws_bytes, rtp_stream_t stream) {
   if (int e = check_shape(S, Hq, Hkv, d)) return e;
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
-  if (window < 1) return fail(RTP_EINVAL, "window must be >= 1");
+  if (mode != RTP_RETRIEVAL_SPARSE && mode != RTP_RETRIEVAL_FULL)
+    return fail(RTP_EINVAL, "retrieval must be RTP_RETRIEVAL_SPARSE or RTP_RETRIEVAL_FULL");
+  const bool full = mode == RTP_RETRIEVAL_FULL;
+  if (windows) {
+    for (int h = 0; h < Hq; ++h)
+      if (!is_retrieval[h] && windows[h] < 1)
+        return fail(RTP_EINVAL, "every streaming head's window must be >= 1");
+  } else if (window < 1) {
+    return fail(RTP_EINVAL, "window must be >= 1");
+  }
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
-  if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
+  if (int e = check_indexer(hi.n_ret, r, block, full ? 0 : top_k)) return e;
   if ((sel_in == nullptr) != (sel_count_in == nullptr))
     return fail(RTP_EINVAL, "sel_in and sel_count_in must both be given or both NULL");
   if ((sel_out == nullptr) != (sel_count_out == nullptr))
     return fail(RTP_EINVAL, "sel_out and sel_count_out must both be given or both NULL");
+  if (full && (sel_in || sel_out))
+    return fail(RTP_EINVAL, "full retrieval heads take and give no selection");
   if (S == 0) return RTP_OK;
   if (!q || !k || !v || !out) return fail(RTP_EINVAL, "q, k, v and out must be non-NULL");
-  if (hi.n_ret > 0 && !sel_in && (!p_q || !p_k))
+  const bool select = !full && hi.n_ret > 0 && !sel_in;
+  if (select && (!p_q || !p_k))
     return fail(RTP_EINVAL, "p_q and p_k must be non-NULL when retrieval heads select");
-  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k);
+  if (centroids && hi.n_ret > 0 && !p_k)
+    return fail(RTP_EINVAL, "p_k must be non-NULL when centroids are requested");
+  const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, full ? 0 : top_k,
+                                         full ? 0 : hi.n_ret);
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -271,15 +293,17 @@ int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
 
   const int32_t* sel = sel_in;
   const int32_t* cnt = sel_count_in;
-  if (hi.n_ret > 0 && !sel_in) {
+  bool centroids_done = !centroids || hi.n_ret == 0;
+  if (select) {
     int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
     int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
     if (int e = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
-                            nullptr, nullptr, w, L, st))
+                            nullptr, centroids, w, L, st, false))
       return e;
     sel = s;
     cnt = c;
-  } else if (hi.n_ret > 0 && sel_out) {
+    centroids_done = true;
+  } else if (!full && hi.n_ret > 0 && sel_out) {
     const size_t n = (size_t)hi.n_ret * n_b;
     hipError_t e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
                                   hipMemcpyDeviceToDevice, st);
@@ -288,11 +312,24 @@ int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
                          hipMemcpyDeviceToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "selection copy");
   }
+  if (!centroids_done) {  // the key projection alone
+    if (int e = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, 0, nullptr,
+                            nullptr, nullptr, centroids, w, L, st, true))
+      return e;
+  }
 
   rtp::u16* vt = reinterpret_cast<rtp::u16*>(w + L.vt);
   hipError_t e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt,
                                          Hkv, S, S_pad, st);
   if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  // Full retrieval heads join the window kernel with a window of S.
+  std::vector<int32_t> head_window;
+  if (windows || full) {
+    head_window.resize(Hq);
+    for (int h = 0; h < Hq; ++h)
+      head_window[h] = full && is_retrieval[h] ? std::max(S, 1)
+                                               : (windows ? windows[h] : window);
+  }
   rtp::AttnLaunch a;
   a.q = static_cast<const rtp::u16*>(q);
   a.k = static_cast<const rtp::u16*>(k);
@@ -307,11 +344,62 @@ int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
   a.n_b = n_b;
   a.G = Hq / Hkv;
   a.Hkv = Hkv;
-  a.window = window;
+  a.window = windows ? 1 : window;
   a.scale = resolve_scale(scale, d);
-  e = rtp::launch_attention(a, is_retrieval, st);
+  a.head_window = head_window.empty() ? nullptr : head_window.data();
+  e = rtp::launch_attention(a, full ? nullptr : is_retrieval, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return RTP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int rtp_hybrid_attn_prefill(const void* q, const void* k, const void* v,
+                            int S, int Hq, int Hkv, int d,
+                            const uint8_t* is_retrieval, int window,
+                            const float* p_q, const float* p_k, int r,
+                            int block, int top_k, float scale,
+                            const int32_t* sel_in,
+                            const int32_t* sel_count_in, void* out,
+                            float* lse, int32_t* sel_out,
+                            int32_t* sel_count_out, void* ws, size_t ws_bytes,
+                            rtp_stream_t stream) {
+  g_err.clear();
+  return prefill_impl(q, k, v, S, Hq, Hkv, d, is_retrieval, window, nullptr,
+                      RTP_RETRIEVAL_SPARSE, p_q, p_k, r, block, top_k, scale,
+                      sel_in, sel_count_in, out, lse, sel_out, sel_count_out,
+                      nullptr, ws, ws_bytes, stream);
+}
+
+size_t rtp_headwise_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
+                                            const uint8_t* is_retrieval,
+                                            int retrieval, int r, int block,
+                                            int top_k) {
+  if (check_shape(S, Hq, Hkv, d) || !is_retrieval) return 0;
+  if (retrieval != RTP_RETRIEVAL_SPARSE && retrieval != RTP_RETRIEVAL_FULL) return 0;
+  const bool full = retrieval == RTP_RETRIEVAL_FULL;
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (check_indexer(hi.n_ret, r, block, full ? 0 : top_k)) return 0;
+  return prefill_layout(S, Hkv, hi.n_ret, r, full ? 0 : top_k,
+                        full ? 0 : hi.n_ret).total;
+}
+
+int rtp_headwise_prefill(const void* q, const void* k, const void* v, int S,
+                         int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                         const int32_t* windows, int retrieval,
+                         const float* p_q, const float* p_k, int r, int block,
+                         int top_k, float scale, const int32_t* sel_in,
+                         const int32_t* sel_count_in, void* out, float* lse,
+                         int32_t* sel_out, int32_t* sel_count_out,
+                         float* centroids, void* ws, size_t ws_bytes,
+                         rtp_stream_t stream) {
+  g_err.clear();
+  if (!windows) return fail(RTP_EINVAL, "windows is NULL");
+  return prefill_impl(q, k, v, S, Hq, Hkv, d, is_retrieval, 1, windows,
+                      retrieval, p_q, p_k, r, block, top_k, scale, sel_in,
+                      sel_count_in, out, lse, sel_out, sel_count_out,
+                      centroids, ws, ws_bytes, stream);
 }
 
 int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
@@ -322,7 +410,7 @@ int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
   if (int e = check_shape(S, Hq, Hkv, d)) return e;
   if (S == 0) return RTP_OK;
   if (!q || !k || !v || !out) return fail(RTP_EINVAL, "q, k, v and out must be non-NULL");
-  const PrefillLayout L = prefill_layout(S, Hkv, 0, 16, 0);
+  const PrefillLayout L = prefill_layout(S, Hkv, 0, 16, 0, 0);
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);

@@ -230,15 +230,20 @@ static_assert(K_DMA == 17 && V_DMA == 18 && DMA_PER_WAVE == 9,
 // blocks of one group.
 constexpr int kXcds = 8;
 
+// Heads are processed in packs: the window heads of one KV head that share
+// a window size (so they share every K/V tile). With one window for all
+// heads a pack is simply a KV group.
 struct WinParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
-  int S, S_pad, n_b, Hkv, window;
+  int S, S_pad, n_b, Hkv;
   float c;
   int per_xcd, n_items;
   int32_t xcd_begin[kXcds + 1];     // item range of each XCD
-  uint8_t hlist[kMaxHeads];   // window heads grouped by KV head
-  int16_t hoff[kMaxHeads + 1];
-  int32_t item_off[kMaxHeads + 1];  // first work item of each KV group
+  uint8_t hlist[kMaxHeads];   // window heads, pack by pack
+  int16_t hoff[kMaxHeads + 1];      // first hlist entry of each pack
+  int32_t item_off[kMaxHeads + 1];  // first work item of each pack
+  uint8_t pack_kv[kMaxHeads];       // KV head of each pack
+  int32_t pack_win[kMaxHeads];      // window of each pack
 };
 
 // The 35 DMA loads of a tile (17 K, 18 V^T) are dealt round-robin to the 4
@@ -542,10 +547,11 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   const int xcd = blockIdx.x % kXcds;
   const int item = p.xcd_begin[xcd] + blockIdx.x / kXcds;
   if (item >= p.xcd_begin[xcd + 1]) return;  // whole workgroup
-  int g = 0;
-  while (item >= p.item_off[g + 1]) ++g;
-  const int ig = item - p.item_off[g];
-  const int h0 = p.hoff[g], nsw = p.hoff[g + 1] - h0;
+  int pk = 0;
+  while (item >= p.item_off[pk + 1]) ++pk;
+  const int ig = item - p.item_off[pk];
+  const int h0 = p.hoff[pk], nsw = p.hoff[pk + 1] - h0;
+  const int g = p.pack_kv[pk];  // KV head
   const int njobs = nsw * p.n_b;
   if (nsw == 0 || 4 * ig >= njobs) return;  // whole workgroup
   const int job = 4 * ig + wave;
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
   const int qb = p.n_b - 1 - jl / nsw;
   const int head = p.hlist[h0 + jl % nsw];
   const int q0 = qb * 64;
-  const int w = p.window;
+  const int w = p.pack_win[pk];
   // union tile range of the workgroup's jobs (up to four consecutive query
   // blocks when a KV group has fewer than four window heads), walked from the
   // top block down: tile t is key block qb_hi - t
@@ -958,30 +964,47 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
   WinParams wp;
   wp.q = a.q; wp.k = a.k; wp.vt = a.vt; wp.out = a.out; wp.lse = a.lse;
   wp.S = a.S; wp.S_pad = a.S_pad; wp.n_b = a.n_b; wp.Hkv = a.Hkv;
-  wp.window = a.window;
   wp.c = c;
-  int nl = 0, n_items = 0;
+  auto win_of = [&](int h) { return a.head_window ? a.head_window[h] : a.window; };
+  // packs: per KV head, its window heads grouped by window size (first
+  // appearance order)
+  int nl = 0, n_items = 0, np = 0;
   for (int g = 0; g < a.Hkv; ++g) {
-    wp.hoff[g] = (int16_t)nl;
-    wp.item_off[g] = n_items;
-    int cnt = 0;
-    for (int h = g * a.G; h < (g + 1) * a.G; ++h)
-      if (!(is_ret && is_ret[h])) {
-        wp.hlist[nl++] = (uint8_t)h;
-        ++cnt;
-      }
-    n_items += (cnt * a.n_b + 3) / 4;
+    bool taken[kMaxHeads] = {};
+    for (int h0 = g * a.G; h0 < (g + 1) * a.G; ++h0) {
+      if ((is_ret && is_ret[h0]) || taken[h0]) continue;
+      const int w0 = win_of(h0);
+      wp.hoff[np] = (int16_t)nl;
+      wp.item_off[np] = n_items;
+      wp.pack_kv[np] = (uint8_t)g;
+      wp.pack_win[np] = w0;
+      int cnt = 0;
+      for (int h = h0; h < (g + 1) * a.G; ++h)
+        if (!(is_ret && is_ret[h]) && !taken[h] && win_of(h) == w0) {
+          taken[h] = true;
+          wp.hlist[nl++] = (uint8_t)h;
+          ++cnt;
+        }
+      n_items += (cnt * a.n_b + 3) / 4;
+      ++np;
+    }
   }
-  wp.hoff[a.Hkv] = (int16_t)nl;
-  wp.item_off[a.Hkv] = n_items;
+  wp.hoff[np] = (int16_t)nl;
+  wp.item_off[np] = n_items;
+  for (int i = np; i < kMaxHeads; ++i) {
+    wp.pack_kv[i] = 0;
+    wp.pack_win[i] = 1;
+    wp.hoff[i + 1] = (int16_t)nl;
+    wp.item_off[i + 1] = n_items;
+  }
   for (int i = nl; i < kMaxHeads; ++i) wp.hlist[i] = 0;
   wp.n_items = n_items;
   // cost-balanced contiguous item ranges per XCD (the tile count of an item
   // follows the kernel's own range computation)
   {
-    const int w = a.window;
-    auto item_cost = [&](int g, int ig) -> int64_t {
-      const int nsw = wp.hoff[g + 1] - wp.hoff[g];
+    auto item_cost = [&](int pk, int ig) -> int64_t {
+      const int w = wp.pack_win[pk];
+      const int nsw = wp.hoff[pk + 1] - wp.hoff[pk];
       const int njobs = nsw * a.n_b;
       const int qb_hi = a.n_b - 1 - (4 * ig) / nsw;
       const int qb_lo = a.n_b - 1 - min(4 * ig + 3, njobs - 1) / nsw;
@@ -990,15 +1013,15 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
       return (qb_hi - kt_lo + 1) + 9;  // + per-item prologue/epilogue
     };
     int64_t total = 0;
-    for (int g = 0; g < a.Hkv; ++g)
-      for (int ig = 0; ig < wp.item_off[g + 1] - wp.item_off[g]; ++ig)
-        total += item_cost(g, ig);
+    for (int pk = 0; pk < np; ++pk)
+      for (int ig = 0; ig < wp.item_off[pk + 1] - wp.item_off[pk]; ++ig)
+        total += item_cost(pk, ig);
     int x = 0, item = 0;
     int64_t run = 0;
     wp.xcd_begin[0] = 0;
-    for (int g = 0; g < a.Hkv; ++g)
-      for (int ig = 0; ig < wp.item_off[g + 1] - wp.item_off[g]; ++ig, ++item) {
-        run += item_cost(g, ig);
+    for (int pk = 0; pk < np; ++pk)
+      for (int ig = 0; ig < wp.item_off[pk + 1] - wp.item_off[pk]; ++ig, ++item) {
+        run += item_cost(pk, ig);
         while (x + 1 < kXcds && run * kXcds >= total * (x + 1))
           wp.xcd_begin[++x] = item + 1;
       }

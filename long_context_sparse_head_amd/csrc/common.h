@@ -78,6 +78,9 @@ struct AttnLaunch {
   const int32_t* sel; const int32_t* sel_cnt; int sel_stride;
   int S, S_pad, n_b, G, Hkv, window;
   float scale;
+  // HOST [Hq] window of each head attended by the window kernel, or NULL
+  // (then `window` for every such head)
+  const int32_t* head_window = nullptr;
 };
 
 hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
@@ -92,6 +95,7 @@ struct IndexerLaunch {
   const uint8_t* ret_heads;  // host: query head of each retrieval index
   u16* khi; u16* klo; u16* qhi; u16* qlo; float* scores;
   int32_t* sel; int32_t* sel_cnt; float* kth; float* centroids;
+  bool keys_only = false;  // only the key projection (and centroids)
 };
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
 

@@ -351,6 +351,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
   hipLaunchKernelGGL(proj_keys_kernel, dim3(a.n_ret, a.S_pad / 64), dim3(64), 0,
                      st, a.k, a.p_k, pa, a.khi, a.klo, a.centroids);
   prof_end(st);
+  if (a.keys_only) return hipGetLastError();
   prof_begin("proj_qmeans", st);
   hipLaunchKernelGGL(proj_qmeans_kernel, dim3(a.n_ret, a.n_b), dim3(64), 0, st,
                      a.q, a.p_q, pa, a.qhi, a.qlo);

@@ -24,6 +24,12 @@ Steps, in the order the pages give them:
 3. Attention over a key set J_i (both head kinds): s_j = scale * q_i . k_j,
    lse_i = log sum_{j in J_i} exp(s_j), p_j = exp(s_j - lse_i),
    o_i = sum_j p_j v_j. The softmax is kept exact; only the key set shrinks.
+
+Variant (RTPurboV2 article, paragraph on the Qwen3-Coder-30B-A3B setup):
+the window may differ per streaming head (some are 8192), and retrieval
+heads may use full attention in prefill, J_i = {j <= i}, while the key
+clustering (the block centroids of step 2a's projected keys) is still
+produced for decode.
 """
 from __future__ import annotations
 
@@ -182,8 +188,14 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
                    scale: Optional[float] = None, sel_override=None,
                    heads: Optional[Iterable[int]] = None,
                    query_blocks: Optional[Iterable[int]] = None,
-                   sel_rows: Optional[Iterable[int]] = None) -> dict:
+                   sel_rows: Optional[Iterable[int]] = None,
+                   retrieval_full: bool = False) -> dict:
     """Headwise hybrid prefill of one layer.
+
+    window: one window for every streaming head, or a sequence of Hq
+    windows (entries of retrieval heads unused). retrieval_full: retrieval
+    heads attend every key j <= i (no selection; centroids are still
+    computed when p_k is given).
 
     q_bits [Hq,S,d], k_bits/v_bits [Hkv,S,d]: bf16 storage (uint16).
     is_retrieval [Hq]: nonzero marks a retrieval head; p_q/p_k [n_ret,r,d]
@@ -204,6 +216,7 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     B = block
     n_b = -(-S // B)
     mask = np.asarray(is_retrieval).astype(bool)
+    win_of = np.broadcast_to(np.asarray(window, dtype=np.int64), (Hq,))
     ret_heads = [h for h in range(Hq) if mask[h]]
     rho_of = {h: i for i, h in enumerate(ret_heads)}
     scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else scale
@@ -233,7 +246,11 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         g = h // G
         kf, vf = kv(g)
         qf = bf16_to_f32(q_bits[h])
-        if mask[h]:
+        if mask[h] and retrieval_full:
+            rho = rho_of[h]
+            if p_k is not None and n_ret:
+                cents[rho] = block_centroids(project_keys(kf, p_k[rho]), B)
+        elif mask[h]:
             rho = rho_of[h]
             if sel_override is not None:
                 sel = sel_override[rho]
@@ -248,10 +265,12 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
                 sel_cnt[rho, qb] = len(s)
         for qb in qblocks:
             rows = np.arange(qb * B, min(S, (qb + 1) * B))
-            if mask[h]:
+            if mask[h] and retrieval_full:
+                union, member = swa_block_keys(rows, S)  # every j <= i
+            elif mask[h]:
                 union, member = retrieval_block_keys(rows, sel[qb], B, S)
             else:
-                union, member = swa_block_keys(rows, window)
+                union, member = swa_block_keys(rows, int(win_of[h]))
             o, l = attend(qf[rows], kf[union], vf[union], member, scale)
             out[h, rows] = o
             lse[h, rows] = l

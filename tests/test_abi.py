@@ -110,6 +110,49 @@ def test_prefill_argument_validation_returns_codes():
     assert _prefill(lib, mp2, Hq=130, Hkv=130) == -2
 
 
+def _headwise(lib, mp, windows, **kw):
+    a = dict(q=1, k=1, v=1, S=128, Hq=4, Hkv=1, d=128, mode=0, pq=1, pk=1,
+             r=16, block=64, top_k=4, scale=0.0, sel_in=None, cnt_in=None,
+             out=1, lse=None, sel_out=None, cnt_out=None, cent=None, ws=None,
+             wsb=0)
+    a.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    wp = None if windows is None else np.array(windows, dtype=np.int32)
+    wptr = None if wp is None else wp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return lib.rtp_headwise_prefill(
+        P(a["q"]), P(a["k"]), P(a["v"]), a["S"], a["Hq"], a["Hkv"], a["d"],
+        mp, wptr, a["mode"], P(a["pq"]), P(a["pk"]), a["r"], a["block"],
+        a["top_k"], a["scale"], P(a["sel_in"]), P(a["cnt_in"]), P(a["out"]),
+        P(a["lse"]), P(a["sel_out"]), P(a["cnt_out"]), P(a["cent"]),
+        P(a["ws"]), a["wsb"], None)
+
+
+def test_headwise_prefill_validation_and_workspace():
+    lib = rtp.load()
+    m, mp = _mask([1, 0, 0, 0])
+    ok = [0, 16, 8192, 1]  # head 0 is a retrieval head: its entry is unused
+    assert _headwise(lib, mp, None) == -1
+    assert _headwise(lib, mp, [5, 16, 0, 1]) == -1          # a window of 0
+    assert _headwise(lib, mp, ok, mode=2) == -1             # unknown mode
+    assert _headwise(lib, mp, ok, mode=1, sel_in=8, cnt_in=8) == -1
+    assert _headwise(lib, mp, ok, mode=1, sel_out=8, cnt_out=8) == -1
+    assert _headwise(lib, mp, ok, mode=0, pq=None) == -1     # must select
+    assert _headwise(lib, mp, ok, mode=1, pk=None, cent=8) == -1
+    assert _headwise(lib, mp, ok, mode=1, pq=None) == -3     # fine, no ws
+    assert _headwise(lib, mp, ok, d=64) == -2
+    assert _headwise(lib, mp, ok, S=0) == 0
+    S, n_b = 2048, 32
+    sparse = lib.rtp_headwise_prefill_workspace_bytes(S, 4, 1, 128, mp, 0, 16,
+                                                      64, 8)
+    assert sparse == lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 16, 64, 8)
+    al = lambda x: (x + 255) // 256 * 256
+    full = lib.rtp_headwise_prefill_workspace_bytes(S, 4, 1, 128, mp, 1, 16,
+                                                    64, 8)
+    assert full == al(128 * S * 2) + 2 * al(S * 16 * 2)  # V^T + projected keys
+    assert lib.rtp_headwise_prefill_workspace_bytes(S, 4, 1, 128, mp, 3, 16,
+                                                    64, 8) == 0
+
+
 def test_decode_and_centroid_validation():
     lib = rtp.load()
     m, mp = _mask([0, 1])

@@ -119,6 +119,49 @@ def test_swa_band_matches_masked_sdpa():
         assert np.abs(res["lse"][h] - lse).max() < 2e-5
 
 
+def test_per_head_windows_match_masked_sdpa():
+    # a window per streaming head: each head is the textbook band of its own
+    # width (1: the value itself; >= S: causal), whatever its neighbours use
+    S = 300
+    windows = [1, 37, 300 + 5, 64, 2, 150]
+    x = _prefill(S, Hq=6, Hkv=2, d=48, ret=(), window=8, top_k=1)
+    res = _run(x, window=windows)
+    q, k, v = _f32(x["qb"]), _f32(x["kb"]), _f32(x["vb"])
+    t = torch.ones(S, S, dtype=torch.bool)
+    for h, w in enumerate(windows):
+        band = (torch.tril(t) & torch.triu(t, diagonal=-(w - 1))).numpy()
+        o, lse = _sdpa64(q[h], k[h // 3], v[h // 3], band)
+        assert np.abs(res["out"][h] - o).max() < 2e-5, h
+        assert np.abs(res["lse"][h] - lse).max() < 2e-5, h
+    assert np.array_equal(res["out"][0], v[0])
+
+
+def test_full_retrieval_heads_are_dense_causal_with_centroids():
+    # retrieval heads in full mode attend every earlier token (dense causal,
+    # textbook), streaming heads keep their windows, and the key clustering
+    # is still produced: centroid = P_k mean(k) per block (linearity)
+    S = 330
+    x = _prefill(S, Hq=4, Hkv=2, d=64, ret=(1, 2), window=40, top_k=2)
+    res = _run(x, retrieval_full=True)
+    q, k, v = _f32(x["qb"]), _f32(x["kb"]), _f32(x["vb"])
+    t = torch.ones(S, S, dtype=torch.bool)
+    causal = torch.tril(t).numpy()
+    band = (torch.tril(t) & torch.triu(t, diagonal=-39)).numpy()
+    for h in range(4):
+        o, lse = _sdpa64(q[h], k[h // 2], v[h // 2],
+                         causal if h in (1, 2) else band)
+        assert np.abs(res["out"][h] - o).max() < 2e-5, h
+        assert np.abs(res["lse"][h] - lse).max() < 2e-5, h
+    n_b = -(-S // 64)
+    for rho, h in enumerate((1, 2)):
+        kg = k[h // 2].astype(np.float64)
+        means = np.stack([kg[b * 64:(b + 1) * 64].mean(0) for b in range(n_b)])
+        alt = means @ x["p_k"][rho].T.astype(np.float64)
+        assert np.abs(res["centroids"][rho] - alt).max() < \
+            1e-5 * np.abs(alt).max()
+    assert (res["sel_count"] == 0).all()  # no selection in full mode
+
+
 def test_block_sparse_matches_masked_sdpa():
     S, B = 640, 64
     x = _prefill(S, Hq=2, Hkv=1, d=64, ret=(0,), window=64, top_k=3)
