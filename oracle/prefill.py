@@ -139,6 +139,21 @@ def selected_keys(sel: np.ndarray, i: int, B: int, S: int) -> np.ndarray:
     return j[j <= i]
 
 
+def head_window(window, h: int) -> int:
+    """Window of streaming head h: one window for all heads, or head h's
+    entry of a per-head sequence (RTPurboV2 article, Qwen3-Coder-30B-A3B
+    paragraph: streaming heads use SWA, some with 8192)."""
+    if np.ndim(window) == 0:
+        return int(window)
+    return int(np.asarray(window)[h])
+
+
+def causal_block_keys(rows: np.ndarray):
+    """Keys of a full (causal) head for a run of queries: every j <= i."""
+    union = np.arange(0, int(rows[-1]) + 1, dtype=np.int64)
+    return union, union[None, :] <= rows[:, None]
+
+
 def swa_block_keys(rows: np.ndarray, w: int):
     """Step 1 for a run of consecutive queries: (union of keys, membership).
 
@@ -216,7 +231,6 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     B = block
     n_b = -(-S // B)
     mask = np.asarray(is_retrieval).astype(bool)
-    win_of = np.broadcast_to(np.asarray(window, dtype=np.int64), (Hq,))
     ret_heads = [h for h in range(Hq) if mask[h]]
     rho_of = {h: i for i, h in enumerate(ret_heads)}
     scale = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else scale
@@ -266,11 +280,11 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         for qb in qblocks:
             rows = np.arange(qb * B, min(S, (qb + 1) * B))
             if mask[h] and retrieval_full:
-                union, member = swa_block_keys(rows, S)  # every j <= i
+                union, member = causal_block_keys(rows)
             elif mask[h]:
                 union, member = retrieval_block_keys(rows, sel[qb], B, S)
             else:
-                union, member = swa_block_keys(rows, int(win_of[h]))
+                union, member = swa_block_keys(rows, head_window(window, h))
             o, l = attend(qf[rows], kf[union], vf[union], member, scale)
             out[h, rows] = o
             lse[h, rows] = l

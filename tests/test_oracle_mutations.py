@@ -97,6 +97,18 @@ def _retrieval_keys_no_causal(rows, sel, B, S):
     return union, np.ones((len(rows), len(union)), dtype=bool)
 
 
+def _head_window_of_neighbour(window, h):
+    if np.ndim(window) == 0:
+        return int(window)
+    w = np.asarray(window)
+    return int(w[(h + 1) % len(w)])             # the next head's window
+
+
+def _causal_keys_without_self(rows):
+    union, member = _orig_causal_keys(rows)
+    return union, member & (union[None, :] < rows[:, None])
+
+
 def _decode_select_no_recent(q_tilde, cents, n_b, k, n_recent):
     sel, a, b = _orig_dec_select(q_tilde, cents, n_b, k, n_recent)
     return sel[sel < n_b - 1] if n_b > 1 else sel, a, b
@@ -107,6 +119,7 @@ _orig_score = op.block_score_row
 _orig_select = op.select_row
 _orig_ret_keys = op.retrieval_block_keys
 _orig_dec_select = od.decode_select
+_orig_causal_keys = op.causal_block_keys
 
 MUTATIONS = [
     (op, "swa_block_keys", _swa_off_by_one),
@@ -122,6 +135,8 @@ MUTATIONS = [
     (op, "attend", _attend_drop_max_row),
     (op, "retrieval_block_keys", _retrieval_keys_no_causal),
     (od, "decode_select", _decode_select_no_recent),
+    (op, "head_window", _head_window_of_neighbour),
+    (op, "causal_block_keys", _causal_keys_without_self),
 ]
 
 PIN_TESTS = [
@@ -136,6 +151,8 @@ PIN_TESTS = [
     pins.test_decode_full_coverage_equals_last_row_of_dense,
     pins.test_decode_window_is_last_w_tokens,
     pins.test_decode_planted_selection,
+    pins.test_per_head_windows_match_masked_sdpa,
+    pins.test_full_retrieval_heads_are_dense_causal_with_centroids,
 ]
 
 
