@@ -133,13 +133,16 @@ __global__ __launch_bounds__(64) void proj_qmeans_kernel(
 
 // ---- block scores: grid (ceil(n_b/128), ceil(n_b/KBC), n_ret), 4 waves.
 // Workgroup = 128 query blocks (32 per wave, along the MFMA N dimension) x a
-// chunk of KBC key blocks. For each key block the 64 projected keys are
-// staged in LDS and each wave computes the 64 x 32 dot products as two
-// 32x32 tiles (keys along M), then max-pools the 64 keys of the block. The
-// query tile is the fastest grid index, so the workgroups that share a key
-// chunk run together and read it from L2. Scores are collected in LDS and
-// written row by row, one contiguous run of up to KBC floats per row.
-constexpr int KBC = 64;
+// chunk of KBC key blocks. Key blocks are staged in LDS KBI at a time (the
+// 64 projected keys of each, hi and lo parts); each wave computes the 64 x 32
+// dot products of a key block as two 32x32 tiles (keys along M) and
+// max-pools its 64 keys. A stage is loaded into registers two stages ahead
+// and written to LDS one stage ahead, so each global round trip is hidden
+// behind two stages of MFMA work. The query tile is the fastest grid index,
+// so the workgroups that share a key chunk run together and read it from
+// L2. Scores are collected in LDS and written row by row, one contiguous run
+// of up to KBC floats per row.
+constexpr int KBC = 48;
 
 template <int R16>
 __global__ __launch_bounds__(256) void block_scores_kernel(
@@ -148,7 +151,10 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
     float* __restrict__ scores, int S_pad, int n_b) {
   constexpr int r = 16 * R16;
   constexpr int RS = r + 8;  // LDS row stride (bf16), 16-byte pad
-  __shared__ __attribute__((aligned(16))) u16 st[2][2][64 * RS];
+  constexpr int KBI = R16 >= 4 ? 1 : 4 / R16;  // key blocks per stage
+  static_assert(KBC % KBI == 0, "a chunk is whole stages");
+  constexpr int SROWS = 64 * KBI;
+  __shared__ __attribute__((aligned(16))) u16 st[2][2][SROWS * RS];
   __shared__ float scs[128][KBC + 1];
   const int qt = blockIdx.x, kc = blockIdx.y, rho = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -176,50 +182,47 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
   const int64_t tri = tri_rows(n_b);
   float* srow_base = scores + (size_t)rho * tri;
 
-  // staging: 64 rows x r bf16 (hi and lo) = 64*r*4 bytes = r*16 chunks of 16 B
-  constexpr int CH_PER_ROW = r / 8;            // 16-byte chunks per row
-  constexpr int NCH = 64 * CH_PER_ROW * 2;     // hi + lo
-  constexpr int PER_T = (NCH + 255) / 256;
-  uint4 reg[PER_T];
+  // a stage: SROWS rows x r bf16, hi and lo = SROWS * r / 4 chunks of 16 B
+  constexpr int CH_PER_ROW = r / 8;
+  constexpr int NCH = SROWS * CH_PER_ROW * 2;
+  static_assert(NCH % 256 == 0, "whole chunks per thread");
+  constexpr int PER_T = NCH / 256;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const u16* kh = khi + (size_t)rho * S_pad * r;
   const u16* kl = klo + (size_t)rho * S_pad * r;
-  auto gload = [&](int kb) {
+  const int nst = (kb_end - kb_begin + KBI - 1) / KBI;
+  // key blocks past the chunk re-read its last block (never used)
+  auto gload = [&](int stg, u32x4 (&reg)[PER_T]) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int c = tid + 256 * i;
-      if (c < NCH) {
-        const int part = c / (64 * CH_PER_ROW), cc = c % (64 * CH_PER_ROW);
-        const int row = cc / CH_PER_ROW, ch = cc % CH_PER_ROW;
-        const u16* src = (part ? kl : kh) + ((size_t)kb * 64 + row) * r + ch * 8;
-        reg[i] = *reinterpret_cast<const uint4*>(src);
-      }
+      const int part = c / (SROWS * CH_PER_ROW), cc = c % (SROWS * CH_PER_ROW);
+      const int row = cc / CH_PER_ROW, ch = cc % CH_PER_ROW;
+      const int kb = min(kb_begin + stg * KBI + row / 64, kb_end - 1);
+      const u16* src = (part ? kl : kh) + ((size_t)kb * 64 + (row & 63)) * r + ch * 8;
+      reg[i] = *reinterpret_cast<const u32x4*>(src);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4 (&reg)[PER_T]) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int c = tid + 256 * i;
-      if (c < NCH) {
-        const int part = c / (64 * CH_PER_ROW), cc = c % (64 * CH_PER_ROW);
-        const int row = cc / CH_PER_ROW, ch = cc % CH_PER_ROW;
-        *reinterpret_cast<uint4*>(&st[buf][part][row * RS + ch * 8]) = reg[i];
-      }
+      const int part = c / (SROWS * CH_PER_ROW), cc = c % (SROWS * CH_PER_ROW);
+      const int row = cc / CH_PER_ROW, ch = cc % CH_PER_ROW;
+      *reinterpret_cast<u32x4*>(&st[buf][part][row * RS + ch * 8]) = reg[i];
     }
   };
-
-  gload(kb_begin);
-  sstore(0);
-  __syncthreads();
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const int buf = (kb - kb_begin) & 1;
-    if (kb + 1 < kb_end) gload(kb + 1);
-    if (kb < wave_qmax) {  // some query block of this wave has kb as candidate
+  auto compute = [&](int stg, int buf) {
+#pragma unroll
+    for (int j = 0; j < KBI; ++j) {
+      const int kb = kb_begin + stg * KBI + j;
+      if (kb >= kb_end || kb >= wave_qmax) continue;  // wave-uniform
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         f32x16 acc = {};
-        const u16* ah = &st[buf][0][(32 * mt + n) * RS + 8 * g];
-        const u16* al = &st[buf][1][(32 * mt + n) * RS + 8 * g];
+        const u16* ah = &st[buf][0][(64 * j + 32 * mt + n) * RS + 8 * g];
+        const u16* al = &st[buf][1][(64 * j + 32 * mt + n) * RS + 8 * g];
 #pragma unroll
         for (int rs = 0; rs < R16; ++rs) {
           const bf16x8 a_hi = *reinterpret_cast<const bf16x8*>(ah + 16 * rs);
@@ -234,8 +237,25 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (g == 0) scs[32 * wave + n][kb - kb_begin] = mx;
     }
-    if (kb + 1 < kb_end) sstore(buf ^ 1);
+  };
+
+  // stage s sits in register set s % 2 until it is written to LDS buffer
+  // s % 2; set (s + 2) % 2 is refilled as soon as stage s is in LDS
+  u32x4 ra[PER_T], rb[PER_T];
+  gload(0, ra);
+  gload(min(1, nst - 1), rb);
+  sstore(0, ra);
+  __syncthreads();
+  auto step = [&](int s, u32x4 (&cur)[PER_T], u32x4 (&nxt)[PER_T]) {
+    // cur held stage s (already in LDS): refill it with stage s + 2
+    gload(min(s + 2, nst - 1), cur);
+    compute(s, s & 1);
+    if (s + 1 < nst) sstore((s + 1) & 1, nxt);
     __syncthreads();
+  };
+  for (int s = 0; s < nst; s += 2) {
+    step(s, ra, rb);
+    if (s + 1 < nst) step(s + 1, rb, ra);
   }
   // write-out: row qb takes candidates kb_begin .. min(kb_end, qb) - 1
   for (int i = 0; i < 32; ++i) {
