@@ -43,9 +43,9 @@ METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA p
 TRAFFIC = {
     "kernel": "attn_window_kernel",
     "source": "long_context_sparse_head_amd/csrc/attn.hip",
-    "sha256": "63f328adc0651f28c74feb8710487508fd6b41b2c102ad70cc5df1e50c639575",
-    "fetch_bytes": 2934394379,
-    "write_bytes": 906019155,
+    "sha256": "34d52e3b0c999161f0ace3d96d3fb0507c5626bafb38565078ff863a5add3ef2",
+    "fetch_bytes": 2937455969,
+    "write_bytes": 906052486,
 }
 
 

@@ -86,6 +86,21 @@ def test_ragged_lengths(gpu_lib, S):
     full_check(gpu_lib, x, f"S={S}")
 
 
+@pytest.mark.parametrize("r", [32, 48, 64])
+def test_indexer_ranks(gpu_lib, r):
+    # other indexer ranks stage a different number of key blocks per step
+    x = make_prefill(_wl(64 * 37 + 11, Hq=4, Hkv=1, ret=(0, 3), window=150,
+                         top_k=5, r=r))
+    full_check(gpu_lib, x, f"r{r}")
+
+
+def test_every_head_retrieval_one_head_per_group(gpu_lib):
+    # G = 1 and no streaming heads: only the sparse kernel runs
+    x = make_prefill(_wl(64 * 21 + 3, Hq=3, Hkv=3, ret=(0, 1, 2), window=64,
+                         top_k=4))
+    full_check(gpu_lib, x, "allret")
+
+
 @pytest.mark.parametrize("window,top_k", [(1, 0), (64, 1), (65, 2),
                                           (4096, 100)])
 def test_window_and_budget_edges(gpu_lib, window, top_k):
