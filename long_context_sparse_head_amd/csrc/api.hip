@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <mutex>
+#include <optional>
 #include <string>
 #include <vector>
 
@@ -107,7 +108,62 @@ constexpr size_t kProfMax = 1 << 14;
 
 }  // namespace
 
+namespace {
+struct AuxSlot {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu;
+AuxSlot g_aux[kMaxDevices];
+}  // namespace
+
 namespace rtp {
+AuxFork::AuxFork(hipStream_t st) : st_(st), aux_(st) {
+  g_aux_mu.lock();
+  locked_ = true;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return;
+  }
+  AuxSlot& x = g_aux[dev];
+  if (x.failed) return;
+  if (!x.s) {
+    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
+      x.failed = true;
+      (void)hipGetLastError();
+      return;
+    }
+  }
+  err_ = hipEventRecord(x.fork, st);
+  if (err_ == hipSuccess) err_ = hipStreamWaitEvent(x.s, x.fork, 0);
+  if (err_ == hipSuccess) {
+    aux_ = x.s;
+    slot_ = &x;
+  }
+}
+
+hipError_t AuxFork::join() {
+  hipError_t e = hipSuccess;
+  if (!joined_ && slot_) {
+    AuxSlot& x = *static_cast<AuxSlot*>(slot_);
+    e = hipEventRecord(x.join, aux_);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st_, x.join, 0);
+  }
+  joined_ = true;
+  if (locked_) {
+    locked_ = false;
+    g_aux_mu.unlock();
+  }
+  return e;
+}
+
+AuxFork::~AuxFork() { (void)join(); }
+
 void prof_begin(const char* name, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on || g_prof_recs.size() >= kProfMax) return;
@@ -291,33 +347,7 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   char* w = static_cast<char*>(ws);
   const int n_b = (S + 63) / 64, S_pad = n_b * 64;
 
-  const int32_t* sel = sel_in;
-  const int32_t* cnt = sel_count_in;
-  bool centroids_done = !centroids || hi.n_ret == 0;
-  if (select) {
-    int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
-    int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
-    if (int e = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
-                            nullptr, centroids, w, L, st, false))
-      return e;
-    sel = s;
-    cnt = c;
-    centroids_done = true;
-  } else if (!full && hi.n_ret > 0 && sel_out) {
-    const size_t n = (size_t)hi.n_ret * n_b;
-    hipError_t e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
-                                  hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(sel_count_out, sel_count_in, n * 4,
-                         hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return hip_fail(e, "selection copy");
-  }
-  if (!centroids_done) {  // the key projection alone
-    if (int e = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, 0, nullptr,
-                            nullptr, nullptr, centroids, w, L, st, true))
-      return e;
-  }
-
+  // V^T first: both attention kernels read it
   rtp::u16* vt = reinterpret_cast<rtp::u16*>(w + L.vt);
   hipError_t e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt,
                                          Hkv, S, S_pad, st);
@@ -336,8 +366,8 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   a.vt = vt;
   a.out = static_cast<rtp::u16*>(out);
   a.lse = lse;
-  a.sel = sel;
-  a.sel_cnt = cnt;
+  a.sel = sel_in;
+  a.sel_cnt = sel_count_in;
   a.sel_stride = top_k + 2;
   a.S = S;
   a.S_pad = S_pad;
@@ -347,8 +377,51 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   a.window = windows ? 1 : window;
   a.scale = resolve_scale(scale, d);
   a.head_window = head_window.empty() ? nullptr : head_window.data();
-  e = rtp::launch_attention(a, full ? nullptr : is_retrieval, st);
+  const uint8_t* sparse_heads = full ? nullptr : is_retrieval;
+
+  // The indexer feeds only the retrieval heads, so on long sequences the
+  // window heads attend on the device's auxiliary stream while it runs. Its
+  // cost grows with S^2 and the window heads' with S w: at 1M tokens this
+  // hides most of the indexer (-2.7% per layer), at 128K the window kernel
+  // fills every CU and the gain is 0.5%, so shorter sequences stay on one
+  // stream (which also keeps each kernel's time measurable on its own).
+  constexpr int kForkMinBlocks = 4096;
+  const bool fork = select && hi.n_ret < Hq && n_b > kForkMinBlocks;
+  std::optional<rtp::AuxFork> aux;
+  if (fork) {
+    aux.emplace(st);
+    if ((e = aux->status()) != hipSuccess) return hip_fail(e, "stream fork");
+    e = rtp::launch_attention(a, sparse_heads, aux->stream(), rtp::kAttnWindow);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+  }
+  bool centroids_done = !centroids || hi.n_ret == 0;
+  if (select) {
+    int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
+    int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
+    if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
+                              nullptr, centroids, w, L, st, false))
+      return err;
+    a.sel = s;
+    a.sel_cnt = c;
+    centroids_done = true;
+  } else if (!full && hi.n_ret > 0 && sel_out) {
+    const size_t n = (size_t)hi.n_ret * n_b;
+    e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
+                       hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(sel_count_out, sel_count_in, n * 4,
+                         hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "selection copy");
+  }
+  if (!centroids_done) {  // the key projection alone
+    if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, 0, nullptr,
+                              nullptr, nullptr, centroids, w, L, st, true))
+      return err;
+  }
+  e = rtp::launch_attention(a, sparse_heads, st,
+                            fork ? rtp::kAttnSparse : rtp::kAttnAll);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (fork && (e = aux->join()) != hipSuccess) return hip_fail(e, "stream join");
   return RTP_OK;
 }
 }  // namespace

@@ -956,7 +956,7 @@ hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
 }
 
 hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
-                            hipStream_t st) {
+                            hipStream_t st, int parts) {
   if (a.n_b == 0) return hipSuccess;
   const int Hq = a.G * a.Hkv;
   const float c = a.scale * 1.4426950408889634f;
@@ -1031,7 +1031,7 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
       longest = max(longest, wp.xcd_begin[i + 1] - wp.xcd_begin[i]);
     wp.per_xcd = longest;
   }
-  if (nl > 0) {
+  if (nl > 0 && (parts & kAttnWindow)) {
     prof_begin("attn_window", st);
     hipLaunchKernelGGL(attn_window_kernel, dim3(wp.per_xcd * kXcds), dim3(256),
                        0, st, wp);
@@ -1040,6 +1040,7 @@ hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
     if (e != hipSuccess) return e;
   }
   // retrieval heads
+  if (!(parts & kAttnSparse)) return hipSuccess;
   int n_ret = 0;
   SparseParams sp;
   for (int h = 0; h < Hq; ++h)

@@ -70,6 +70,31 @@ __device__ __forceinline__ int perm_row(int r) {
 void prof_begin(const char* name, hipStream_t st);
 void prof_end(hipStream_t st);
 
+// Fork and join with the device's auxiliary stream: a library-owned stream
+// (default priority, created on first use) on which independent work runs
+// concurrently with the caller's stream. Constructing an AuxFork records an
+// event on `st` that the auxiliary stream waits for, so work put on
+// stream() starts after everything enqueued on `st` before; join() makes
+// `st` wait for that work. Holds a process-wide lock from construction to
+// join() (or destruction), so the events are never shared by two calls.
+// If the auxiliary stream cannot be created, stream() is `st` itself.
+class AuxFork {
+ public:
+  explicit AuxFork(hipStream_t st);
+  ~AuxFork();
+  AuxFork(const AuxFork&) = delete;
+  AuxFork& operator=(const AuxFork&) = delete;
+  hipStream_t stream() const { return aux_; }
+  hipError_t status() const { return err_; }
+  hipError_t join();
+
+ private:
+  hipStream_t st_, aux_;
+  void* slot_ = nullptr;
+  hipError_t err_ = hipSuccess;
+  bool locked_ = false, joined_ = false;
+};
+
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
@@ -85,9 +110,11 @@ struct AttnLaunch {
 
 hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
                               hipStream_t st);
-// is_ret: host [Hq]; nullptr means every head is a window head.
+// is_ret: host [Hq]; nullptr means every head is a window head. parts: 1 =
+// window heads only, 2 = retrieval heads only, 3 = both.
+constexpr int kAttnWindow = 1, kAttnSparse = 2, kAttnAll = 3;
 hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
-                            hipStream_t st);
+                            hipStream_t st, int parts = kAttnAll);
 
 struct IndexerLaunch {
   const u16* q; const u16* k; const float* p_q; const float* p_k;

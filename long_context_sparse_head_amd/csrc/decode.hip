@@ -18,8 +18,6 @@
 #include "common.h"
 #include "select.h"
 
-#include <mutex>
-
 namespace rtp {
 
 constexpr int kDecMaxUnitHeads = 8;
@@ -595,41 +593,10 @@ __global__ __launch_bounds__(128) void dec_merge_kernel(
     lse[(size_t)b * Hq + h] = (M * c + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
-// Streaming-head attention needs no block choice, so it runs on a
-// library-owned auxiliary stream of the device, concurrently with the block
-// choice and the retrieval-head attention on the caller's stream. Events
-// order it after the caller's earlier work and the merge after it, so the
-// call keeps plain stream semantics (and no host synchronisation).
-namespace {
-struct AuxStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_aux_mu;
-AuxStream g_aux[kMaxDevices];
-
-// Creates the device's auxiliary stream on first use; nullptr if that is
-// impossible (the caller then runs everything on its own stream).
-AuxStream* aux_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  AuxStream& x = g_aux[dev];
-  if (x.failed) return nullptr;
-  if (!x.s) {
-    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
-      x.failed = true;
-      (void)hipGetLastError();
-      return nullptr;
-    }
-  }
-  return &x;
-}
-}  // namespace
-
+// Streaming-head attention needs no block choice, so it runs on the
+// device's auxiliary stream (AuxFork), concurrently with the block choice and
+// the retrieval-head attention on the caller's stream; the merge waits for
+// both.
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
@@ -708,26 +675,19 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     prof_end(on);
   };
   hipError_t e = hipSuccess;
-  {
-    std::lock_guard<std::mutex> lk(g_aux_mu);
-    AuxStream* aux = n_win_units > 0 && n_ret_units > 0 ? aux_stream() : nullptr;
-    if (aux) {
-      e = hipEventRecord(aux->fork, st);
-      if (e == hipSuccess) e = hipStreamWaitEvent(aux->s, aux->fork, 0);
-      if (e != hipSuccess) return e;
-      attend("dec_attn_window", 0, n_win_units, aux->s);
-      e = hipGetLastError();
-      if (e == hipSuccess) e = hipEventRecord(aux->join, aux->s);
-      if (e != hipSuccess) return e;
-      select();
-      attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
-      e = hipStreamWaitEvent(st, aux->join, 0);
-      if (e != hipSuccess) return e;
-    } else {
-      if (a.n_ret > 0) select();
-      if (n_win_units > 0) attend("dec_attn_window", 0, n_win_units, st);
-      if (n_ret_units > 0) attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
-    }
+  if (n_win_units > 0 && n_ret_units > 0) {
+    AuxFork fork(st);
+    if ((e = fork.status()) != hipSuccess) return e;
+    attend("dec_attn_window", 0, n_win_units, fork.stream());
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    select();
+    attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = fork.join()) != hipSuccess) return e;
+  } else {
+    if (a.n_ret > 0) select();
+    if (n_win_units > 0) attend("dec_attn_window", 0, n_win_units, st);
+    if (n_ret_units > 0) attend("dec_attn_retrieval", n_win_units, n_ret_units, st);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -125,6 +125,17 @@ def test_prefill_1m_all_sparse_sampled(gpu_lib):
     sampled_check(gpu_lib, w, _qbs(n_b, 2, 3), heads=heads)
 
 
+def test_prefill_past_the_stream_fork_threshold(gpu_lib):
+    # beyond 4096 blocks the window heads run on the auxiliary stream while
+    # the indexer runs; ragged, two KV groups, one retrieval head
+    from workloads import PrefillWorkload
+    w = PrefillWorkload("fork_threshold", S=64 * 4100 + 7, Hq=4, Hkv=2, d=128,
+                        n_ret=1, window=300, r=16, block=64, top_k=8,
+                        retrieval_heads=(1,))
+    n_b = w.n_blocks
+    sampled_check(gpu_lib, w, [0, 1, 2047, 4095, 4096, n_b - 2, n_b - 1])
+
+
 def test_decode_32x256k_sampled_sequences(gpu_lib):
     w = DECODE_32x256K
     print(f"[full-size] {w.name}", flush=True)
