@@ -39,8 +39,12 @@
  *    stream). The library allocates no device memory: scratch space comes
  *    from the caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned),
  *    sized by the matching *_workspace_bytes query. Calls never synchronise.
- *    (rtp_hybrid_attn_decode also uses a library-owned auxiliary stream;
- *    see there.)
+ *    Some calls also run part of their work on a library-owned auxiliary
+ *    stream of the device (default priority, created on first use):
+ *    rtp_hybrid_attn_decode, and the prefills on sequences of more than
+ *    4096 blocks. Events order that work after what was enqueued on
+ *    `stream` before the call, and the rest of the call after it, so each
+ *    call stays ordered on `stream` as a whole.
  *  - Arguments are validated on the host before anything is enqueued. On an
  *    error nothing is launched, outputs are untouched, and a negative status
  *    is returned; rtp_last_error() gives a thread-local message.
