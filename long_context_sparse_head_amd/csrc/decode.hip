@@ -171,8 +171,13 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     int32_t* __restrict__ sel_cnt) {
   __shared__ uint32_t keys[TK_LDS + TK_LDS / 32];
   __shared__ float qt[kD];
-  __shared__ TopkShared sh;
-  __shared__ WaveTopkShared wsh;
+  // the two selection workspaces are never used by the same call
+  __shared__ union {
+    TopkShared block;
+    WaveTopkShared wave;
+  } tsh;
+  TopkShared& sh = tsh.block;
+  WaveTopkShared& wsh = tsh.wave;
   const int rho = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = cache_len[b];
   L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);

@@ -314,13 +314,14 @@ __global__ __launch_bounds__(256) void topk_kernel(
   // 1 <= top_k < n_c
   const bool in_lds = n_c <= TK_LDS;
   if (in_lds) {
-    // eight loads per thread in flight
-    for (int e0 = tid; e0 < n_c; e0 += 8 * 256) {
-      float v[8];
+    // sixteen loads per thread in flight: a row of up to 4096 candidates
+    // costs one memory round trip
+    for (int e0 = tid; e0 < n_c; e0 += 16 * 256) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = row[min(e0 + 256 * u, n_c - 1)];
+      for (int u = 0; u < 16; ++u) v[u] = row[min(e0 + 256 * u, n_c - 1)];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int e = e0 + 256 * u;
         if (e < n_c) keys[e + (e >> 5)] = order_key(v[u]);
       }
@@ -347,10 +348,11 @@ __global__ __launch_bounds__(256) void topk_kernel(
       if (key < res.T) below = max(below, key);
     }
     below = block_max_u32(below, sh.tmp);
+    const int count_ge = res.count_ge;
     if (tid == 0) {
       kth[row_id * 2 + 0] = order_key_inv(res.T);
-      kth[row_id * 2 + 1] = res.count_ge >= top_k + 1 ? order_key_inv(res.T)
-                                                      : order_key_inv(below);
+      kth[row_id * 2 + 1] = count_ge >= top_k + 1 ? order_key_inv(res.T)
+                                                  : order_key_inv(below);
     }
   }
 }

@@ -303,9 +303,10 @@ __device__ uint32_t wave_kth(Key key, int m, int kk, int* hist) {
 }
 
 // Hands the k largest of key(i), i < m (1 <= k <= m; ties: lower i first)
-// to emit(p, i, key) with p = 0..k-1 in ascending i. One wave.
+// to emit(p, i, key) with p = 0..k-1 in ascending i, and returns the k-th
+// largest key. One wave.
 template <class Key, class Emit>
-__device__ void wave_take(Key key, int m, int k, Emit emit, int* hist) {
+__device__ uint32_t wave_take(Key key, int m, int k, Emit emit, int* hist) {
   const int lane = threadIdx.x & 63;
   const uint32_t T = wave_kth(key, m, k, hist);
   int gt = 0;
@@ -326,24 +327,31 @@ __device__ void wave_take(Key key, int m, int k, Emit emit, int* hist) {
     pos += __builtin_popcountll(bt);
     eq_seen += __builtin_popcountll(beq);
   }
+  return T;
 }
 
+// The per-wave selection suits small budgets over a few thousand keys (the
+// decode block choice): its first radix pass bins on the top key bits, where
+// scores of one row crowd into a few bins, so its LDS atomics serialise as
+// rows and budgets grow. Prefill rows use the block-wide select above.
 constexpr int kWaveTopkMax = 64;
 
 struct WaveTopkShared {
   int hist[4][256];
   uint32_t ckey[4 * kWaveTopkMax];
   int cidx[4 * kWaveTopkMax];
+  uint32_t T;
 };
 
 // Requires 1 <= k <= kWaveTopkMax and k < n; 256 threads. Writes out[0..k)
-// = idx_base + chosen e, ascending (ties: lower e first). The four waves
-// take consecutive quarters of [0, n); every member of the final top k is
-// in its quarter's top k, and the survivors are stored in quarter order,
-// i.e. in ascending e, so the last selection keeps the tie order.
+// = idx_base + chosen e, ascending (ties: lower e first), and returns the
+// k-th largest key (block-uniform). The four waves take consecutive
+// quarters of [0, n); every member of the final top k is in its quarter's
+// top k, and the survivors are stored in quarter order, i.e. in ascending
+// e, so the last selection keeps the tie order.
 template <class GetK>
-__device__ void wave_topk(GetK getk, int n, int k, int32_t* out, int idx_base,
-                          WaveTopkShared& sh) {
+__device__ uint32_t wave_topk(GetK getk, int n, int k, int32_t* out,
+                              int idx_base, WaveTopkShared& sh) {
   const int wave = threadIdx.x >> 6;
   const int C = (n + 3) / 4;
   auto kw_of = [&](int w) {
@@ -363,11 +371,14 @@ __device__ void wave_topk(GetK getk, int n, int k, int32_t* out, int idx_base,
   __syncthreads();
   if (wave == 0) {
     const int M = kw_of(0) + kw_of(1) + kw_of(2) + kw_of(3);
-    wave_take([&](int i) { return sh.ckey[i]; }, M, k,
-              [&](int p, int i, uint32_t) { out[p] = idx_base + sh.cidx[i]; },
-              sh.hist[0]);
+    const uint32_t T = wave_take(
+        [&](int i) { return sh.ckey[i]; }, M, k,
+        [&](int p, int i, uint32_t) { out[p] = idx_base + sh.cidx[i]; },
+        sh.hist[0]);
+    if ((threadIdx.x & 63) == 0) sh.T = T;
   }
   __syncthreads();
+  return sh.T;
 }
 
 }  // namespace rtp

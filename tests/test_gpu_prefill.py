@@ -218,19 +218,25 @@ def test_identity_projection_selects_true_top_blocks(gpu_lib):
     full_check(gpu_lib, x, "identity")
 
 
-def test_indexer_select_kth_scores_and_centroids(gpu_lib):
-    S = 4096
-    x = make_prefill(_wl(S, Hq=8, Hkv=2, ret=(0, 3, 6), window=64, top_k=9,
-                         seed=11))
+@pytest.mark.parametrize("S,top_k", [(4096, 9), (64 * 700, 300)])
+def test_indexer_select_kth_scores_and_centroids(gpu_lib, S, top_k):
+    # a small and a large budget; both report the k-th and (k+1)-th scores
+    x = make_prefill(_wl(S, Hq=8, Hkv=2, ret=(0, 3, 6), window=64,
+                         top_k=top_k, seed=11))
     d = _to_dev(x)
     sel, cnt, kth, cent = gpu_lib.indexer_select(
-        d["q"], d["k"], x["is_retrieval"], d["p_q_t"], d["p_k_t"], 9,
+        d["q"], d["k"], x["is_retrieval"], d["p_q_t"], d["p_k_t"], top_k,
         kth=True, centroids=True)
     torch.cuda.synchronize()
     ora_sel = oracle.hybrid_prefill(*_bits(x), x["is_retrieval"], 64,
-                                    x["p_q"], x["p_k"], 64, 9, heads=[0, 3, 6],
-                                    query_blocks=[0],
+                                    x["p_q"], x["p_k"], 64, top_k,
+                                    heads=[0, 3, 6], query_blocks=[0],
                                     sel_rows=range(S // 64))
+    for rho, h in enumerate((0, 3, 6)):
+        fn = parity.prefill_rows_fn(x, *_bits(x)[:2], rho, h)
+        parity.compare_selection(sel.cpu().numpy()[rho], cnt.cpu().numpy()[rho],
+                                 ora_sel["sel"][rho], ora_sel["sel_count"][rho],
+                                 ora_sel["kth"][rho], fn, f"kth rho={rho}")
     k_g, k_o = kth.cpu().numpy(), ora_sel["kth"]
     both = ~np.isnan(k_o)
     assert np.array_equal(np.isnan(k_g), np.isnan(k_o))
