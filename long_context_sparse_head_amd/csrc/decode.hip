@@ -11,7 +11,7 @@
 // n_recent blocks are attended exactly.
 //
 // Decode is bound by HBM bandwidth: every key/value byte is read once. The
-// window heads of one KV group share one pass over the window (up to 8 heads
+// window heads of one KV group share one pass over the window (up to 32 heads
 // per pass, GQA), retrieval heads gather their own blocks, and the keys of a
 // (sequence, unit) are split over many workgroups whose partial softmax
 // states are merged by log-sum-exp.
@@ -20,7 +20,10 @@
 
 namespace rtp {
 
-constexpr int kDecMaxUnitHeads = 8;
+// Heads of one KV group that share a pass over its window: the N dimension
+// of the MFMA tiles (32), so a group of up to 32 window heads reads its K/V
+// once.
+constexpr int kDecMaxUnitHeads = 32;
 
 // ---------------------------------------------------------------- centroids
 struct CentArgs {
@@ -322,7 +325,7 @@ constexpr int kDecTile = 32 * kD * 2;
 // grid (n_split, n_units, B), 256 threads. Each wave takes 32-key tiles in
 // turn (tiles wave, wave + 4, ...), independently of the other waves until
 // the final merge. Both products run on MFMA with the unit's heads along N
-// (so up to 8 heads share every K/V byte): S^T = K Q^T with K rows read in
+// (so up to 32 heads share every K/V byte): S^T = K Q^T with K rows read in
 // perm_row order, which makes the accumulator of S^T the B operand of
 // O^T += V^T P; that product wants 8 consecutive keys of one d per lane, so V
 // is read transposed from LDS. The next tile's K and V are loaded into
@@ -536,9 +539,10 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
   }
 
   // wave-level totals: l over the lane pair; O^T columns of the unit's heads
-  // go to this wave's own (now idle) V tile
+  // go to this wave's own (now idle) K and V tiles (16 KiB: 32 heads x 128 d)
   l_run += __shfl_xor(l_run, 32);
   float* const red_o = reinterpret_cast<float*>(ktile);  // [head][d]
+  static_assert(kDecMaxUnitHeads * kD * 4 <= 2 * kDecTile, "fits the tiles");
   if (n < nh) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)

@@ -119,11 +119,13 @@ def test_decode_window_one_returns_last_value(gpu_lib):
             assert torch.equal(out[b, h], y["v_cache"][b, 0, L - 1])
 
 
-def test_decode_many_heads_per_group(gpu_lib):
-    # 16 window heads share one KV head: two passes of 8 heads
-    y = make_decode(_wl(2, 3000, Hq=16, Hkv=1, ret=(3,), window=700,
+@pytest.mark.parametrize("Hq", [16, 40])
+def test_decode_many_heads_per_group(gpu_lib, Hq):
+    # one KV head for all heads: 15 window heads share one pass over the
+    # window; 39 need two (32 + 7)
+    y = make_decode(_wl(2, 3000, Hq=Hq, Hkv=1, ret=(3,), window=700,
                         top_k=4), cache_len=[3000, 1800])
-    check(gpu_lib, y, "gqa16")
+    check(gpu_lib, y, f"gqa{Hq}")
 
 
 def test_decode_runs_after_earlier_work_on_the_callers_stream(gpu_lib):
