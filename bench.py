@@ -371,7 +371,8 @@ def main():
                     help="time the 128K prefill only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense", "full"],
+    ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense", "full",
+                                      "dense1m"],
                     help="run only this secondary leg and print its detail "
                          "(for profiling); no bench line")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -396,9 +397,10 @@ def main():
                                args.warmup)
         else:
             w = {"1m": PREFILL_1M, "32k": PREFILL_32K,
-                 "dense": PREFILL_128K, "full": PREFILL_128K}[args.leg]
+                 "dense": PREFILL_128K, "full": PREFILL_128K,
+                 "dense1m": PREFILL_1M}[args.leg]
             res = bench_prefill(rtp, torch, w, args.steps, args.warmup,
-                                dense=args.leg == "dense",
+                                dense=args.leg in ("dense", "dense1m"),
                                 full=args.leg == "full")
         print(json.dumps({"leg": args.leg, **res}), flush=True)
         return
@@ -425,6 +427,22 @@ def main():
             f"ms/step")
         extra["speedup_vs_dense_128k"] = (extra["dense_128k"]["ms_per_step"] /
                                           main["ms_per_step"])
+        # the pages' comparison (full attention vs the hybrid, 32K to 1M):
+        # the same dense engine at 32K and, for one step, at 1M
+        extra["dense_32k"] = bench_prefill(rtp, torch, PREFILL_32K,
+                                           max(2, args.steps // 2), 1,
+                                           dense=True)
+        extra["speedup_vs_dense_32k"] = (extra["dense_32k"]["ms_per_step"] /
+                                         extra["prefill_32k"]["ms_per_step"])
+        extra["dense_1m"] = bench_prefill(rtp, torch, PREFILL_1M, 1, 0,
+                                          dense=True)
+        extra["speedup_vs_dense_1m"] = (extra["dense_1m"]["ms_per_step"] /
+                                        extra["prefill_1m"]["ms_per_step"])
+        log(f"[bench] dense 32K: {extra['dense_32k']['ms_per_step']:.2f} ms, "
+            f"dense 1M: {extra['dense_1m']['ms_per_step']:.0f} ms; hybrid "
+            f"speedup {extra['speedup_vs_dense_32k']:.2f}x (32K), "
+            f"{extra['speedup_vs_dense_128k']:.2f}x (128K), "
+            f"{extra['speedup_vs_dense_1m']:.2f}x (1M)")
         extra["full_retrieval_128k"] = bench_prefill(
             rtp, torch, PREFILL_128K, max(2, args.steps // 2), 1, full=True)
         log(f"[bench] 128K with full retrieval heads: "
