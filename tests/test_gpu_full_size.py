@@ -136,6 +136,31 @@ def test_prefill_past_the_stream_fork_threshold(gpu_lib):
     sampled_check(gpu_lib, w, [0, 1, 2047, 4095, 4096, n_b - 2, n_b - 1])
 
 
+def test_forked_prefill_runs_after_earlier_work_on_the_callers_stream(gpu_lib):
+    # Past 4096 blocks the window heads run on the library's auxiliary
+    # stream. V = 1 is produced by a kernel on a side stream right before
+    # the call on that stream: every output is exactly 1 only if all heads
+    # waited for it, and the next kernel on the stream sees the outputs.
+    from workloads import PrefillWorkload
+    w = PrefillWorkload("fork_order", S=64 * 4097 + 3, Hq=4, Hkv=2, d=128,
+                        n_ret=1, window=256, r=16, block=64, top_k=4,
+                        retrieval_heads=(2,))
+    x = make_prefill(w, device="cuda")
+    pq = torch.from_numpy(x["p_q"]).cuda()
+    pk = torch.from_numpy(x["p_k"]).cuda()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            v1 = torch.empty_like(x["k"])
+            v1.copy_(x["k"]).mul_(0).add_(1)
+            out = gpu_lib.hybrid_attn_prefill(x["q"], x["k"], v1,
+                                              x["is_retrieval"], w.window, pq,
+                                              pk, w.top_k)
+            bad = (out != 1).sum()
+            assert int(bad.item()) == 0
+
+
 def test_decode_32x256k_sampled_sequences(gpu_lib):
     w = DECODE_32x256K
     print(f"[full-size] {w.name}", flush=True)
