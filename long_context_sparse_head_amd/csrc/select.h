@@ -199,24 +199,43 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
     T = radix_kth(getk, [&](int e) { return bin(getk(e)) == bstar; }, n, kk,
                   sh);
   }
-  // take every key above T and the first (by index) keys equal to T
+  // take every key above T and the first (by index) keys equal to T: one
+  // scan of the packed counts (greater in the low half, equal in the high
+  // half; a row has fewer than 2^16 keys). Equal keys are taken in index
+  // order, so those taken before thread t number min(equal before t, keq).
   int ngt = 0, neq = 0;
   for (int e = e0; e < e1; ++e) {
     const uint32_t x = getk(e);
     ngt += x > T;
     neq += x == T;
   }
-  const int gt_incl = block_incl_scan(ngt, sh.tmp);
-  if (tid == 255) sh.bcast[3] = gt_incl;
-  __syncthreads();
-  const int keq = k - sh.bcast[3];  // keys equal to T to take
-  const int eq_incl = block_incl_scan(neq, sh.tmp);
-  const int take_eq = max(0, min(keq - (eq_incl - neq), neq));
-  const int ntake = ngt + take_eq;
-  const int pos_incl = block_incl_scan(ntake, sh.tmp);
-  const int ge_incl = block_incl_scan(ngt + neq, sh.tmp);
-  if (tid == 255) sh.bcast[2] = ge_incl;
-  int pos = pos_incl - ntake;
+  int gt_before, eq_before, tot_gt, tot_eq;
+  if (n < 65536) {
+    const int both = ngt | (neq << 16);
+    const int incl = block_incl_scan(both, sh.tmp);
+    if (tid == 255) sh.bcast[3] = incl;
+    __syncthreads();
+    tot_gt = sh.bcast[3] & 0xffff;
+    tot_eq = sh.bcast[3] >> 16;
+    const int excl = incl - both;
+    gt_before = excl & 0xffff;
+    eq_before = excl >> 16;
+  } else {  // longer rows: one scan per count
+    const int gi = block_incl_scan(ngt, sh.tmp);
+    const int ei = block_incl_scan(neq, sh.tmp);
+    if (tid == 255) {
+      sh.bcast[3] = gi;
+      sh.bcast[2] = ei;
+    }
+    __syncthreads();
+    tot_gt = sh.bcast[3];
+    tot_eq = sh.bcast[2];
+    gt_before = gi - ngt;
+    eq_before = ei - neq;
+  }
+  const int keq = k - tot_gt;  // keys equal to T to take
+  const int take_eq = max(0, min(keq - eq_before, neq));
+  int pos = gt_before + min(eq_before, keq);
   int eq_seen = 0;
   for (int e = e0; e < e1; ++e) {
     const uint32_t x = getk(e);
@@ -230,7 +249,7 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
   __syncthreads();
   TopkResult res;
   res.T = T;
-  res.count_ge = sh.bcast[2];
+  res.count_ge = tot_gt + tot_eq;
   return res;
 }
 
