@@ -43,9 +43,9 @@ METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA p
 TRAFFIC = {
     "kernel": "attn_window_kernel",
     "source": "long_context_sparse_head_amd/csrc/attn.hip",
-    "sha256": "34d52e3b0c999161f0ace3d96d3fb0507c5626bafb38565078ff863a5add3ef2",
-    "fetch_bytes": 2937455969,
-    "write_bytes": 906052486,
+    "sha256": "50d2602969755c6ac8f08f195eb4df428077c5c776e4c956d0a4d728d9e7891d",
+    "fetch_bytes": 2934929590,
+    "write_bytes": 906052218,
 }
 
 
