@@ -286,6 +286,8 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     return in_lds ? keys[e + (e >> 5)] : order_key(srow[e]);
   };
   if (a.top_k > kWaveTopkMax) radix_topk(getk, n_c, a.top_k, out + 1, 1, sh);
+  else if (a.top_k > 0 && n_c <= 4 * 64 * 16)
+    wave_topk_regs<16>(getk, n_c, a.top_k, out + 1, 1, wsh);
   else if (a.top_k > 0) wave_topk(getk, n_c, a.top_k, out + 1, 1, wsh);
   const int n_rec = n_b - 1 - n_c;  // = n_recent here
   if (tid == 0) {

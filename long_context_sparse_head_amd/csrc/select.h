@@ -400,4 +400,132 @@ __device__ uint32_t wave_topk(GetK getk, int n, int k, int32_t* out,
   return sh.T;
 }
 
+// The same selection with each lane's keys held in registers (NPL per lane
+// and wave, so n <= 4 * 64 * NPL): every radix pass and the collection then
+// read registers, and only the histogram atomics touch LDS. Same contract
+// and result as wave_topk.
+template <int NPL>
+__device__ uint32_t wave_kth_regs(const uint32_t (&kr)[NPL], int m, int kk,
+                                  int* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane + 64 * j] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      if (i < m && (kr[j] & pmask) == prefix)
+        atomicAdd(&hist[(kr[j] >> shift) & 255], 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    int h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = hist[255 - 4 * lane - j];
+      sum += h[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int incl = wave_incl_scan(sum);
+    const int excl = incl - sum;
+    const bool mine = excl < kk && kk <= incl;  // exactly one lane
+    int bin = 0, above = excl;
+    if (mine) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above + h[j] >= kk) {
+          bin = 255 - 4 * lane - j;
+          break;
+        }
+        above += h[j];
+      }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(mine));
+    bin = __shfl(bin, src);
+    above = __shfl(above, src);
+    prefix |= (uint32_t)bin << shift;
+    pmask |= 0xffu << shift;
+    kk -= above;
+  }
+  return prefix;
+}
+
+// key i = lane + 64 j of the wave's range sits in kr[j] (i < m valid)
+template <int NPL, class Emit>
+__device__ uint32_t wave_take_regs(const uint32_t (&kr)[NPL], int m, int k,
+                                   Emit emit, int* hist) {
+  const uint32_t T = wave_kth_regs<NPL>(kr, m, k, hist);
+  const int lane = threadIdx.x & 63;
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) gt += (lane + 64 * j < m) && kr[j] > T;
+  gt = __shfl(wave_incl_scan(gt), 63);
+  const int take_eq = k - gt;
+  const uint64_t below = lanes_below();
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int i = lane + 64 * j;
+    const bool valid = i < m;
+    const bool is_gt = valid && kr[j] > T, is_eq = valid && kr[j] == T;
+    const uint64_t beq = __ballot(is_eq);
+    const bool t =
+        is_gt || (is_eq && eq_seen + __builtin_popcountll(beq & below) < take_eq);
+    const uint64_t bt = __ballot(t);
+    if (t) emit(pos + __builtin_popcountll(bt & below), i, kr[j]);
+    pos += __builtin_popcountll(bt);
+    eq_seen += __builtin_popcountll(beq);
+  }
+  return T;
+}
+
+// wave_topk for n <= 4 * 64 * NPL, with register-held keys
+template <int NPL, class GetK>
+__device__ uint32_t wave_topk_regs(GetK getk, int n, int k, int32_t* out,
+                                   int idx_base, WaveTopkShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int C = (n + 3) / 4;
+  auto kw_of = [&](int w) {
+    return min(k, max(0, min(n, (w + 1) * C) - w * C));
+  };
+  const int lo = min(wave * C, n), m = min(n, lo + C) - lo;
+  int off = 0;
+  for (int w = 0; w < wave; ++w) off += kw_of(w);
+  const int kw = kw_of(wave);
+  if (kw > 0) {
+    uint32_t kr[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      kr[j] = i < m ? getk(lo + i) : 0u;
+    }
+    wave_take_regs<NPL>(kr, m, kw,
+                        [&](int p, int i, uint32_t x) {
+                          sh.ckey[off + p] = x;
+                          sh.cidx[off + p] = lo + i;
+                        },
+                        sh.hist[wave]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int NS = (4 * kWaveTopkMax + 63) / 64;
+    const int M = kw_of(0) + kw_of(1) + kw_of(2) + kw_of(3);
+    uint32_t kr[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int i = lane + 64 * j;
+      kr[j] = i < M ? sh.ckey[i] : 0u;
+    }
+    const uint32_t T = wave_take_regs<NS>(
+        kr, M, k,
+        [&](int p, int i, uint32_t) { out[p] = idx_base + sh.cidx[i]; },
+        sh.hist[0]);
+    if (lane == 0) sh.T = T;
+  }
+  __syncthreads();
+  return sh.T;
+}
+
 }  // namespace rtp
