@@ -33,8 +33,9 @@
 //
 // Window kernel: 4 waves = 4 (head, query block) jobs of one KV group share
 // one stream of 64-key tiles, staged by direct global->LDS loads
-// (global_load_lds_dwordx4) into a 3-deep LDS ring of padded rows. Each XCD
-// takes a contiguous, equal share of all KV groups' work items.
+// (global_load_lds_dwordx4) into a 3-deep LDS ring of padded rows; a tile's
+// loads are dealt one per MFMA group of a step, not issued in one burst. Each
+// XCD takes a contiguous, equal share of all KV groups' work items.
 //
 // Sparse kernel: each wave runs its own (retrieval head, query block) job over
 // its block list in 32-key half tiles: K goes straight into registers in MFMA
@@ -286,16 +287,40 @@ __device__ __attribute__((noinline)) void win_issue_ragged_k(
   dma16(p.k + ((size_t)g * p.S + key) * kD + c * 8, stage + ld * 1024);
 }
 
-// Loads j = 0..3 of every wave are K rows, load 4 is K for wave 0 and V^T
-// for the others, loads 5..8 are V^T (wave 3 has no load 8). kt/vt: the
-// tile's first byte of K and of V^T.
+// First byte of a tile's K rows and of its V^T block.
+__device__ __forceinline__ void win_tile_src(const WinParams& p, int g, int kb,
+                                             const char*& kt, const char*& vt) {
+  kt = reinterpret_cast<const char*>(p.k) +
+       ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
+  vt = reinterpret_cast<const char*>(p.vt + ((size_t)g * p.n_b + kb) * 64 * kD);
+}
+
+// Load j (0..8) of this wave for a full tile: loads 0..3 are K rows, load 4 is
+// K for wave 0 and V^T for the others, loads 5..8 are V^T. The stage has only
+// 35 loads, so wave 3 repeats its load 7 as load 8 (same bytes, same place),
+// which keeps the issue free of branches.
+__device__ __forceinline__ void win_issue_one(const char* kt, const char* vt,
+                                              char* stage,
+                                              const WinLaneOffsets& o,
+                                              int wave, int j) {
+  if (j < 4) {
+    dma16(kt + o.off[j], stage + wave * 1024 + j * 4096);
+  } else if (j == 4) {
+    dma16((wave == 0 ? kt : vt) + o.off[4], stage + wave * 1024 + 4 * 4096);
+  } else if (j < 8) {
+    dma16(vt + o.off[j], stage + wave * 1024 + j * 4096);
+  } else {
+    const int jj = wave < 3 ? 8 : 7;
+    dma16(vt + o.off[jj], stage + wave * 1024 + jj * 4096);
+  }
+}
+
+// All loads of this wave for tile kb, back to back.
 __device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
                                           char* stage, const WinLaneOffsets& o,
                                           int wave, int lane) {
-  const char* kt = reinterpret_cast<const char*>(p.k) +
-                   ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
-  const char* vt = reinterpret_cast<const char*>(
-      p.vt + ((size_t)g * p.n_b + kb) * 64 * kD);
+  const char *kt, *vt;
+  win_tile_src(p, g, kb, kt, vt);
   if ((kb + 1) * 64 > p.S) {  // last block of a ragged S: rows past S
 #pragma unroll 1                // re-read row S-1 (masked anyway)
     for (int j = 0; j < DMA_PER_WAVE; ++j) {
@@ -305,13 +330,8 @@ __device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
     }
     return;
   }
-  char* dst = stage + wave * 1024;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma16(kt + o.off[j], dst + j * 4096);
-  dma16((wave == 0 ? kt : vt) + o.off[4], dst + 4 * 4096);
-#pragma unroll
-  for (int j = 5; j < 8; ++j) dma16(vt + o.off[j], dst + j * 4096);
-  if (wave < 3) dma16(vt + o.off[8], dst + 8 * 4096);
+  for (int j = 0; j < DMA_PER_WAVE; ++j) win_issue_one(kt, vt, stage, o, wave, j);
 }
 
 // S^T for one 32-key sub-tile st of a staged tile: s[0][j], j = query tile
@@ -407,10 +427,13 @@ __device__ __forceinline__ void diag_refs(const u16* kbase, int S, int q0,
 // one (V^T operand vop(h, mt)) are issued in groups of 4, next to the
 // exp/pack work of the current scores s and the operand reads of the next
 // group. sched_barrier keeps the compiler from regrouping them (it otherwise
-// issues all QK MFMAs, then all exps, then all P.V MFMAs). Returns whether a
-// row sum left the safe range.
-template <class KOp, class VOp>
-__device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
+// issues all QK MFMAs, then all exps, then all P.V MFMAs). dop(i), i = 0..8,
+// runs at the head of group i: the caller's staging loads for a later tile go
+// there, one per group, because a burst of them stalls the wave's issue for
+// several hundred cycles while spread out they hide behind the MFMAs. Returns
+// whether a row sum left the safe range.
+template <class KOp, class VOp, class DOp>
+__device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
                                           const bf16x8 (&qf)[2][8],
                                           const f32x16 (&s)[1][2],
                                           f32x16 (&sn)[1][2], Soft& sf,
@@ -449,11 +472,13 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   //   g8      PV h1 j1
   // Group 0 has no MFMA of its own: the previous step's last ones drain
   // while it runs.
+  dop(0);
   bf16x8 ka = kop(0), kb = kop(1);
   expq(0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 1; q < 4; ++q) {
+    dop(q);
     const bf16x8 kc = kop(2 * q), kd = kop(2 * q + 1);
     sn[0][0] = mfma32(ka, qf[0][2 * q - 2], sn[0][0]);
     sn[0][1] = mfma32(ka, qf[1][2 * q - 2], sn[0][1]);
@@ -465,6 +490,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
     __builtin_amdgcn_sched_barrier(0);
   }
   // g4
+  dop(4);
   bf16x8 va = vop(0, 0), vb = vop(0, 1);
   sn[0][0] = mfma32(ka, qf[0][6], sn[0][0]);
   sn[0][1] = mfma32(ka, qf[1][6], sn[0][1]);
@@ -473,6 +499,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   expq(0, 1, 0);
   __builtin_amdgcn_sched_barrier(0);
   // g5
+  dop(5);
   const bf16x8 vc = vop(0, 2), vd = vop(0, 3);
   {
     const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
@@ -484,6 +511,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   expq(0, 1, 2);
   __builtin_amdgcn_sched_barrier(0);
   // g6
+  dop(6);
   const bf16x8 v10 = vop(1, 0), v11 = vop(1, 1), v12 = vop(1, 2),
                v13 = vop(1, 3);
   {
@@ -496,6 +524,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   expq(1, 1, 0);
   __builtin_amdgcn_sched_barrier(0);
   // g7
+  dop(7);
   {
     const bf16x8 p = pb(0, 1);
     acc[0][0] = mfma32(v10, p, acc[0][0]);
@@ -506,6 +535,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
   expq(1, 1, 2);
   __builtin_amdgcn_sched_barrier(0);
   // g8
+  dop(8);
   {
     const bf16x8 p = pb(1, 1);
     acc[1][0] = mfma32(v10, p, acc[1][0]);
@@ -520,13 +550,14 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop,
 
 // The window kernel's step: K rows of stage kst (half kh) and V^T rows of
 // stage vst (half vh), both from the padded LDS tile.
+template <class DOp>
 __device__ __forceinline__ bool win_step(const char* kst, int kh,
                                          const char* vst, int vh,
                                          const bf16x8 (&qf)[2][8],
                                          const f32x16 (&s)[1][2],
                                          f32x16 (&sn)[1][2], Soft& sf,
                                          f32x16 (&acc)[2][4], float c,
-                                         int lane) {
+                                         int lane, DOp dop) {
   const int g = lane >> 5, n = lane & 31;
   const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
   const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
@@ -536,7 +567,7 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
         return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B +
                                                 32 * h);
       },
-      qf, s, sn, sf, acc, c);
+      dop, qf, s, sn, sf, acc, c);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) {
@@ -614,18 +645,29 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
         win_pv(cur, 0, pb, acc, lane);
         mask(sb, kb * 64 + 32);
       } else {
-        over |= win_step(cur, 1, cur, 0, qf, sa, sb, sf, acc, p.c, lane);
+        over |= win_step(cur, 1, cur, 0, qf, sa, sb, sf, acc, p.c, lane,
+                         [](int) {});
       }
       wait_vm_all();
       __syncthreads();  // tile t+1 resident; spare (tile t-1) free
-      if (t + 2 < nt) win_issue(p, g, kb - 2, spare, off, wave, lane);
+      const bool pf = t + 2 < nt;
       if constexpr (M) {
+        if (pf) win_issue(p, g, kb - 2, spare, off, wave, lane);
         win_qk(nxt, 0, qf, sa, lane);
         over |= softmax_step<1>(sb, sf, pb, p.c);
         win_pv(cur, 1, pb, acc, lane);
         mask(sa, (kb - 1) * 64);
       } else {
-        over |= win_step(nxt, 0, cur, 1, qf, sb, sa, sf, acc, p.c, lane);
+        // Tile t+2's loads ride along with this step's MFMA groups, one per
+        // group (a prefetched tile is below the top one, so never ragged).
+        // Past the last tile they re-read tile t into the spare stage, which
+        // is then never read, so the issue needs no branch.
+        const char *kt, *vt;
+        win_tile_src(p, g, pf ? kb - 2 : kb, kt, vt);
+        over |= win_step(nxt, 0, cur, 1, qf, sb, sa, sf, acc, p.c, lane,
+                         [&](int j) {
+                           win_issue_one(kt, vt, spare, off, wave, j);
+                         });
       }
       char* const done = cur;
       cur = nxt;
@@ -648,6 +690,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     mask(sb, kt_lo * 64 + 32);
     over |= softmax_step<1>(sb, sf, pb, p.c);
     win_pv(cur, 1, pb, acc, lane);
+    wait_vm_all();  // no load may still be writing the ring
     if (attempt > 0) break;  // exact references: nothing can overflow
     if (__any(over)) over_flag = 1;
     __syncthreads();  // also: every wave is done with the LDS ring
@@ -873,7 +916,8 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     auto step = [&](int t, char* kslot, f32x16 (&sc)[1][2],
                     f32x16 (&sn)[1][2]) {
       wait_vm24();  // K(t+1) and V^T(t) resident
-      over |= attn_step(kop_at(kslot), vop_at(vcur), qf, sc, sn, sf, acc, p.c);
+      over |= attn_step(kop_at(kslot), vop_at(vcur), [](int) {}, qf, sc, sn,
+                        sf, acc, p.c);
       const int k0f = tile_k0(t + 3);
       wait_lgkm0();  // this wave's reads of both slots are done
       sp_issue_k(kbase, S, k0f, koffs, kslot, lane);
