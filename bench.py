@@ -39,23 +39,33 @@ METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA p
 #   bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-gib 1
 # each divided by what the same counter reads per byte of the run's 1 GiB
 # plain device copy. Valid only for the kernel source it was measured on
-# (sha256 below); after any change to it the figure is reported as null.
+# (sha256 of the sources below, build flags included); after any change to
+# them the figure is reported as null.
 TRAFFIC = {
     "kernel": "attn_window_kernel",
-    "source": "long_context_sparse_head_amd/csrc/attn.hip",
-    "sha256": "50d2602969755c6ac8f08f195eb4df428077c5c776e4c956d0a4d728d9e7891d",
-    "fetch_bytes": 2934929590,
-    "write_bytes": 906052218,
+    "sources": ["long_context_sparse_head_amd/csrc/attn_window.hip",
+                "long_context_sparse_head_amd/csrc/attn_core.h",
+                "long_context_sparse_head_amd/build.py"],
+    "sha256": None,
+    "fetch_bytes": None,
+    "write_bytes": None,
 }
 
 
-def measured_traffic():
+def traffic_sources_sha256():
     import hashlib
+    h = hashlib.sha256()
+    for src in TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
     if TRAFFIC["sha256"] is None:
         return None
-    with open(os.path.join(ROOT, TRAFFIC["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["sha256"]:
-            return None
+    if traffic_sources_sha256() != TRAFFIC["sha256"]:
+        return None
     return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
 
 

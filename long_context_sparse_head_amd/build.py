@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "librtp.so")
-SOURCES = ["attn.hip", "indexer.hip", "decode.hip", "api.hip"]
+SOURCES = ["attn_window.hip", "attn.hip", "indexer.hip", "decode.hip",
+           "api.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 HIPFLAGS = [
@@ -24,6 +25,14 @@ HIPFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+
+# Per-file backend options. The window kernel's score accumulators should
+# live in VGPRs (the softmax reads every one of them) while its O accumulator
+# stays in AGPRs; asking the backend to prefer the VGPR form of MFMA results
+# gets that placement (the sparse kernel is faster without it).
+EXTRA_FLAGS = {
+    "attn_window.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -35,7 +44,8 @@ def hipcc() -> str:
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *HIPFLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+    cmd = [hipcc(), *HIPFLAGS, *EXTRA_FLAGS.get(src, []),
+           "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"

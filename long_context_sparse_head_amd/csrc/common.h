@@ -112,6 +112,10 @@ hipError_t launch_transpose_v(const u16* v, u16* vt, int Hkv, int S, int S_pad,
 // is_ret: host [Hq]; nullptr means every head is a window head. parts: 1 =
 // window heads only, 2 = retrieval heads only, 3 = both.
 constexpr int kAttnWindow = 1, kAttnSparse = 2, kAttnAll = 3;
+// The window / dense heads of a launch (attn_window.hip); launch_attention
+// calls it for the kAttnWindow part.
+hipError_t launch_window_heads(const AttnLaunch& a, const uint8_t* is_ret,
+                               hipStream_t st);
 hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
                             hipStream_t st, int parts = kAttnAll);
 
