@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     auto step = [&](int t, char* kslot, f32x16 (&sc)[1][2],
                     f32x16 (&sn)[1][2]) {
       wait_vm24();  // K(t+1) and V^T(t) resident
-      over |= attn_step(kop_at(kslot), vop_at(vcur), [](int) {}, qf, sc, sn,
+      over |= attn_step<false>(kop_at(kslot), vop_at(vcur), [](int) {}, qf, sc, sn,
                         sf, acc, p.c);
       const int k0f = tile_k0(t + 3);
       wait_lgkm0();  // this wave's reads of both slots are done

@@ -46,9 +46,26 @@ namespace rtp {
 // tile left that range (a score more than ~64 / c above m); if so (rare), a
 // max-only pass finds every row's true maximum and the job is recomputed
 // with it (then p <= 1). The O accumulator is touched only by MFMAs, which
-// keeps it resident in AGPRs with no per-tile rescale. Row sums use the
-// bf16-rounded p that also feeds the P.V MFMA.
+// keeps it resident in AGPRs with no per-tile rescale.
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
+
+// Row-sum update with one packed pair of p. F32: the two fp32 values, by
+// plain adds. Otherwise the bf16-rounded pair that feeds the P.V MFMA, by one
+// v_dot2_f32_bf16. Both give O / l within the bf16 rounding of p. On gfx950 a
+// dot2 waits for the MFMA in flight, so the window kernel, whose steps keep
+// the matrix pipe busy, uses the adds (2% faster at 128K); the sparse kernel
+// measures faster with dot2.
+template <bool F32>
+__device__ __forceinline__ float row_add(float acc, float p0, float p1,
+                                         uint32_t w) {
+  if constexpr (F32) {
+    return (acc + p0) + p1;
+  } else {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one,
+                                           acc, false);
+  }
+}
 
 struct Soft {
   float mref[2];
@@ -66,14 +83,12 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[NS][2], int j) {
   return fmaxf(m, __shfl_xor(m, 32));
 }
 
-// p = exp2(c s - c m) packed to bf16 (the B operand of P.V); ls = sum of the
-// packed values of this lane.
-
-template <int NS>
+// p = exp2(c s - c m) packed to bf16 (the B operand of P.V); ls = this
+// lane's sum of p (row_add<F32>).
+template <int NS, bool F32>
 __device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2],
                                          const Soft& sf, bf16x8 (&pb)[NS][2][2],
                                          float (&ls)[2], float c) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const float mc = sf.mref[j] * c;
@@ -89,8 +104,7 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2],
           const float p0 = fast_exp2(fmaf(s[u][j][i], c, -mc));
           const float p1 = fast_exp2(fmaf(s[u][j][i + 1], c, -mc));
           w[e] = pack_bf16x2(p0, p1);
-          acc = __builtin_amdgcn_fdot2_f32_bf16(
-              __builtin_bit_cast(bf16x2, w[e]), one, acc, false);
+          acc = row_add<F32>(acc, p0, p1, w[e]);
         }
         const uint4 q4 = make_uint4(w[0], w[1], w[2], w[3]);
         pb[u][j][h] = __builtin_bit_cast(bf16x8, q4);
@@ -103,12 +117,12 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[NS][2],
 // returns whether this lane's partial sum left the safe range. NaN (from NaN
 // inputs) does not count: raising the reference cannot remove it, so it just
 // propagates to the output.
-template <int NS>
+template <int NS, bool F32>
 __device__ __forceinline__ bool softmax_step(const f32x16 (&s)[NS][2],
                                              Soft& sf, bf16x8 (&pb)[NS][2][2],
                                              float c) {
   float ls[2];
-  exp_pack<NS>(s, sf, pb, ls, c);
+  exp_pack<NS, F32>(s, sf, pb, ls, c);
   sf.lsum[0] += ls[0];
   sf.lsum[1] += ls[1];
   return (ls[0] > kSumLimit) || (ls[1] > kSumLimit);
@@ -203,15 +217,14 @@ __device__ __forceinline__ void load_q(const u16* q, int head, int q0, int S,
 // issues all QK MFMAs, then all exps, then all P.V MFMAs). dop(i), i = 0..8,
 // runs at the head of group i: the caller's staging loads for a later tile go
 // there, one per group, because a burst of them stalls the wave's issue for
-// several hundred cycles while spread out they hide behind the MFMAs. Returns
-// whether a row sum left the safe range.
-template <class KOp, class VOp, class DOp>
+// several hundred cycles while spread out they hide behind the MFMAs. Row
+// sums use row_add<F32>. Returns whether a row sum left the safe range.
+template <bool F32, class KOp, class VOp, class DOp>
 __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
                                           const bf16x8 (&qf)[2][8],
                                           const f32x16 (&s)[1][2],
                                           f32x16 (&sn)[1][2], Soft& sf,
                                           f32x16 (&acc)[2][4], float c) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   const float mc[2] = {sf.mref[0] * c, sf.mref[1] * c};
   uint32_t w[2][2][4];  // packed P: [query tile j][key half h][pair]
   float ls[2] = {0.f, 0.f};
@@ -223,8 +236,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
       const float p0 = fast_exp2(fmaf(s[0][j][i], c, -mc[j]));
       const float p1 = fast_exp2(fmaf(s[0][j][i + 1], c, -mc[j]));
       w[j][h][e] = pack_bf16x2(p0, p1);
-      ls[j] = __builtin_amdgcn_fdot2_f32_bf16(
-          __builtin_bit_cast(bf16x2, w[j][h][e]), one, ls[j], false);
+      ls[j] = row_add<F32>(ls[j], p0, p1, w[j][h][e]);
     }
   };
   auto pb = [&](int j, int h) {

@@ -247,7 +247,7 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
   const int g = lane >> 5, n = lane & 31;
   const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
   const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
-  return attn_step(
+  return attn_step<true>(
       [&](int ks) { return *reinterpret_cast<const bf16x8*>(krow + 32 * ks); },
       [&](int h, int mt) {
         return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B +
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
       const int kb = qb_hi - t;
       if constexpr (M) {
         win_qk(cur, 1, qf, sb, lane);
-        over |= softmax_step<1>(sa, sf, pb, p.c);
+        over |= softmax_step<1, true>(sa, sf, pb, p.c);
         win_pv(cur, 0, pb, acc, lane);
         mask(sb, kb * 64 + 32);
       } else {
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
       if constexpr (M) {
         if (pf) win_issue(p, g, kb - 2, spare, off, wave, lane);
         win_qk(nxt, 0, qf, sa, lane);
-        over |= softmax_step<1>(sb, sf, pb, p.c);
+        over |= softmax_step<1, true>(sb, sf, pb, p.c);
         win_pv(cur, 1, pb, acc, lane);
         mask(sa, (kb - 1) * 64);
       } else {
@@ -371,10 +371,10 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     for (; t < t_b; ++t) iter(std::false_type{}, t);
     for (; t < nt - 1; ++t) iter(std::true_type{}, t);
     win_qk(cur, 1, qf, sb, lane);
-    over |= softmax_step<1>(sa, sf, pb, p.c);
+    over |= softmax_step<1, true>(sa, sf, pb, p.c);
     win_pv(cur, 0, pb, acc, lane);
     mask(sb, kt_lo * 64 + 32);
-    over |= softmax_step<1>(sb, sf, pb, p.c);
+    over |= softmax_step<1, true>(sb, sf, pb, p.c);
     win_pv(cur, 1, pb, acc, lane);
     wait_vm_all();  // no load may still be writing the ring
     if (attempt > 0) break;  // exact references: nothing can overflow

@@ -142,8 +142,13 @@ def test_hybrid_with_full_budget_equals_dense(gpu_lib):
     out = _run_gpu(gpu_lib, d)[0]
     dense = gpu_lib.dense_attn_prefill(d["q"], d["k"], d["v"])
     torch.cuda.synchronize()
-    diff = (out.float() - dense.float()).abs().max().item()
-    assert diff <= 2 * 2 ** -8, diff
+    # The two kernels differ only in rounding (the window kernel sums the
+    # fp32 weights, the sparse one their bf16-rounded copies), so they agree
+    # to about one bf16 ulp of each output: allow two.
+    a, b = out.float(), dense.float()
+    tol = 2.0 ** -6 * b.abs().clamp_min(0.5)
+    excess = ((a - b).abs() - tol).max().item()
+    assert excess <= 0, excess
 
 
 @pytest.mark.parametrize("with_diag", [True, False])
