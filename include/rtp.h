@@ -50,8 +50,10 @@
  *    is returned; rtp_last_error() gives a thread-local message.
  *  - Results are deterministic: no atomics take part in any reduction.
  *  - Supported shapes: d = 128, block = 64, r a multiple of 16 in [16, 128],
- *    Hq <= 128, Hq % Hkv == 0. S may be any size >= 0 (a ragged last block
- *    is handled).
+ *    Hq <= 128, Hq % Hkv == 0. A prefill's S may be any size from 0 to
+ *    16 777 152 = 2^24 - 64 (a ragged last block is handled; one KV head's
+ *    K must fit a 4 GiB buffer descriptor); larger S returns
+ *    RTP_EUNSUPPORTED.
  *  - Two calls that share a workspace must not overlap in time.
  */
 #ifndef RTP_H
@@ -67,7 +69,8 @@ extern "C" {
 /* Status codes. */
 #define RTP_OK 0
 #define RTP_EINVAL (-1)       /* null pointer, negative or inconsistent size */
-#define RTP_EUNSUPPORTED (-2) /* d != 128, block != 64, bad r, Hq > 128 */
+#define RTP_EUNSUPPORTED (-2) /* d != 128, block != 64, bad r, Hq > 128,
+                                prefill S > 2^24 - 64 */
 #define RTP_EWORKSPACE (-3)   /* ws too small or not 256-byte aligned */
 #define RTP_EHIP (-4)         /* HIP runtime or launch error */
 

@@ -47,6 +47,8 @@ int check_shape(int S, int Hq, int Hkv, int d) {
   if (d != rtp::kD) return fail(RTP_EUNSUPPORTED, "only d = 128 is supported");
   if (Hq > rtp::kMaxHeads)
     return fail(RTP_EUNSUPPORTED, "at most 128 query heads are supported");
+  if (S > rtp::kMaxSeq)
+    return fail(RTP_EUNSUPPORTED, "S must be at most 16777152 tokens");
   return RTP_OK;
 }
 

@@ -39,17 +39,16 @@ __device__ __forceinline__ uint32_t sp_v_lane_off(int lane) {
   return (uint32_t)((lane >> 2) * 128 + c * 16);
 }
 
-// vbase: the KV group's first V^T block; k0: first key of the half tile
-__device__ __forceinline__ void sp_issue_v(const u16* vbase, int k0,
+// rv: buffer descriptor of the KV group's V^T blocks; k0: first key of the
+// half tile
+__device__ __forceinline__ void sp_issue_v(__amdgpu_buffer_rsrc_t rv, int k0,
                                            uint32_t voff, char* slot) {
-  const char* vb = reinterpret_cast<const char*>(
-                       vbase + (size_t)(k0 >> 6) * 64 * kD) + (k0 & 63) * 2;
+  const uint32_t toff = (uint32_t)(k0 >> 6) * (64 * kD * 2) + (k0 & 63) * 2;
 #pragma unroll
   for (int ins = 0; ins < 8; ++ins)
-    dma16(vb + ins * 16 * 128 + voff, slot + ins * 1024);
+    buf_dma16(rv, voff + ins * 16 * 128, toff, slot + ins * 1024);
 }
 
-// s_waitcnt vmcnt(24), other counters at their maximum (gfx9 encoding)
 __device__ __forceinline__ void wait_vm24() {
   __builtin_amdgcn_s_waitcnt((24 & 15) | (7 << 4) | (15 << 8) | ((24 >> 4) << 14));
 }
@@ -69,26 +68,27 @@ __device__ __forceinline__ void sp_k_lane_offs(int lane, uint32_t (&o)[4]) {
 }
 
 __device__ __attribute__((noinline)) void sp_issue_k_ragged(
-    const u16* kbase, int S, int k0, char* slot, int lane) {
+    __amdgpu_buffer_rsrc_t rk, int S, int k0, char* slot, int lane) {
   for (int ins = 0; ins < 8; ++ins) {
     const int r = 4 * ins + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     const int key = k0 + r < S ? k0 + r : S - 1;  // rows past S: masked
-    dma16(kbase + (size_t)key * kD + c * 8, slot + ins * 1024);
+    buf_dma16(rk, (uint32_t)key * (kD * 2) + c * 16, 0, slot + ins * 1024);
   }
 }
 
-__device__ __forceinline__ void sp_issue_k(const u16* kbase, int S, int k0,
-                                           const uint32_t (&o)[4], char* slot,
-                                           int lane) {
+// rk: buffer descriptor of the KV group's K rows
+__device__ __forceinline__ void sp_issue_k(__amdgpu_buffer_rsrc_t rk, int S,
+                                           int k0, const uint32_t (&o)[4],
+                                           char* slot, int lane) {
   if (k0 + 32 > S) {
-    sp_issue_k_ragged(kbase, S, k0, slot, lane);
+    sp_issue_k_ragged(rk, S, k0, slot, lane);
     return;
   }
-  const char* kb = reinterpret_cast<const char*>(kbase + (size_t)k0 * kD);
+  const uint32_t toff = (uint32_t)k0 * (kD * 2);
 #pragma unroll
   for (int ins = 0; ins < 8; ++ins)
-    dma16(kb + (ins >> 2) * 4096 + o[ins & 3], slot + ins * 1024);
+    buf_dma16(rk, (ins >> 2) * 4096 + o[ins & 3], toff, slot + ins * 1024);
 }
 
 __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams p) {
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   const int rho = r0 + jj % nr;
   const int qb = p.n_b - 1 - jj / nr;
   const int head = p.head_of_rho[rho];
-  const int g = head / p.G;
+  const int g = __builtin_amdgcn_readfirstlane(head / p.G);
   const int q0 = qb * 64;
   const int S = p.S;
   // The list is read-only here: reading it through the constant address
@@ -122,8 +122,10 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   const int nt = 2 * cnt;  // 32-key half tiles (even)
   char* const kslots = smem + wave * SP_WAVE_B;
   char* const vslots = kslots + 2 * KHALF_B;
-  const u16* kbase = p.k + (size_t)g * S * kD;
-  const u16* vbase = p.vt + (size_t)g * p.n_b * 64 * kD;
+  const __amdgpu_buffer_rsrc_t kbase =
+      buf_rsrc(p.k + (size_t)g * S * kD, (uint32_t)S * (kD * 2));
+  const __amdgpu_buffer_rsrc_t vbase = buf_rsrc(
+      p.vt + (size_t)g * p.n_b * 64 * kD, (uint32_t)p.n_b * (64 * kD * 2));
   // Half tile t: blocks from the last (the diagonal) to the first, halves
   // ascending, so the first half tile holds every query's own key and sets
   // the reference. Indices past the end re-read the last half tile, so every

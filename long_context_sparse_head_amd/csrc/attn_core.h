@@ -256,15 +256,20 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
   //   g7      PV h1 j0                      | exp (j1,h1) second half
   //   g8      PV h1 j1
   // Group 0 has no MFMA of its own: the previous step's last ones drain
-  // while it runs.
+  // while it runs. Each group's operand reads (and staging load) are fenced
+  // off at its head: left to itself the scheduler sinks them to the end of
+  // the group, right before the next group waits for them, which leaves
+  // the LDS latency uncovered.
   dop(0);
   bf16x8 ka = kop(0), kb = kop(1);
+  __builtin_amdgcn_sched_barrier(0);
   expq(0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int q = 1; q < 4; ++q) {
     dop(q);
     const bf16x8 kc = kop(2 * q), kd = kop(2 * q + 1);
+    __builtin_amdgcn_sched_barrier(0);
     sn[0][0] = mfma32(ka, qf[0][2 * q - 2], sn[0][0]);
     sn[0][1] = mfma32(ka, qf[1][2 * q - 2], sn[0][1]);
     sn[0][0] = mfma32(kb, qf[0][2 * q - 1], sn[0][0]);
@@ -277,6 +282,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
   // g4
   dop(4);
   bf16x8 va = vop(0, 0), vb = vop(0, 1);
+  __builtin_amdgcn_sched_barrier(0);
   sn[0][0] = mfma32(ka, qf[0][6], sn[0][0]);
   sn[0][1] = mfma32(ka, qf[1][6], sn[0][1]);
   sn[0][0] = mfma32(kb, qf[0][7], sn[0][0]);
@@ -286,6 +292,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
   // g5
   dop(5);
   const bf16x8 vc = vop(0, 2), vd = vop(0, 3);
+  __builtin_amdgcn_sched_barrier(0);
   {
     const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
     acc[0][0] = mfma32(va, p00, acc[0][0]);
@@ -299,6 +306,7 @@ __device__ __forceinline__ bool attn_step(KOp kop, VOp vop, DOp dop,
   dop(6);
   const bf16x8 v10 = vop(1, 0), v11 = vop(1, 1), v12 = vop(1, 2),
                v13 = vop(1, 3);
+  __builtin_amdgcn_sched_barrier(0);
   {
     const bf16x8 p00 = pb(0, 0), p10 = pb(1, 0);
     acc[0][2] = mfma32(vc, p00, acc[0][2]);

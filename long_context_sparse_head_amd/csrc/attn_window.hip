@@ -96,54 +96,65 @@ __device__ __attribute__((noinline)) void win_issue_ragged_k(
   const int r = u / 17, c = min(u % 17, 15);
   int key = kb * 64 + (r & 32) + perm_row(r & 31);
   key = key < p.S ? key : p.S - 1;
-  dma16(p.k + ((size_t)g * p.S + key) * kD + c * 8, stage + ld * 1024);
+  buf_dma16(buf_rsrc(p.k + (size_t)g * p.S * kD, (uint32_t)p.S * (kD * 2)),
+            (uint32_t)key * (kD * 2) + c * 16, 0, stage + ld * 1024);
 }
 
-// First byte of a tile's K rows and of its V^T block.
-__device__ __forceinline__ void win_tile_src(const WinParams& p, int g, int kb,
-                                             const char*& kt, const char*& vt) {
-  kt = reinterpret_cast<const char*>(p.k) +
-       ((size_t)g * p.S + (size_t)kb * 64) * (kD * 2);
-  vt = reinterpret_cast<const char*>(p.vt + ((size_t)g * p.n_b + kb) * 64 * kD);
+// Buffer descriptors of one KV head's K rows and V^T blocks; a tile's bytes
+// start at kb * 16 KiB in both.
+struct WinSrc {
+  __amdgpu_buffer_rsrc_t k, v;
+};
+constexpr uint32_t kTileBytes = 64 * kD * 2;  // K rows or V^T of 64 keys
+__device__ __forceinline__ WinSrc win_src(const WinParams& p, int g) {
+  WinSrc r;
+  r.k = buf_rsrc(p.k + (size_t)g * p.S * kD, (uint32_t)p.S * (kD * 2));
+  r.v = buf_rsrc(p.vt + (size_t)g * p.n_b * 64 * kD,
+                 (uint32_t)p.n_b * kTileBytes);
+  return r;
 }
 
 // Load j (0..8) of this wave for a full tile: loads 0..3 are K rows, load 4 is
 // K for wave 0 and V^T for the others, loads 5..8 are V^T. The stage has only
 // 35 loads, so wave 3 repeats its load 7 as load 8 (same bytes, same place),
 // which keeps the issue free of branches.
-__device__ __forceinline__ void win_issue_one(const char* kt, const char* vt,
+__device__ __forceinline__ void win_issue_one(const WinSrc& src, int kb,
                                               char* stage,
                                               const WinLaneOffsets& o,
                                               int wave, int j) {
+  const uint32_t toff = (uint32_t)kb * kTileBytes;
   if (j < 4) {
-    dma16(kt + o.off[j], stage + wave * 1024 + j * 4096);
+    buf_dma16(src.k, o.off[j], toff, stage + wave * 1024 + j * 4096);
   } else if (j == 4) {
-    dma16((wave == 0 ? kt : vt) + o.off[4], stage + wave * 1024 + 4 * 4096);
+    buf_dma16(wave == 0 ? src.k : src.v, o.off[4], toff,
+              stage + wave * 1024 + 4 * 4096);
   } else if (j < 8) {
-    dma16(vt + o.off[j], stage + wave * 1024 + j * 4096);
+    buf_dma16(src.v, o.off[j], toff, stage + wave * 1024 + j * 4096);
   } else {
     const int jj = wave < 3 ? 8 : 7;
-    dma16(vt + o.off[jj], stage + wave * 1024 + jj * 4096);
+    buf_dma16(src.v, o.off[jj], toff, stage + wave * 1024 + jj * 4096);
   }
 }
 
 // All loads of this wave for tile kb, back to back.
-__device__ __forceinline__ void win_issue(const WinParams& p, int g, int kb,
-                                          char* stage, const WinLaneOffsets& o,
-                                          int wave, int lane) {
-  const char *kt, *vt;
-  win_tile_src(p, g, kb, kt, vt);
+__device__ __forceinline__ void win_issue(const WinParams& p, const WinSrc& src,
+                                          int g, int kb, char* stage,
+                                          const WinLaneOffsets& o, int wave,
+                                          int lane) {
   if ((kb + 1) * 64 > p.S) {  // last block of a ragged S: rows past S
 #pragma unroll 1                // re-read row S-1 (masked anyway)
     for (int j = 0; j < DMA_PER_WAVE; ++j) {
       const int ld = wave + 4 * j;
       if (ld < K_DMA) win_issue_ragged_k(p, g, kb, stage, ld, lane);
-      else if (ld < K_DMA + V_DMA) dma16(vt + o.off[j], stage + ld * 1024);
+      else if (ld < K_DMA + V_DMA)
+        buf_dma16(src.v, o.off[j], (uint32_t)kb * kTileBytes,
+                  stage + ld * 1024);
     }
     return;
   }
 #pragma unroll
-  for (int j = 0; j < DMA_PER_WAVE; ++j) win_issue_one(kt, vt, stage, o, wave, j);
+  for (int j = 0; j < DMA_PER_WAVE; ++j)
+    win_issue_one(src, kb, stage, o, wave, j);
 }
 
 // S^T for one 32-key sub-tile st of a staged tile: s[0][j], j = query tile
@@ -293,6 +304,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     if (!(kmax <= q0 && kmin > qmax - w)) mask_sub(s[0], kmin, q0, w, lane);
   };
   const WinLaneOffsets off = win_offsets(wave, lane);
+  const WinSrc src = win_src(p, g);
 
   bf16x8 qf[2][8];
   load_q(p.q, head, q0, p.S, qf, lane);
@@ -309,8 +321,8 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     char* cur = smem;
     char* nxt = smem + STAGE_B;
     char* spare = smem + 2 * STAGE_B;
-    win_issue(p, g, qb_hi, cur, off, wave, lane);
-    if (nt > 1) win_issue(p, g, qb_hi - 1, nxt, off, wave, lane);
+    win_issue(p, src, g, qb_hi, cur, off, wave, lane);
+    if (nt > 1) win_issue(p, src, g, qb_hi - 1, nxt, off, wave, lane);
     wait_vm_all();
     __syncthreads();
     // Sub-tile u = 32 keys (tile u/2, half u%2). Step u runs the QK MFMAs of
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
       __syncthreads();  // tile t+1 resident; spare (tile t-1) free
       const bool pf = t + 2 < nt;
       if constexpr (M) {
-        if (pf) win_issue(p, g, kb - 2, spare, off, wave, lane);
+        if (pf) win_issue(p, src, g, kb - 2, spare, off, wave, lane);
         win_qk(nxt, 0, qf, sa, lane);
         over |= softmax_step<1, true>(sb, sf, pb, p.c);
         win_pv(cur, 1, pb, acc, lane);
@@ -348,11 +360,10 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
         // group (a prefetched tile is below the top one, so never ragged).
         // Past the last tile they re-read tile t into the spare stage, which
         // is then never read, so the issue needs no branch.
-        const char *kt, *vt;
-        win_tile_src(p, g, pf ? kb - 2 : kb, kt, vt);
+        const int kb_pf = pf ? kb - 2 : kb;
         over |= win_step(nxt, 0, cur, 1, qf, sb, sa, sf, acc, p.c, lane,
                          [&](int j) {
-                           win_issue_one(kt, vt, spare, off, wave, j);
+                           win_issue_one(src, kb_pf, spare, off, wave, j);
                          });
       }
       char* const done = cur;
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void attn_window_kernel(const WinParams p) 
     sf.mref[0] = sf.mref[1] = -INFINITY;
 #pragma unroll 1
     for (int t = 0; t < nt; ++t) {
-      win_issue(p, g, qb_hi - t, smem, off, wave, lane);
+      win_issue(p, src, g, qb_hi - t, smem, off, wave, lane);
       wait_vm_all();
       __syncthreads();
 #pragma unroll 1

@@ -14,6 +14,8 @@ typedef uint16_t u16;
 constexpr int kD = 128;      // head dim
 constexpr int kBlk = 64;     // indexer block = attention key tile
 constexpr int kMaxHeads = 128;
+// Longest prefill: one KV head's K (S x 256 B) must fit a buffer descriptor.
+constexpr int kMaxSeq = (1 << 24) - 64;
 
 // MFMA lane layouts on gfx950 (checked on hardware against a CPU matmul):
 //  v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+e] and
@@ -44,6 +46,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {  // RNE
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
+}
+// The same LDS DMA through a buffer descriptor (the MUBUF "lds" form):
+// 16 bytes per lane from base + voff + soff land at lds_base + 16 i. The FLAT
+// form above counts, for the compiler, as possibly touching LDS, and while
+// one is in flight every LDS wait it inserts is a full lgkmcnt(0); with the
+// buffer form the waits stay exact, so operand reads issued ahead really do
+// overlap the MFMAs. A descriptor covers at most 4 GiB (bytes < 2^32).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base,
+                                                          uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_dma16(__amdgpu_buffer_rsrc_t r,
+                                          uint32_t voff, uint32_t soff,
+                                          void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, voff,
+                                           soff, 0, 0);
 }
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 // s_waitcnt vmcnt(N), other counters at their maximum (gfx9 encoding)

@@ -106,6 +106,8 @@ def test_prefill_argument_validation_returns_codes():
     assert _prefill(lib, mp, ws=1 << 20 | 8, wsb=1 << 40) == -3  # misaligned
     assert b"workspace" in lib.rtp_last_error()
     assert _prefill(lib, mp, S=0) == 0             # empty: nothing to do
+    assert _prefill(lib, mp, S=(1 << 24) - 63) == -2  # K past 4 GiB per head
+    assert b"16777152" in lib.rtp_last_error()
     m2, mp2 = _mask([0] * 130)
     assert _prefill(lib, mp2, Hq=130, Hkv=130) == -2
 
