@@ -46,9 +46,9 @@ TRAFFIC = {
     "sources": ["long_context_sparse_head_amd/csrc/attn_window.hip",
                 "long_context_sparse_head_amd/csrc/attn_core.h",
                 "long_context_sparse_head_amd/build.py"],
-    "sha256": None,
-    "fetch_bytes": None,
-    "write_bytes": None,
+    "sha256": "8631befb3ae35fcb19d9f895f862036c91d74cd6b4cd81fae4ba36efa94872b8",
+    "fetch_bytes": 2935474530,
+    "write_bytes": 906254451,
 }
 
 

@@ -26,12 +26,15 @@ HIPFLAGS = [
     "-Wno-unused-result",
 ]
 
-# Per-file backend options. The window kernel's score accumulators should
-# live in VGPRs (the softmax reads every one of them) while its O accumulator
-# stays in AGPRs; asking the backend to prefer the VGPR form of MFMA results
-# gets that placement (the sparse kernel is faster without it).
+# Per-file backend options. Asking the backend to prefer the VGPR form of
+# MFMA results puts the window kernel's score accumulators and the block
+# scores of the indexer in VGPRs, where the VALU reads every one of them,
+# instead of in AGPRs that need a copy per value (the sparse kernel and the
+# decode kernel are no faster with it and keep the default).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {
-    "attn_window.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_window.hip": VGPR_FORM,
+    "indexer.hip": VGPR_FORM,
 }
 
 
