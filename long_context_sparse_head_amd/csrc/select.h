@@ -201,8 +201,10 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
   }
   // take every key above T and the first (by index) keys equal to T: one
   // scan of the packed counts (greater in the low half, equal in the high
-  // half; a row has fewer than 2^16 keys). Equal keys are taken in index
-  // order, so those taken before thread t number min(equal before t, keq).
+  // half). Both totals are below n < 2^15 there, so every partial sum stays
+  // below 2^31 and the signed scan cannot overflow. Equal keys are taken in
+  // index order, so those taken before thread t number
+  // min(equal before t, keq).
   int ngt = 0, neq = 0;
   for (int e = e0; e < e1; ++e) {
     const uint32_t x = getk(e);
@@ -210,7 +212,7 @@ __device__ TopkResult radix_topk(GetK getk, int n, int k, int32_t* out,
     neq += x == T;
   }
   int gt_before, eq_before, tot_gt, tot_eq;
-  if (n < 65536) {
+  if (n < 32768) {
     const int both = ngt | (neq << 16);
     const int incl = block_incl_scan(both, sh.tmp);
     if (tid == 255) sh.bcast[3] = incl;

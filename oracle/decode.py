@@ -69,11 +69,16 @@ def hybrid_decode(q_bits: np.ndarray, kc_bits: np.ndarray,
                   vc_bits: np.ndarray, cache_len, is_retrieval, window: int,
                   p_q: np.ndarray, p_k: np.ndarray, block: int, top_k: int,
                   n_recent: int = 2, scale: Optional[float] = None,
-                  seqs: Optional[Iterable[int]] = None) -> dict:
+                  seqs: Optional[Iterable[int]] = None,
+                  sel_override: Optional[dict] = None) -> dict:
     """One decode step for a batch.
 
     q_bits [Bn,Hq,d]; kc_bits/vc_bits [Bn,Hkv,Lmax,d] (bf16 storage);
-    cache_len [Bn] counts the new token. Returns out fp32 [Bn,Hq,d],
+    cache_len [Bn] counts the new token. sel_override: optional dict
+    (b, rho) -> ascending block ids that replaces the block choice of that
+    (sequence, retrieval head), so attention can be compared under an
+    identical selection (centroids are still computed). Returns out fp32
+    [Bn,Hq,d],
     out_bf16, lse [Bn,Hq], sel [Bn,n_ret,top_k+1+n_recent] (ascending,
     -1 padded), sel_count [Bn,n_ret], kth [Bn,n_ret,2],
     centroids dict (b, rho) -> [n_full, r].
@@ -108,9 +113,15 @@ def hybrid_decode(q_bits: np.ndarray, kc_bits: np.ndarray,
                     rho = ret_heads.index(h)
                     c = decode_centroids(kf, p_k[rho], B, n_full)
                     cents[(b, rho)] = c
-                    qt = (p_q[rho].astype(F32) @ qf).astype(F32)
-                    sel, s_k, s_k1 = decode_select(qt, c, n_b, top_k,
-                                                   n_recent)
+                    if sel_override is not None and (b, rho) in \
+                            sel_override:
+                        sel = np.asarray(sel_override[(b, rho)],
+                                         dtype=np.int64)
+                        s_k = s_k1 = math.nan
+                    else:
+                        qt = (p_q[rho].astype(F32) @ qf).astype(F32)
+                        sel, s_k, s_k1 = decode_select(qt, c, n_b, top_k,
+                                                       n_recent)
                     sel_arr[b, rho, :len(sel)] = sel
                     sel_cnt[b, rho] = len(sel)
                     kth[b, rho] = (s_k, s_k1)

@@ -33,18 +33,17 @@ def run_gpu(rtp, y):
 
 def check(rtp, y, label, seqs=None):
     out, lse, sel, cent = run_gpu(rtp, y)
-    ora = oracle.hybrid_decode(bf16_bits(y["q"]), bf16_bits(y["k_cache"]),
-                               bf16_bits(y["v_cache"]), y["cache_len"],
-                               y["is_retrieval"], y["window"], y["p_q"],
-                               y["p_k"], 64, y["top_k"], y["n_recent"],
-                               seqs=seqs)
+    args = (bf16_bits(y["q"]), bf16_bits(y["k_cache"]),
+            bf16_bits(y["v_cache"]), y["cache_len"], y["is_retrieval"],
+            y["window"], y["p_q"], y["p_k"], 64, y["top_k"], y["n_recent"])
+    ora = oracle.hybrid_decode(*args, seqs=seqs)
     seqs = range(len(y["cache_len"])) if seqs is None else seqs
     gsel = sel.cpu().numpy()
     gcent = cent.cpu().numpy()
-    ties = []
+    ties, override = [], {}
     for b in seqs:
         L = int(y["cache_len"][b])
-        n_full = L // 64
+        n_full, n_b = L // 64, -(-L // 64)
         for rho in range(len(y["retrieval_heads"])):
             c_o = ora["centroids"][(b, rho)]
             c_g = gcent[b, rho, :n_full]
@@ -55,29 +54,31 @@ def check(rtp, y, label, seqs=None):
             gcnt = int((g >= 0).sum())
             qt = (y["p_q"][rho] @ oracle.bf16_to_f32(bf16_bits(
                 y["q"][b, y["retrieval_heads"][rho]])))
-
-            def fn(_, c_o=c_o, qt=qt):
-                return c_o[1:] @ qt.astype(np.float32)
-            ties += parity.compare_selection(
+            t = parity.compare_selection(
                 g[None], np.array([gcnt]), ora["sel"][b, rho][None],
-                ora["sel_count"][b, rho][None], ora["kth"][b, rho][None], fn,
+                ora["sel_count"][b, rho][None], ora["kth"][b, rho][None],
+                parity.decode_scores_fn(c_o, qt, n_b, y["n_recent"]),
+                parity.decode_required(n_b, y["n_recent"]),
                 f"{label} b={b} rho={rho}")
-    # rows whose choice differs at a logged near-tie are left out of the
-    # output comparison (the oracle attended a different, equally valid set)
+            if t:
+                override[(b, rho)] = g[:gcnt]
+            ties += t
     assert len(ties) <= 2, ties
-    skip = {(int(t[0].split("b=")[1].split()[0]),
-             int(y["retrieval_heads"][int(t[0].split("rho=")[1])]))
-            for t in ties}
+    # rows whose choice differs at a logged near-tie are compared under the
+    # GPU's own (equally valid) choice
+    if override:
+        ora = oracle.hybrid_decode(*args, seqs=seqs, sel_override=override)
     o_g = parity.bf16_to_f32(out)
     l_g = lse.cpu().numpy()
+    worst = 0.0
     for b in seqs:
         for h in range(o_g.shape[1]):
-            if (b, h) in skip:
-                continue
             err = parity.max_abs(o_g[b, h], ora["out"][b, h])
             assert err <= parity.OUT_TOL, (label, b, h, err)
-            assert abs(l_g[b, h] - ora["lse"][b, h]) <= parity.LSE_TOL, \
-                (label, b, h)
+            lerr = abs(l_g[b, h] - ora["lse"][b, h])
+            assert lerr <= parity.LSE_TOL_BF16_SUM, (label, b, h, lerr)
+            worst = max(worst, lerr)
+    print(f"[lse] decode {label}: {worst:.2e}, ties {len(ties)}", flush=True)
     return out, ora
 
 

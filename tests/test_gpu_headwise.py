@@ -49,12 +49,14 @@ def test_sparse_mode_with_a_window_per_head(gpu_lib):
         fn = parity.prefill_rows_fn(x, qb_, kb_, rho, h)
         parity.compare_selection(gsel[rho], gcnt[rho], ora["sel"][rho],
                                  ora["sel_count"][rho], ora["kth"][rho], fn,
+                                 parity.prefill_required(int),
                                  f"headwise rho={rho}")
     ref = oracle.hybrid_prefill(qb_, kb_, vb_, x["is_retrieval"], windows,
                                 x["p_q"], x["p_k"], 64, 5,
                                 sel_override=override)
     assert parity.max_abs(parity.bf16_to_f32(out), ref["out"]) <= parity.OUT_TOL
-    assert parity.max_abs(lse.cpu().numpy(), ref["lse"]) <= parity.LSE_TOL
+    parity.check_prefill_lse(lse.cpu().numpy(), ref["lse"], x["is_retrieval"],
+                             "headwise sparse")
     # window 1 returns V bitwise
     assert torch.equal(out[0].cpu(), x["v"][0])
     c = cent.cpu().numpy()
@@ -77,7 +79,10 @@ def test_full_mode_matches_oracle_and_decode_centroids(gpu_lib, S):
     ora = oracle.hybrid_prefill(qb_, kb_, vb_, x["is_retrieval"], windows,
                                 x["p_q"], x["p_k"], 64, 4, retrieval_full=True)
     assert parity.max_abs(parity.bf16_to_f32(out), ora["out"]) <= parity.OUT_TOL
-    assert parity.max_abs(lse.cpu().numpy(), ora["lse"]) <= parity.LSE_TOL
+    lerr = parity.check_prefill_lse(lse.cpu().numpy(), ora["lse"],
+                                    x["is_retrieval"], "headwise full",
+                                    retrieval_full=True)
+    print(f"[lse] headwise full S={S}: {lerr['window']:.2e}", flush=True)
     c = cent.cpu().numpy()
     assert np.abs(c - ora["centroids"]).max() <= 1e-5 * np.abs(ora["centroids"]).max()
     # decode cache [1, Hkv, Lmax, d] holding the sequence
@@ -142,22 +147,25 @@ def test_full_prefill_then_sparse_decode_recipe(gpu_lib):
                                x["is_retrieval"], 512, x["p_q"], x["p_k"], 64,
                                8, 2)
     g = sel.cpu().numpy()
-    ties = []
+    n_b = -(-(S + 1) // 64)
+    override = {}
     for rho, h in enumerate(ret):
         c_o = ora["centroids"][(0, rho)]
         qt = x["p_q"][rho] @ oracle.bf16_to_f32(bf16_bits(qd[0, h]))
-
-        def fn(_, c_o=c_o, qt=qt):
-            return c_o[1:] @ qt.astype(np.float32)
         gcnt = int((g[0, rho] >= 0).sum())
-        ties += parity.compare_selection(
+        ties = parity.compare_selection(
             g[0, rho][None], np.array([gcnt]), ora["sel"][0, rho][None],
-            ora["sel_count"][0, rho][None], ora["kth"][0, rho][None], fn,
-            f"recipe rho={rho}")
-    skip = {ret[int(t[0].split("rho=")[1])] for t in ties}
+            ora["sel_count"][0, rho][None], ora["kth"][0, rho][None],
+            parity.decode_scores_fn(c_o, qt, n_b, 2),
+            parity.decode_required(n_b, 2), f"recipe rho={rho}")
+        if ties:
+            override[(0, rho)] = g[0, rho][:gcnt]
+    if override:  # attend under the GPU's own (equally valid) choice
+        ora = oracle.hybrid_decode(bf16_bits(qd), kcb, vcb, np.array([S + 1]),
+                                   x["is_retrieval"], 512, x["p_q"],
+                                   x["p_k"], 64, 8, 2, sel_override=override)
     o_g = parity.bf16_to_f32(out)
     for h in range(8):
-        if h in skip:
-            continue
         assert parity.max_abs(o_g[0, h], ora["out"][0, h]) <= parity.OUT_TOL, h
-        assert abs(lse.cpu().numpy()[0, h] - ora["lse"][0, h]) <= parity.LSE_TOL
+        assert abs(lse.cpu().numpy()[0, h] - ora["lse"][0, h]) <= \
+            parity.LSE_TOL_BF16_SUM

@@ -55,7 +55,8 @@ def full_check(rtp, x, label):
         fn = parity.prefill_rows_fn(x, qb_, kb_, rho, h)
         ties += parity.compare_selection(gsel[rho], gcnt[rho], ora["sel"][rho],
                                          ora["sel_count"][rho], ora["kth"][rho],
-                                         fn, f"{label} rho={rho}")
+                                         fn, parity.prefill_required(int),
+                                         f"{label} rho={rho}")
     # attention under the GPU's own selection (equal to the oracle's except
     # at logged ties)
     override = {rho: {qb: gsel[rho, qb, :gcnt[rho, qb]] for qb in range(n_b)}
@@ -64,12 +65,14 @@ def full_check(rtp, x, label):
         qb_, kb_, vb_, x["is_retrieval"], x["window"], x["p_q"], x["p_k"],
         x["block"], x["top_k"], sel_override=override)
     err = parity.max_abs(parity.bf16_to_f32(out), ref["out"])
-    lerr = parity.max_abs(lse.cpu().numpy(), ref["lse"])
     assert err <= parity.OUT_TOL, (label, err)
-    assert lerr <= parity.LSE_TOL, (label, lerr)
+    lerr = parity.check_prefill_lse(lse.cpu().numpy(), ref["lse"],
+                                    x["is_retrieval"], label)
+    print(f"[lse] {label}: window {lerr['window']:.2e} sparse "
+          f"{lerr['sparse']:.2e}", flush=True)
     assert not torch.isnan(out.float()).any()
-    return dict(err=err, lse_err=lerr, ties=ties, out=out, sel=gsel, cnt=gcnt,
-                ora=ora)
+    return dict(err=err, lse_err=max(lerr.values()), ties=ties, out=out,
+                sel=gsel, cnt=gcnt, ora=ora)
 
 
 def test_tiny_workload_full_parity(gpu_lib):
@@ -130,7 +133,9 @@ def test_dense_kernel_equals_oracle_full_coverage(gpu_lib):
     ora = oracle.hybrid_prefill(*_bits(x), x["is_retrieval"], S, x["p_q"],
                                 x["p_k"], 64, 1)
     assert parity.max_abs(parity.bf16_to_f32(out), ora["out"]) <= parity.OUT_TOL
-    assert parity.max_abs(lse.cpu().numpy(), ora["lse"]) <= parity.LSE_TOL
+    lerr = parity.check_prefill_lse(lse.cpu().numpy(), ora["lse"],
+                                    x["is_retrieval"], "dense")
+    print(f"[lse] dense: {lerr['window']:.2e}", flush=True)
 
 
 def test_hybrid_with_full_budget_equals_dense(gpu_lib):
@@ -241,7 +246,8 @@ def test_indexer_select_kth_scores_and_centroids(gpu_lib, S, top_k):
         fn = parity.prefill_rows_fn(x, *_bits(x)[:2], rho, h)
         parity.compare_selection(sel.cpu().numpy()[rho], cnt.cpu().numpy()[rho],
                                  ora_sel["sel"][rho], ora_sel["sel_count"][rho],
-                                 ora_sel["kth"][rho], fn, f"kth rho={rho}")
+                                 ora_sel["kth"][rho], fn,
+                                 parity.prefill_required(int), f"kth rho={rho}")
     k_g, k_o = kth.cpu().numpy(), ora_sel["kth"]
     both = ~np.isnan(k_o)
     assert np.array_equal(np.isnan(k_g), np.isnan(k_o))

@@ -8,6 +8,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle
 import oracle.decode as od
 import oracle.prefill as op
 from tests import test_oracle_pins as pins
@@ -114,6 +115,31 @@ def _decode_select_no_recent(q_tilde, cents, n_b, k, n_recent):
     return sel[sel < n_b - 1] if n_b > 1 else sel, a, b
 
 
+def _dec_centroids_max_pool(k_seq, p_k, B, n_full):
+    proj = k_seq[:n_full * B].astype(F32) @ p_k.astype(F32).T
+    return proj.reshape(n_full, B, -1).max(axis=1).astype(F32)
+
+
+def _dec_centroids_first_key(k_seq, p_k, B, n_full):
+    proj = k_seq[:n_full * B].astype(F32) @ p_k.astype(F32).T
+    return proj.reshape(n_full, B, -1)[:, 0].astype(F32)
+
+
+def _decode_query_projected_with_pk(*args, **kw):
+    # the decode query is wrongly projected with P_k instead of P_q
+    args = list(args)
+    if "p_k" in kw:
+        pk = kw["p_k"]
+    else:
+        pk = args[7]
+    if "p_q" in kw:
+        kw["p_q"] = pk
+    else:
+        args[6] = pk
+    return _orig_hybrid_decode(*args, **kw)
+
+
+_orig_hybrid_decode = od.hybrid_decode
 _orig_attend = op.attend
 _orig_score = op.block_score_row
 _orig_select = op.select_row
@@ -137,6 +163,9 @@ MUTATIONS = [
     (od, "decode_select", _decode_select_no_recent),
     (op, "head_window", _head_window_of_neighbour),
     (op, "causal_block_keys", _causal_keys_without_self),
+    (od, "decode_centroids", _dec_centroids_max_pool),
+    (od, "decode_centroids", _dec_centroids_first_key),
+    (oracle, "hybrid_decode", _decode_query_projected_with_pk),
 ]
 
 PIN_TESTS = [
@@ -153,6 +182,9 @@ PIN_TESTS = [
     pins.test_decode_planted_selection,
     pins.test_per_head_windows_match_masked_sdpa,
     pins.test_full_retrieval_heads_are_dense_causal_with_centroids,
+    pins.test_decode_centroids_are_projected_block_means,
+    pins.test_decode_selection_matches_fp64_brute_force,
+    pins.test_decode_selection_override_attends_the_given_blocks,
 ]
 
 

@@ -442,3 +442,104 @@ def test_decode_short_cache_keeps_everything():
                 top_k=3)
     res = _run_dec(x)
     assert res["sel"][0, 0][res["sel"][0, 0] >= 0].tolist() == list(range(6))
+
+
+def _fp64_decode_centroids(k_seq, p_k, n_full, B=64):
+    """fp64: P_k applied to the mean key of each full block (linearity)."""
+    if n_full == 0:
+        return np.zeros((0, p_k.shape[0]))
+    kg = k_seq[:n_full * B].astype(np.float64)
+    return kg.reshape(n_full, B, -1).mean(1) @ p_k.T.astype(np.float64)
+
+
+def test_decode_centroids_are_projected_block_means():
+    # Random, non-constant keys and ragged caches: only the full blocks get
+    # a centroid (the partial block holding the newest tokens has none), and
+    # each is P_k applied to the block's mean key, computed in fp64. A
+    # max-pooled, first-key or mis-projected centroid fails.
+    lens = [64 * 9 + 23, 64 * 4, 63, 64 * 6 + 1]
+    x = _decode(4, max(lens), Hq=4, Hkv=2, d=64, ret=(1, 2), window=16,
+                top_k=2, lens=lens, seed=7)
+    res = _run_dec(x)
+    k = _f32(x["kb"])
+    for b, L in enumerate(lens):
+        n_full = L // 64
+        for rho, h in enumerate((1, 2)):
+            c = res["centroids"][(b, rho)]
+            assert c.shape == (n_full, 16), (b, rho, c.shape)
+            alt = _fp64_decode_centroids(k[b, h // 2], x["p_k"][rho], n_full)
+            if n_full:
+                assert np.abs(c - alt).max() <= 1e-5 * np.abs(alt).max(), \
+                    (b, rho)
+                direct = oracle.decode_centroids(k[b, h // 2, :L],
+                                                 x["p_k"][rho], 64, n_full)
+                assert np.array_equal(direct, c)
+
+
+def test_decode_selection_matches_fp64_brute_force():
+    # Independent random P_q and P_k (so that using one for the other, or
+    # scoring with anything but the block mean, changes the choice). The
+    # kept set is {0} u top-k u {last n_recent blocks}, with the top-k taken
+    # by fp64 scores (P_q q).(P_k mean k) over the candidates 1 .. n_b-3,
+    # fully sorted, ties to the lower block; s_k / s_{k+1} are the k-th and
+    # (k+1)-th of the same sort.
+    lens = [64 * 150 + 17, 64 * 90, 64 * 40 + 1, 64 * 13 + 5]
+    top_k = 12
+    x = _decode(4, max(lens), Hq=4, Hkv=2, d=64, ret=(0, 3), window=16,
+                top_k=top_k, lens=lens, seed=4)
+    assert np.abs(x["p_q"] - x["p_k"]).max() > 0.1
+    res = _run_dec(x)
+    q, k = _f32(x["qb"]), _f32(x["kb"])
+    log = []
+    for b, L in enumerate(lens):
+        n_b, n_full = -(-L // 64), L // 64
+        n_c = n_b - x["n_recent"] - 1
+        for rho, h in enumerate((0, 3)):
+            qt = x["p_q"][rho].astype(np.float64) @ q[b, h].astype(np.float64)
+            cents = _fp64_decode_centroids(k[b, h // 2], x["p_k"][rho],
+                                           n_full)
+            sc = cents[1:1 + n_c] @ qt
+            cand = np.arange(1, 1 + n_c)
+            order = np.lexsort((cand, -sc))
+            want = set(cand[order[:top_k]].tolist()) | {0} | set(
+                range(n_b - x["n_recent"], n_b))
+            got_row = res["sel"][b, rho]
+            got = set(got_row[got_row >= 0].tolist())
+            assert res["sel_count"][b, rho] == len(got)
+            if got != want and n_c > top_k:
+                s_k, s_k1 = sc[order[top_k - 1]], sc[order[top_k]]
+                assert abs(s_k - s_k1) < 1e-4 * abs(s_k), (b, rho)
+                for blk in got ^ want:
+                    assert 1 <= blk <= n_c
+                    assert abs(sc[blk - 1] - s_k) < 1e-4 * abs(s_k)
+                log.append((b, rho))
+            if n_c <= top_k:  # short cache: every block, no k-th score
+                assert got == set(range(n_b)), (b, rho)
+                continue
+            srt = np.sort(sc)[::-1]
+            assert abs(res["kth"][b, rho, 0] - srt[top_k - 1]) <= \
+                1e-5 * abs(srt[top_k - 1]) + 1e-6, (b, rho)
+            assert abs(res["kth"][b, rho, 1] - srt[top_k]) <= \
+                1e-5 * abs(srt[top_k]) + 1e-6, (b, rho)
+    assert len(log) <= 1
+
+
+def test_decode_selection_override_attends_the_given_blocks():
+    # sel_override replaces the block choice of one (sequence, head): the
+    # output is then exact attention over the tokens of the given blocks
+    # (fp64 textbook softmax), whatever the scores say
+    lens = [64 * 20 + 9]
+    x = _decode(1, lens[0], Hq=2, Hkv=1, d=32, ret=(1,), window=8, top_k=3,
+                lens=lens)
+    blocks = [0, 5, 6, 13, 19, 20]
+    res = _run_dec(x, sel_override={(0, 0): blocks})
+    q, k, v = _f32(x["qb"]), _f32(x["kb"]), _f32(x["vb"])
+    L = lens[0]
+    js = np.concatenate([np.arange(b * 64, min(L, b * 64 + 64))
+                         for b in blocks])
+    s = (k[0, 0, js].astype(np.float64) @ q[0, 1]) / math.sqrt(32)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    assert np.abs(res["out"][0, 1] - p @ v[0, 0, js]).max() < 1e-5
+    got = res["sel"][0, 0]
+    assert got[got >= 0].tolist() == blocks
