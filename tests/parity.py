@@ -105,6 +105,20 @@ def compare_selection(gsel, gcnt, osel, ocnt, okth, score_fn, required_fn,
     return ties
 
 
+# A row may differ from the oracle only at a near-tie (checked row by row
+# above). Such rows stay rare: the GPU scores carry ~1e-5 relative error, so
+# a row differs only where its k-th and (k+1)-th scores are about that close
+# (0.15% of the 128K layer's rows measured). A systematic scoring error would
+# change far more rows, so the rate is capped at 1% (and 2 rows on small
+# inputs).
+MAX_TIE_RATE = 0.01
+
+
+def assert_tie_rate(ties, n_rows, label=""):
+    cap = max(2, int(MAX_TIE_RATE * n_rows))
+    assert len(ties) <= cap, (label, len(ties), n_rows, ties[:8])
+
+
 def prefill_required(qb_of_row):
     """Always-kept blocks of prefill row i: the sink and the diagonal."""
     return lambda i: {0, int(qb_of_row(i))}
