@@ -202,17 +202,35 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False):
                                        (spa["ms_per_launch"] / 1e3) / 1e12)
     res["attn_frac_bf16_peak"] = res["attn_tflops"] / PEAK_BF16_TFLOPS
     if not dense and not full and n_ret:
-        # indexer figures (algorithmic): scores are 2r flops per (query
-        # block, candidate key); projections read K and Q once
+        # indexer figures (algorithmic). Scores: 2r flops per (query block,
+        # candidate key), run as three bf16 MFMA products (hi.hi, hi.lo,
+        # lo.hi), so the matrix cores execute 3x that. Projections: K of each
+        # KV group with retrieval heads read once, the projected keys (64 B
+        # per key per head) written once; Q of each retrieval head read once.
         cand_keys = 64 * sum(max(q - 1, 0) for q in range(n_b))
-        sc = ks.get("block_scores")
+        G = Hq // Hkv
+        n_grp = len({int(h) // G for h in x["retrieval_heads"]})
+        sc = ks.get("score_select")
         if sc:
-            res["block_scores_tflops_alg"] = (n_ret * cand_keys * 2 * w.r /
-                                              (sc["ms_per_launch"] / 1e3) / 1e12)
+            alg = n_ret * cand_keys * 2 * w.r / (sc["ms_per_launch"] / 1e3)
+            res["score_select_tflops_alg"] = alg / 1e12
+            res["score_select_mfma_frac"] = 3 * alg / 1e12 / PEAK_BF16_TFLOPS
         pkk = ks.get("proj_keys")
         if pkk:
-            byt = n_ret * S * (256 + 64)
+            byt = n_grp * S * 256 + n_ret * S * 64
             res["proj_keys_gbs_alg"] = byt / (pkk["ms_per_launch"] / 1e3) / 1e9
+        pqm = ks.get("proj_qmeans")
+        if pqm:
+            byt = n_ret * S * 256
+            res["proj_qmeans_gbs_alg"] = byt / (pqm["ms_per_launch"] / 1e3) / 1e9
+        res["indexer_ms"] = sum(ks[k]["ms_per_launch"] for k in
+                                ("proj_keys", "proj_qmeans", "score_select",
+                                 "block_scores", "topk") if k in ks)
+        bs = ks.get("block_scores")
+        if bs:
+            res["block_scores_tflops_alg"] = (n_ret * cand_keys * 2 * w.r /
+                                              (bs["ms_per_launch"] / 1e3) / 1e12)
+        res["workspace_gib"] = ws.numel() / 2**30
     del x, out, ws
     torch.cuda.empty_cache()
     return res
@@ -401,6 +419,17 @@ def main():
     rtp.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    def copy_probe():
+        # a plain device copy of known size, for calibrating byte counters
+        n = int(args.copy_probe_gib * 2**30)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 2 x {n} bytes copied")
+        del src, dst
+
     if args.leg:
         if args.leg == "decode":
             res = bench_decode(rtp, torch, DECODE_32x256K, args.steps,
@@ -412,6 +441,8 @@ def main():
             res = bench_prefill(rtp, torch, w, args.steps, args.warmup,
                                 dense=args.leg in ("dense", "dense1m"),
                                 full=args.leg == "full")
+        if args.copy_probe_gib > 0:
+            copy_probe()
         print(json.dumps({"leg": args.leg, **res}), flush=True)
         return
     main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup)
@@ -458,14 +489,7 @@ def main():
         log(f"[bench] 128K with full retrieval heads: "
             f"{extra['full_retrieval_128k']['ms_per_step']:.2f} ms/step")
     if args.copy_probe_gib > 0:
-        n = int(args.copy_probe_gib * 2**30)
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: 2 x {n} bytes copied")
-        del src, dst
+        copy_probe()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(PREFILL_128K, main["attn_pairs"]["retrieval"],

@@ -32,9 +32,14 @@ HIPFLAGS = [
 # instead of in AGPRs that need a copy per value (the sparse kernel and the
 # decode kernel are no faster with it and keep the default).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# The indexer is built without NaN-preserving float semantics: its block
+# scores are maxima over MFMA results, and with NaNs honoured every operand of
+# a max is first canonicalised (one extra VALU op per value, which made the
+# scoring loop VALU-bound). Its selection logic compares integer order keys;
+# a NaN score is not a supported input there either way (the max ignores it).
 EXTRA_FLAGS = {
     "attn_window.hip": VGPR_FORM,
-    "indexer.hip": VGPR_FORM,
+    "indexer.hip": VGPR_FORM + ["-fno-honor-nans"],
 }
 
 

@@ -3,9 +3,9 @@
 #include "common.h"
 #include "../../include/rtp.h"
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
-#include <optional>
 #include <string>
 #include <vector>
 
@@ -60,8 +60,11 @@ int check_indexer(int n_ret, int r, int block, int top_k) {
   return RTP_OK;
 }
 
+// Prefill workspace. The indexer's scratch and V^T share the first region:
+// the indexer runs first, and V^T (needed only by the attention kernels) is
+// written after it has finished, on the same stream.
 struct PrefillLayout {
-  size_t vt, khi, klo, qhi, qlo, sc, sel, cnt, total;
+  size_t vt, idx, sel, cnt, total;
 };
 
 // n_sel: retrieval heads that select (0 when none runs the indexer)
@@ -70,16 +73,17 @@ PrefillLayout prefill_layout(int S, int Hkv, int n_ret, int r, int top_k,
   using rtp::align256;
   const size_t n_b = (size_t)(S + 63) / 64, S_pad = n_b * 64;
   PrefillLayout L;
+  const size_t vt_bytes = align256((size_t)Hkv * rtp::kD * S_pad * 2);
+  const size_t idx_bytes =
+      n_sel ? rtp::indexer_sizes(n_sel, (int)n_b, r, top_k).total : 0;
   size_t off = 0;
-  L.vt = off;  off += align256((size_t)Hkv * rtp::kD * S_pad * 2);
-  L.khi = off; off += align256((size_t)n_ret * S_pad * r * 2);
-  L.klo = off; off += align256((size_t)n_ret * S_pad * r * 2);
-  L.qhi = off; off += align256((size_t)n_sel * n_b * r * 2);
-  L.qlo = off; off += align256((size_t)n_sel * n_b * r * 2);
-  L.sc = off;  off += align256((size_t)n_sel * rtp::tri_rows((int64_t)n_b) * 4);
+  L.vt = 0;
+  L.idx = 0;
+  off = std::max(vt_bytes, idx_bytes);
   L.sel = off; off += align256((size_t)n_sel * n_b * (top_k + 2) * 4);
   L.cnt = off; off += align256((size_t)n_sel * n_b * 4);
   L.total = off;
+  (void)n_ret;
   return L;
 }
 
@@ -248,8 +252,7 @@ size_t rtp_dense_workspace_bytes(int S, int Hq, int Hkv, int d) {
 static int run_indexer(const void* q, const void* k, int S, int Hq, int Hkv,
                        const HeadInfo& hi, const float* p_q, const float* p_k,
                        int r, int top_k, int32_t* sel, int32_t* sel_count,
-                       float* kth, float* cent, char* ws,
-                       const PrefillLayout& L, hipStream_t st,
+                       float* kth, float* cent, char* scratch, hipStream_t st,
                        bool keys_only) {
   rtp::IndexerLaunch a;
   a.q = static_cast<const rtp::u16*>(q);
@@ -258,18 +261,13 @@ static int run_indexer(const void* q, const void* k, int S, int Hq, int Hkv,
   a.p_k = p_k;
   a.S = S;
   a.n_b = (S + 63) / 64;
-  a.S_pad = a.n_b * 64;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.n_ret = hi.n_ret;
   a.r = r;
   a.top_k = top_k;
   a.ret_heads = hi.ret_heads.data();
-  a.khi = reinterpret_cast<rtp::u16*>(ws + L.khi);
-  a.klo = reinterpret_cast<rtp::u16*>(ws + L.klo);
-  a.qhi = reinterpret_cast<rtp::u16*>(ws + L.qhi);
-  a.qlo = reinterpret_cast<rtp::u16*>(ws + L.qlo);
-  a.scores = reinterpret_cast<float*>(ws + L.sc);
+  a.scratch = scratch;
   a.sel = sel;
   a.sel_cnt = sel_count;
   a.kth = kth;
@@ -297,7 +295,7 @@ int rtp_indexer_select(const void* q, const void* k, int S, int Hq, int Hkv,
   const PrefillLayout L = prefill_layout(S, Hkv, hi.n_ret, r, top_k, hi.n_ret);
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
   return run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, sel, sel_count,
-                     kth_scores, centroids, static_cast<char*>(ws), L,
+                     kth_scores, centroids, static_cast<char*>(ws) + L.idx,
                      reinterpret_cast<hipStream_t>(stream), false);
 }
 
@@ -349,10 +347,39 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   char* w = static_cast<char*>(ws);
   const int n_b = (S + 63) / 64, S_pad = n_b * 64;
 
-  // V^T first: both attention kernels read it
+  // The indexer (or the key projection alone, for the centroids) runs
+  // first: its scratch is the region V^T takes afterwards.
+  const int32_t* sel_use = sel_in;
+  const int32_t* cnt_use = sel_count_in;
+  hipError_t e = hipSuccess;
+  if (select) {
+    int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
+    int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
+    if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
+                              nullptr, centroids, w + L.idx, st, false))
+      return err;
+    sel_use = s;
+    cnt_use = c;
+  } else {
+    if (!full && hi.n_ret > 0 && sel_out) {
+      const size_t n = (size_t)hi.n_ret * n_b;
+      e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
+                         hipMemcpyDeviceToDevice, st);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(sel_count_out, sel_count_in, n * 4,
+                           hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return hip_fail(e, "selection copy");
+    }
+    if (centroids && hi.n_ret > 0) {  // the key projection alone
+      if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, 0, nullptr,
+                                nullptr, nullptr, centroids, nullptr, st, true))
+        return err;
+    }
+  }
+  // V^T: both attention kernels read it
   rtp::u16* vt = reinterpret_cast<rtp::u16*>(w + L.vt);
-  hipError_t e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt,
-                                         Hkv, S, S_pad, st);
+  e = rtp::launch_transpose_v(static_cast<const rtp::u16*>(v), vt, Hkv, S,
+                              S_pad, st);
   if (e != hipSuccess) return hip_fail(e, "transpose launch");
   // Full retrieval heads join the window kernel with a window of S.
   std::vector<int32_t> head_window;
@@ -368,8 +395,8 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   a.vt = vt;
   a.out = static_cast<rtp::u16*>(out);
   a.lse = lse;
-  a.sel = sel_in;
-  a.sel_cnt = sel_count_in;
+  a.sel = sel_use;
+  a.sel_cnt = cnt_use;
   a.sel_stride = top_k + 2;
   a.S = S;
   a.S_pad = S_pad;
@@ -381,49 +408,27 @@ int prefill_impl(const void* q, const void* k, const void* v, int S, int Hq,
   a.head_window = head_window.empty() ? nullptr : head_window.data();
   const uint8_t* sparse_heads = full ? nullptr : is_retrieval;
 
-  // The indexer feeds only the retrieval heads, so on long sequences the
-  // window heads attend on the device's auxiliary stream while it runs. Its
-  // cost grows with S^2 and the window heads' with S w: at 1M tokens this
-  // hides most of the indexer (-2.7% per layer), at 128K the window kernel
-  // fills every CU and the gain is 0.5%, so shorter sequences stay on one
-  // stream (which also keeps each kernel's time measurable on its own).
+  // On long sequences the window heads attend on the device's auxiliary
+  // stream while the block-sparse heads run on the caller's stream: the
+  // window kernel is bound by the matrix cores, the block-sparse kernel at
+  // 1M tokens by its K/V gathers, so the two share the GPU well. Up to 4096
+  // blocks every kernel fills the GPU alone; there they run one after the
+  // other (which also keeps each kernel's time measurable on its own).
   constexpr int kForkMinBlocks = 4096;
-  const bool fork = select && hi.n_ret < Hq && n_b > kForkMinBlocks;
-  std::optional<rtp::AuxFork> aux;
+  const bool sparse_part = !full && hi.n_ret > 0;
+  const bool fork = sparse_part && hi.n_ret < Hq && n_b > kForkMinBlocks;
   if (fork) {
-    aux.emplace(st);
-    if ((e = aux->status()) != hipSuccess) return hip_fail(e, "stream fork");
-    e = rtp::launch_attention(a, sparse_heads, aux->stream(), rtp::kAttnWindow);
+    rtp::AuxFork aux(st);
+    if ((e = aux.status()) != hipSuccess) return hip_fail(e, "stream fork");
+    e = rtp::launch_attention(a, sparse_heads, aux.stream(), rtp::kAttnWindow);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
+    e = rtp::launch_attention(a, sparse_heads, st, rtp::kAttnSparse);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if ((e = aux.join()) != hipSuccess) return hip_fail(e, "stream join");
+    return RTP_OK;
   }
-  bool centroids_done = !centroids || hi.n_ret == 0;
-  if (select) {
-    int32_t* s = sel_out ? sel_out : reinterpret_cast<int32_t*>(w + L.sel);
-    int32_t* c = sel_count_out ? sel_count_out : reinterpret_cast<int32_t*>(w + L.cnt);
-    if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, top_k, s, c,
-                              nullptr, centroids, w, L, st, false))
-      return err;
-    a.sel = s;
-    a.sel_cnt = c;
-    centroids_done = true;
-  } else if (!full && hi.n_ret > 0 && sel_out) {
-    const size_t n = (size_t)hi.n_ret * n_b;
-    e = hipMemcpyAsync(sel_out, sel_in, n * (top_k + 2) * 4,
-                       hipMemcpyDeviceToDevice, st);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(sel_count_out, sel_count_in, n * 4,
-                         hipMemcpyDeviceToDevice, st);
-    if (e != hipSuccess) return hip_fail(e, "selection copy");
-  }
-  if (!centroids_done) {  // the key projection alone
-    if (int err = run_indexer(q, k, S, Hq, Hkv, hi, p_q, p_k, r, 0, nullptr,
-                              nullptr, nullptr, centroids, w, L, st, true))
-      return err;
-  }
-  e = rtp::launch_attention(a, sparse_heads, st,
-                            fork ? rtp::kAttnSparse : rtp::kAttnAll);
+  e = rtp::launch_attention(a, sparse_heads, st, rtp::kAttnAll);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (fork && (e = aux->join()) != hipSuccess) return hip_fail(e, "stream join");
   return RTP_OK;
 }
 }  // namespace

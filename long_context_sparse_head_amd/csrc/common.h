@@ -113,6 +113,11 @@ class AuxFork {
   bool locked_ = false, joined_ = false;
 };
 
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline int64_t tri_rows(int64_t n_b) {  // candidates of rows 2..n_b-1
+  return n_b >= 3 ? (n_b - 2) * (n_b - 1) / 2 : 0;
+}
+
 // ---------------------------------------------------------------- launchers
 // All launchers enqueue on `stream` and return the launch status.
 
@@ -138,11 +143,52 @@ hipError_t launch_window_heads(const AttnLaunch& a, const uint8_t* is_ret,
 hipError_t launch_attention(const AttnLaunch& a, const uint8_t* is_ret,
                             hipStream_t st, int parts = kAttnAll);
 
+// Scratch of the indexer, per call:
+//  - projected keys of every retrieval head in the MFMA operand order of
+//    the scoring kernel: per (head, key block) 4*r/16 KiB (hi and lo bf16
+//    parts of 64 keys x r);
+//  - projected query-block means, hi and lo bf16 parts, [n_ret, n_b, r];
+//  - up to kStreamMinBlocks key blocks: the score rows (fp32, the lower
+//    triangle of each head);
+//  - longer sequences: the fused kernel's candidate buffers, one per row of
+//    each wave slot, `cap` entries of 8 bytes (order key, block), and a work
+//    counter.
+constexpr int kScoreMaxWG = 512;  // persistent workgroups (2 per CU)
+constexpr int kStreamMinBlocks = 4097;
+struct IndexerSizes {
+  size_t kop, qpart, scores, buf, counter, total;
+  int cap, n_items, n_wg;
+  bool fused;
+};
+__host__ inline IndexerSizes indexer_sizes(int n_ret, int n_b, int r,
+                                           int top_k) {
+  IndexerSizes z;
+  const int need = top_k + 1;  // the top_k + 1 best are kept (for s_{k+1})
+  const int c = 2 * need > need + 64 ? 2 * need : need + 64;
+  z.cap = (c + 63) / 64 * 64;
+  // a row has at most n_b - 2 candidates: a buffer with 64 slots more than
+  // that is never shrunk (so cap >= need + 64 wherever shrinking happens)
+  const int all = (n_b + 63) / 64 * 64 + 64;
+  if (z.cap > all) z.cap = all;
+  const int tiles = (n_b + 63) / 64;
+  z.n_items = 4 * n_ret * ((tiles + 3) / 4);
+  int wg = (z.n_items + 3) / 4;
+  z.n_wg = wg < 1 ? 1 : (wg > kScoreMaxWG ? kScoreMaxWG : wg);
+  z.fused = n_b >= kStreamMinBlocks;
+  z.kop = align256((size_t)n_ret * n_b * 256 * r);
+  z.qpart = align256((size_t)n_ret * n_b * r * 2);
+  z.scores = z.fused ? 0 : align256((size_t)n_ret * tri_rows(n_b) * 4);
+  z.buf = z.fused ? align256((size_t)z.n_wg * 4 * 64 * z.cap * 8) : 0;
+  z.counter = 256;
+  z.total = z.kop + 2 * z.qpart + z.scores + z.buf + z.counter;
+  return z;
+}
+
 struct IndexerLaunch {
   const u16* q; const u16* k; const float* p_q; const float* p_k;
-  int S, S_pad, n_b, Hq, Hkv, n_ret, r, top_k;
+  int S, n_b, Hq, Hkv, n_ret, r, top_k;
   const uint8_t* ret_heads;  // host: query head of each retrieval index
-  u16* khi; u16* klo; u16* qhi; u16* qlo; float* scores;
+  char* scratch;             // indexer_sizes(...).total bytes, 256-aligned
   int32_t* sel; int32_t* sel_cnt; float* kth; float* centroids;
   bool keys_only = false;  // only the key projection (and centroids)
 };
@@ -171,9 +217,5 @@ hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
                                 int Lmax, int Hkv, int n_ret, int r, int G,
                                 const uint8_t* ret_heads, hipStream_t st);
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline int64_t tri_rows(int64_t n_b) {  // candidates of rows 2..n_b-1
-  return n_b >= 3 ? (n_b - 2) * (n_b - 1) / 2 : 0;
-}
 
 }  // namespace rtp

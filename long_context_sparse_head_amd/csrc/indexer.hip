@@ -1,5 +1,5 @@
-// Retrieval-head indexer for gfx950: low-rank projection, block scoring and
-// per-query-block top-k selection.
+// Retrieval-head indexer for gfx950: low-rank projection, and block scoring
+// fused with the per-query-block top-k selection.
 //
 // What it computes (RTPurboV2 article, paragraph on the low-rank projector
 // that maps the head dimension to r = 16; aitop.news summary of "Full
@@ -16,122 +16,229 @@
 // high and low bf16 parts (a = a_hi + a_lo): a.b ~ a_hi.b_hi + a_hi.b_lo +
 // a_lo.b_hi, i.e. three MFMAs per tile (error ~1e-5 relative, well inside the
 // 1e-4 tie band), instead of one fp32-VALU pass that would be ~5x slower.
+//
+// The RTPurboV2 article criticises fixed, materialised top-k budgets for
+// their cost at long context; here the score rows are never written out.
+// Each row's scores stream through a register of the lane that owns the row,
+// and only the ones that can still enter its top k + 1 go to a small
+// candidate buffer (see score_select_kernel). At 1M tokens that replaces
+// 11.5 GiB of score rows by about 0.6 GB of buffers.
 #include "common.h"
 #include "select.h"
 
 namespace rtp {
 
 struct ProjArgs {
-  int S, S_pad, n_b, r;
-  uint8_t kvh_of_rho[kMaxHeads];
-  uint8_t head_of_rho[kMaxHeads];
+  int S, n_b, r, n_ret;
+  uint8_t head_of_rho[kMaxHeads];     // query head of retrieval index rho
+  uint8_t grp_kvh[kMaxHeads];         // KV head of group slot j
+  uint8_t grp_first[kMaxHeads + 1];   // retrieval indices of slot j:
+                                      // grp_first[j] .. grp_first[j+1]-1
 };
 
-// ---- projection of keys: grid (n_ret, S_pad/64), one wave per 64 keys.
-__global__ __launch_bounds__(64) void proj_keys_kernel(
+// k-th / (k+1)-th score slots are written as bit patterns: this file is
+// built without NaN semantics, and an absent score is a quiet NaN.
+constexpr uint32_t kQuietNaN = 0x7fc00000u;
+__device__ __forceinline__ uint32_t order_key_bits(uint32_t key) {
+  return (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
+}
+__device__ __forceinline__ void put_score(float* kth, size_t i, bool have,
+                                          uint32_t key) {
+  reinterpret_cast<uint32_t*>(kth)[i] = have ? order_key_bits(key) : kQuietNaN;
+}
+
+// Projected keys in the A-operand order of the scoring MFMA: for head rho
+// and key block kb, 4*R16 chunks of 1 KiB; chunk ((mt*2 + part)*R16 + rs)
+// holds, at 16-byte slot L (0..63), the 8 values
+//     k^[64 kb + 32 mt + L%32][16 rs + 8 (L/32) + e], e = 0..7
+// of the hi (part 0) or lo (part 1) bf16 part: exactly what lane L feeds to
+// v_mfma_f32_32x32x16_bf16 for the 32-key tile mt, so every operand load is
+// one contiguous 1 KiB read per wave.
+__host__ __device__ inline size_t kop_block_elems(int r) { return 2048 * (r / 16); }
+
+// ---- projection of keys: grid (ceil(n_b/4), groups), 4 waves, a wave per
+// key block and a lane per key. The group's K is read once; every retrieval
+// head of the group projects it (fp32 VALU, P staged in LDS 16 rows at a
+// time). Optionally also the per-block centroids (mean of the projected
+// keys over the block's tokens).
+__global__ __launch_bounds__(256) void proj_keys_kernel(
     const u16* __restrict__ k, const float* __restrict__ p_k, const ProjArgs pa,
-    u16* __restrict__ khi, u16* __restrict__ klo, float* __restrict__ cent) {
+    u16* __restrict__ kop, float* __restrict__ cent) {
   __shared__ __attribute__((aligned(16))) float P[16 * kD];
-  const int rho = blockIdx.x, kb = blockIdx.y, lane = threadIdx.x;
-  const int S = pa.S, r = pa.r;
-  const int g = pa.kvh_of_rho[rho];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kb = blockIdx.x * 4 + wave;
+  const int j = blockIdx.y;
+  const int S = pa.S, r = pa.r, n_b = pa.n_b;
+  const int g = pa.grp_kvh[j];
   const int key = kb * 64 + lane;
-  const u16* krow = k + ((size_t)g * S + (key < S ? key : 0)) * kD;
-  for (int rc = 0; rc < r; rc += 16) {
-    const float* src = p_k + ((size_t)rho * r + rc) * kD;
+  const bool kb_ok = kb < n_b;
+  const bool valid = kb_ok && key < S;
+  uint4 kr[16];
+  {
+    const u16* krow = k + ((size_t)g * S + (valid ? key : 0)) * kD;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      reinterpret_cast<float4*>(P)[lane + 64 * i] =
-          reinterpret_cast<const float4*>(src)[lane + 64 * i];
-    __syncthreads();
-    float acc[16];
+    for (int dc = 0; dc < 16; ++dc)
+      kr[dc] = valid ? reinterpret_cast<const uint4*>(krow)[dc]
+                     : make_uint4(0, 0, 0, 0);
+  }
+  const int mt = lane >> 5, L0 = lane & 31;
+  const int R16 = r / 16;
+  for (int rho = pa.grp_first[j]; rho < pa.grp_first[j + 1]; ++rho) {
+    u16* kout = kop ? kop + ((size_t)rho * n_b + (kb_ok ? kb : 0)) * kop_block_elems(r)
+                    : nullptr;
+    for (int rc = 0; rc < r; rc += 16) {
+      __syncthreads();  // the previous rows of P are no longer read
+      const float* src = p_k + ((size_t)rho * r + rc) * kD;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-    for (int dc = 0; dc < 16; ++dc) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (key < S) raw = *reinterpret_cast<const uint4*>(krow + dc * 8);
-      float kf[8];
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      for (int i = 0; i < 2; ++i)
+        reinterpret_cast<float4*>(P)[threadIdx.x + 256 * i] =
+            reinterpret_cast<const float4*>(src)[threadIdx.x + 256 * i];
+      __syncthreads();
+      if (!kb_ok) continue;
+      float acc[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int dc = 0; dc < 16; ++dc) {
+        const uint32_t w[4] = {kr[dc].x, kr[dc].y, kr[dc].z, kr[dc].w};
+        float kf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[2 * e] = __uint_as_float(w[e] << 16);
+          kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const float4 p0 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8);
+          const float4 p1 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8 + 4);
+          float x = acc[rr];
+          x = fmaf(p0.x, kf[0], x); x = fmaf(p0.y, kf[1], x);
+          x = fmaf(p0.z, kf[2], x); x = fmaf(p0.w, kf[3], x);
+          x = fmaf(p1.x, kf[4], x); x = fmaf(p1.y, kf[5], x);
+          x = fmaf(p1.z, kf[6], x); x = fmaf(p1.w, kf[7], x);
+          acc[rr] = x;
+        }
+      }
+      // hi / lo bf16 parts, written in the operand order (not needed when
+      // only the centroids are asked for)
+      if (kop) {
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u16 h0 = f2bf(acc[2 * i]), h1 = f2bf(acc[2 * i + 1]);
+          const u16 l0 = f2bf(acc[2 * i] - bf2f(h0));
+          const u16 l1 = f2bf(acc[2 * i + 1] - bf2f(h1));
+          hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        const int rs = rc / 16;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int L = L0 + 32 * half;
+          uint4* dh = reinterpret_cast<uint4*>(
+              kout + (size_t)(((mt * 2 + 0) * R16 + rs) * 64 + L) * 8);
+          uint4* dl = reinterpret_cast<uint4*>(
+              kout + (size_t)(((mt * 2 + 1) * R16 + rs) * 64 + L) * 8);
+          *dh = make_uint4(hw[4 * half], hw[4 * half + 1], hw[4 * half + 2],
+                           hw[4 * half + 3]);
+          *dl = make_uint4(lw[4 * half], lw[4 * half + 1], lw[4 * half + 2],
+                           lw[4 * half + 3]);
+        }
+      }
+      if (cent) {
+        const int cnt = min(64, S - kb * 64);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          float v = key < S ? acc[rr] : 0.f;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+          if (lane == 0)
+            cent[((size_t)rho * n_b + kb) * r + rc + rr] = v / (float)cnt;
+        }
+      }
+    }
+  }
+}
+
+// ---- block means of queries, projected: grid (ceil(n_b/4), n_ret), 4
+// waves, a wave per query block. Lane l reads 16 bytes (8 values of d) of
+// rows 4i + l/16, i = 0..15: every load instruction reads 4 whole rows, and
+// all 16 are in flight at once. Also clears the scoring kernel's work
+// counter, so the two launches need nothing else between them.
+__global__ __launch_bounds__(256) void proj_qmeans_kernel(
+    const u16* __restrict__ q, const float* __restrict__ p_q, const ProjArgs pa,
+    u16* __restrict__ qhi, u16* __restrict__ qlo, int* __restrict__ counter) {
+  __shared__ float mean[4][kD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qb = blockIdx.x * 4 + wave, rho = blockIdx.y;
+  const int S = pa.S, r = pa.r, n_b = pa.n_b;
+  if (counter && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    *counter = 0;
+  if (qb < n_b) {
+    const int h = pa.head_of_rho[rho];
+    const int rows = min(64, S - qb * 64);
+    const int c = lane & 15, s = lane >> 4;
+    const u16* base = q + ((size_t)h * S + (size_t)qb * 64) * kD + 8 * c;
+    uint4 w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 4 * i + s;
+      w[i] = row < rows ? *reinterpret_cast<const uint4*>(base + (size_t)row * kD)
+                        : make_uint4(0, 0, 0, 0);
+    }
+    float a[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t u[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kf[2 * e] = __uint_as_float(w[e] << 16);
-        kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const float4 pa0 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8);
-        const float4 pa1 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8 + 4);
-        float x = acc[rr];
-        x = fmaf(pa0.x, kf[0], x); x = fmaf(pa0.y, kf[1], x);
-        x = fmaf(pa0.z, kf[2], x); x = fmaf(pa0.w, kf[3], x);
-        x = fmaf(pa1.x, kf[4], x); x = fmaf(pa1.y, kf[5], x);
-        x = fmaf(pa1.z, kf[6], x); x = fmaf(pa1.w, kf[7], x);
-        acc[rr] = x;
+        a[2 * e] += __uint_as_float(u[e] << 16);
+        a[2 * e + 1] += __uint_as_float(u[e] & 0xffff0000u);
       }
     }
-    // split into high/low bf16 parts for the scoring MFMAs
-    uint32_t hw[8], lw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u16 h0 = f2bf(acc[2 * i]), h1 = f2bf(acc[2 * i + 1]);
-      const u16 l0 = f2bf(acc[2 * i] - bf2f(h0));
-      const u16 l1 = f2bf(acc[2 * i + 1] - bf2f(h1));
-      hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int e = 0; e < 8; ++e) {
+      a[e] += __shfl_xor(a[e], 16);
+      a[e] += __shfl_xor(a[e], 32);
     }
-    const size_t o = ((size_t)rho * pa.S_pad + key) * r + rc;
-    uint4* dh = reinterpret_cast<uint4*>(khi + o);
-    uint4* dl = reinterpret_cast<uint4*>(klo + o);
-    dh[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    dh[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-    dl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    dl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-    if (cent) {
-      const int cnt = min(64, S - kb * 64);
+    if (s == 0) {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float v = key < S ? acc[rr] : 0.f;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0) cent[((size_t)rho * pa.n_b + kb) * r + rc + rr] = v / (float)cnt;
-      }
+      for (int e = 0; e < 8; ++e) mean[wave][8 * c + e] = a[e] / (float)rows;
     }
-    __syncthreads();
   }
-}
-
-// ---- block means of queries, projected: grid (n_ret, n_b), one wave each.
-__global__ __launch_bounds__(64) void proj_qmeans_kernel(
-    const u16* __restrict__ q, const float* __restrict__ p_q, const ProjArgs pa,
-    u16* __restrict__ qhi, u16* __restrict__ qlo) {
-  __shared__ float mean[kD];
-  const int rho = blockIdx.x, qb = blockIdx.y, lane = threadIdx.x;
-  const int S = pa.S, r = pa.r;
-  const int h = pa.head_of_rho[rho];
-  const int rows = min(64, S - qb * 64);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(
-      q + ((size_t)h * S + (size_t)qb * 64) * kD) + lane;
-  float s0 = 0.f, s1 = 0.f;
-  for (int i = 0; i < rows; ++i) {
-    const uint32_t w = base[(size_t)i * (kD / 2)];
-    s0 += __uint_as_float(w << 16);
-    s1 += __uint_as_float(w & 0xffff0000u);
-  }
-  mean[2 * lane] = s0 / (float)rows;
-  mean[2 * lane + 1] = s1 / (float)rows;
   __syncthreads();
-  for (int rr = lane; rr < r; rr += 64) {
-    const float* prow = p_q + ((size_t)rho * r + rr) * kD;
-    float acc = 0.f;
-    for (int d = 0; d < kD; ++d) acc = fmaf(prow[d], mean[d], acc);
-    const u16 hi = f2bf(acc);
-    const size_t o = ((size_t)rho * pa.n_b + qb) * r + rr;
-    qhi[o] = hi;
-    qlo[o] = f2bf(acc - bf2f(hi));
+  if (qb < n_b) {
+    for (int rr = lane; rr < r; rr += 64) {
+      const float4* prow =
+          reinterpret_cast<const float4*>(p_q + ((size_t)rho * r + rr) * kD);
+      float acc = 0.f;
+#pragma unroll 8
+      for (int d4 = 0; d4 < kD / 4; ++d4) {
+        const float4 p = prow[d4];
+        acc = fmaf(p.x, mean[wave][4 * d4], acc);
+        acc = fmaf(p.y, mean[wave][4 * d4 + 1], acc);
+        acc = fmaf(p.z, mean[wave][4 * d4 + 2], acc);
+        acc = fmaf(p.w, mean[wave][4 * d4 + 3], acc);
+      }
+      const u16 hi = f2bf(acc);
+      const size_t o = ((size_t)rho * n_b + qb) * r + rr;
+      qhi[o] = hi;
+      qlo[o] = f2bf(acc - bf2f(hi));
+    }
   }
 }
 
-// ---- block scores: grid (ceil(n_b/128), ceil(n_b/KBC), n_ret), 4 waves.
+// ------------------------------------------- short sequences: score rows
+// Up to kStreamMinBlocks key blocks (256K tokens) a head's score rows take at
+// most 33.5 MB, and writing them out, then selecting each row in its own
+// workgroup, keeps far more waves busy than one wave per 64 rows could: the
+// rows are written as a lower triangle per head and the top k of each row
+// found by the block-wide select. Longer sequences use the fused kernel
+// below, whose memory does not grow with the square of the length.
+// ---- block scores of short sequences (up to kStreamMinBlocks blocks):
+// grid (ceil(n_b/128), ceil(n_b/KBC), n_ret), 4 waves.
 // Workgroup = 128 query blocks (32 per wave, along the MFMA N dimension) x a
 // chunk of KBC key blocks. Key blocks are staged in LDS KBI at a time (the
 // 64 projected keys of each, hi and lo parts); each wave computes the 64 x 32
@@ -146,9 +253,8 @@ constexpr int KBC = 48;
 
 template <int R16>
 __global__ __launch_bounds__(256) void block_scores_kernel(
-    const u16* __restrict__ khi, const u16* __restrict__ klo,
-    const u16* __restrict__ qhi, const u16* __restrict__ qlo,
-    float* __restrict__ scores, int S_pad, int n_b) {
+    const u16* __restrict__ kop, const u16* __restrict__ qhi,
+    const u16* __restrict__ qlo, float* __restrict__ scores, int n_b) {
   constexpr int r = 16 * R16;
   constexpr int RS = r + 8;  // LDS row stride (bf16), 16-byte pad
   constexpr int KBI = R16 >= 4 ? 1 : 4 / R16;  // key blocks per stage
@@ -188,8 +294,7 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
   static_assert(NCH % 256 == 0, "whole chunks per thread");
   constexpr int PER_T = NCH / 256;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u16* kh = khi + (size_t)rho * S_pad * r;
-  const u16* kl = klo + (size_t)rho * S_pad * r;
+  const u16* kop_h = kop + (size_t)rho * n_b * kop_block_elems(r);
   const int nst = (kb_end - kb_begin + KBI - 1) / KBI;
   // key blocks past the chunk re-read its last block (never used)
   auto gload = [&](int stg, u32x4 (&reg)[PER_T]) {
@@ -199,7 +304,11 @@ __global__ __launch_bounds__(256) void block_scores_kernel(
       const int part = c / (SROWS * CH_PER_ROW), cc = c % (SROWS * CH_PER_ROW);
       const int row = cc / CH_PER_ROW, ch = cc % CH_PER_ROW;
       const int kb = min(kb_begin + stg * KBI + row / 64, kb_end - 1);
-      const u16* src = (part ? kl : kh) + ((size_t)kb * 64 + (row & 63)) * r + ch * 8;
+      // (key m, values 8 ch .. 8 ch + 7) of block kb in the operand order
+      const int m = row & 63;
+      const int L = (m & 31) + 32 * (ch & 1);
+      const u16* src = kop_h + (size_t)kb * kop_block_elems(r) +
+                       ((((m >> 5) * 2 + part) * R16 + (ch >> 1)) * 64 + L) * 8;
       reg[i] = *reinterpret_cast<const u32x4*>(src);
     }
   };
@@ -280,7 +389,7 @@ __global__ __launch_bounds__(256) void topk_kernel(
   int32_t* out = sel + row_id * stride;
   const float* row = scores + (size_t)rho * tri_rows(n_b) +
                      (qb >= 2 ? (int64_t)(qb - 2) * (qb - 1) / 2 : 0);
-  const float qnan = __builtin_nanf("");
+  uint32_t* kthb = reinterpret_cast<uint32_t*>(kth);
 
   if (n_c <= top_k || top_k == 0) {
     // keep every candidate, or none when top_k == 0
@@ -303,9 +412,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
       }
       mn = block_min_u32(mn, sh.tmp);
       mx = block_max_u32(mx, sh.tmp);
-      if (tid == 0) {
-        kth[row_id * 2 + 0] = (top_k >= 1 && n_c == top_k) ? order_key_inv(mn) : qnan;
-        kth[row_id * 2 + 1] = (top_k == 0 && n_c >= 1) ? order_key_inv(mx) : qnan;
+      if (tid == 0) {  // absent scores are quiet NaNs, written as bits
+        kthb[row_id * 2 + 0] = (top_k >= 1 && n_c == top_k) ? order_key_bits(mn) : kQuietNaN;
+        kthb[row_id * 2 + 1] = (top_k == 0 && n_c >= 1) ? order_key_bits(mx) : kQuietNaN;
       }
     }
     return;
@@ -350,10 +459,718 @@ __global__ __launch_bounds__(256) void topk_kernel(
     below = block_max_u32(below, sh.tmp);
     const int count_ge = res.count_ge;
     if (tid == 0) {
-      kth[row_id * 2 + 0] = order_key_inv(res.T);
-      kth[row_id * 2 + 1] = count_ge >= top_k + 1 ? order_key_inv(res.T)
-                                                  : order_key_inv(below);
+      kthb[row_id * 2 + 0] = order_key_bits(res.T);
+      kthb[row_id * 2 + 1] = order_key_bits(count_ge >= top_k + 1 ? res.T : below);
     }
+  }
+}
+
+// ---------------------------------------------------------------- scoring
+// Global-memory accesses of the scoring kernel go through address-space-1
+// pointers, so they compile to global (not FLAT) instructions: a FLAT load
+// also counts against the LDS wait counter, which would make every wait in
+// the prefetch ring a full wait.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
+// A candidate-buffer entry: (order key of the score, key block).
+typedef uint32_t entry_t __attribute__((ext_vector_type(2)));
+
+struct ScoreArgs {
+  const u16* kop;               // projected keys, operand order
+  const u16* qhi; const u16* qlo;
+  entry_t* buf;                 // [4 n_wg][64][cap] (order key, block)
+  int* counter;                 // next work item (cleared before launch)
+  int32_t* sel; int32_t* sel_cnt; float* kth;
+  int n_b, n_ret, top_k, cap, n_tiles, n_items;
+};
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    v = min(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+    v = max(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Stores of one lane become visible to the other lanes of its wave (and
+// workgroup) before the loads that follow.
+__device__ __forceinline__ void fence_wg() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+}
+
+__device__ __forceinline__ bool nan_key(uint32_t x) {
+  return x > 0xff800000u || x < 0x007fffffu;
+}
+
+// Shrinks one row's candidate buffer rb[0..c) in place, in order, to a set
+// that still holds the row's `need` best entries (order key descending, then
+// lower position, i.e. lower block, first). Every entry removed is below
+// every entry kept, so after it `thr` (returned) bounds what can still
+// enter: a later block enters only with a key strictly above thr, because
+// at least `need` kept entries are >= thr and come from lower blocks.
+//
+// Normally one histogram pass of the keys' values (256 bins between the
+// row's minimum and maximum, as in the block-wide select) finds the bin
+// holding the need-th best; everything from that bin up is kept and thr is
+// the least kept key. When that frees fewer than 64 slots (many equal or
+// crowded values), the exact need-th key T is found by radix select and
+// exactly `need` entries are kept (those above T, then the first ones equal
+// to T), with thr = T. One wave; returns the new count.
+__device__ __forceinline__ int compact_row(entry_t* rb, int c, int need, int* hist,
+                           uint32_t& thr) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int e = lane; e < c; e += 64) {
+    const uint32_t x = rb[e].x;
+    if (!nan_key(x)) {
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  float flo = 0.f, scale = 0.f;
+  if (lo <= hi) {
+    flo = order_key_inv(lo);
+    const float span = order_key_inv(hi) - flo;
+    if (span > 0.f) scale = 255.99f / span;
+    if (!(scale < 1e30f)) scale = 0.f;
+  }
+  auto bin = [&](uint32_t x) -> int {
+    if (x > 0xff800000u) return 255;
+    if (x < 0x007fffffu) return 0;
+    float f = (order_key_inv(x) - flo) * scale;
+    f = fminf(fmaxf(f, 0.f), 255.f);
+    return (int)f;
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hist[lane + 64 * j] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int e = lane; e < c; e += 64) atomicAdd(&hist[bin(rb[e].x)], 1);
+  __builtin_amdgcn_wave_barrier();
+  int h[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = hist[255 - 4 * lane - j];
+    sum += h[j];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int incl = wave_incl_scan(sum);
+  const int excl = incl - sum;
+  const bool mine = excl < need && need <= incl;
+  int bstar = 0, kept = 0;
+  if (mine) {
+    int above = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (above + h[j] >= need) {
+        bstar = 255 - 4 * lane - j;
+        kept = above + h[j];
+        break;
+      }
+      above += h[j];
+    }
+  }
+  const int src = (int)__builtin_ctzll(__ballot(mine));
+  bstar = __shfl(bstar, src);
+  kept = __shfl(kept, src);
+  const bool exact = kept > c - 64;
+  uint32_t T = 0u;
+  int take_eq = 0;
+  if (exact) {
+    T = wave_kth([&](int i) { return rb[i].x; }, c, need, hist);
+    int gt = 0;
+    for (int e = lane; e < c; e += 64) gt += rb[e].x > T;
+    take_eq = need - wave_sum(gt);
+  }
+  const uint64_t below = lanes_below();
+  int w = 0, eq_seen = 0;
+  uint32_t mn = 0xffffffffu;
+  for (int e0 = 0; e0 < c; e0 += 64) {
+    const int e = e0 + lane;
+    const bool in = e < c;
+    const entry_t v = in ? rb[e] : entry_t{0u, 0u};
+    bool keep;
+    if (exact) {
+      const bool is_gt = in && v.x > T, is_eq = in && v.x == T;
+      const uint64_t beq = __ballot(is_eq);
+      keep = is_gt || (is_eq && eq_seen + __builtin_popcountll(beq & below) < take_eq);
+      eq_seen += __builtin_popcountll(beq);
+    } else {
+      keep = in && bin(v.x) >= bstar;
+    }
+    const uint64_t bk = __ballot(keep);
+    if (keep) {
+      rb[w + __builtin_popcountll(bk & below)] = v;
+      mn = min(mn, v.x);
+    }
+    w += __builtin_popcountll(bk);
+  }
+  thr = exact ? T : wave_min_u32(mn);
+  return w;
+}
+
+// ---- the same two operations with the row held in registers (buffers of up
+// to 64 * kRowRegs entries): one memory round trip per call instead of one
+// per pass. Entry i of the row sits in slot i / 64 of lane i % 64.
+constexpr int kRowRegs = 16;
+
+struct RowRegs {
+  uint32_t key[kRowRegs], kb[kRowRegs];
+  int bn[kRowRegs];  // value bin of each entry (valid after row_bins)
+  int c;
+};
+
+__device__ __forceinline__ void load_row(const entry_t* rb, int c, RowRegs& R) {
+  const int lane = threadIdx.x & 63;
+  R.c = c;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const int i = lane + 64 * j;
+    entry_t v = {0u, 0u};
+    if (i < c) v = gmem(rb)[i];
+    R.key[j] = v.x;
+    R.kb[j] = v.y;
+  }
+}
+
+// 256 bins of a linear quantisation of the entries' values between the
+// row's least and greatest (non-NaN) value; NaN keys go to the end bins.
+// Monotone: a greater value never lands in a lower bin.
+__device__ __forceinline__ void row_bins(RowRegs& R) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const uint32_t x = R.key[j];
+    if (lane + 64 * j < R.c && !nan_key(x)) {
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  float flo = 0.f, scale = 0.f;
+  if (lo <= hi) {
+    flo = order_key_inv(lo);
+    const float span = order_key_inv(hi) - flo;
+    if (span > 0.f) scale = 255.99f / span;
+    if (!(scale < 1e30f)) scale = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    const uint32_t x = R.key[j];
+    int b;
+    if (x > 0xff800000u) {
+      b = 255;
+    } else if (x < 0x007fffffu) {
+      b = 0;
+    } else {
+      const float f = fminf(fmaxf((order_key_inv(x) - flo) * scale, 0.f), 255.f);
+      b = min(max((int)f, 0), 255);
+    }
+    R.bn[j] = b;
+  }
+}
+
+// The bin holding the rank-th best entry, the count of entries in higher
+// bins and the count in that bin.
+__device__ __forceinline__ void bin_threshold(const RowRegs& R, int rank,
+                                              int* hist, int& bstar,
+                                              int& above, int& nbin) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hist[lane + 64 * j] = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j)
+    if (lane + 64 * j < R.c) atomicAdd(&hist[R.bn[j]], 1);
+  __builtin_amdgcn_wave_barrier();
+  int h[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = hist[255 - 4 * lane - j];
+    sum += h[j];
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int incl = wave_incl_scan(sum);
+  const int excl = incl - sum;
+  const bool mine = excl < rank && rank <= incl;
+  int b = 0, ab = 0, nb = 0;
+  if (mine) {
+    int run = excl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run + h[j] >= rank) {
+        b = 255 - 4 * lane - j;
+        ab = run;
+        nb = h[j];
+        break;
+      }
+      run += h[j];
+    }
+  }
+  const int src = (int)__builtin_ctzll(__ballot(mine));
+  bstar = __shfl(b, src);
+  above = __shfl(ab, src);
+  nbin = __shfl(nb, src);
+}
+
+// The rank-th largest key among the entries of bin bstar (1 <= rank <= the
+// bin's count): a 4-pass, 8-bit radix select over those entries only.
+__device__ __forceinline__ uint32_t kth_in_bin(const RowRegs& R, int bstar, int rank,
+                               int* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hist[lane + 64 * j] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) {
+      const uint32_t x = R.key[j];
+      if (lane + 64 * j < R.c && R.bn[j] == bstar && (x & pmask) == prefix)
+        atomicAdd(&hist[(x >> shift) & 255], 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    int h[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = hist[255 - 4 * lane - j];
+      sum += h[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int incl = wave_incl_scan(sum);
+    const int excl = incl - sum;
+    const bool mine = excl < rank && rank <= incl;
+    int digit = 0, run = excl;
+    if (mine) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run + h[j] >= rank) {
+          digit = 255 - 4 * lane - j;
+          break;
+        }
+        run += h[j];
+      }
+    }
+    const int src = (int)__builtin_ctzll(__ballot(mine));
+    digit = __shfl(digit, src);
+    run = __shfl(run, src);
+    prefix |= (uint32_t)digit << shift;
+    pmask |= 0xffu << shift;
+    rank -= run;
+  }
+  return prefix;
+}
+
+// compact_row for a row held in registers (same contract).
+__device__ __forceinline__ int compact_regs(entry_t* rb, RowRegs& R, int need, int* hist,
+                            uint32_t& thr) {
+  const int lane = threadIdx.x & 63;
+  row_bins(R);
+  int bstar, above, nbin;
+  bin_threshold(R, need, hist, bstar, above, nbin);
+  const bool exact = above + nbin > R.c - 64;
+  uint32_t T = 0u;
+  int take_eq = 0;
+  if (exact) {
+    T = kth_in_bin(R, bstar, need - above, hist);
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) gt += (lane + 64 * j < R.c) && R.key[j] > T;
+    take_eq = need - wave_sum(gt);
+  }
+  const uint64_t below = lanes_below();
+  int w = 0, eq_seen = 0;
+  uint32_t mn = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    if (64 * j >= R.c) break;  // wave-uniform
+    const bool in = lane + 64 * j < R.c;
+    const uint32_t x = R.key[j];
+    bool keep;
+    if (exact) {
+      const bool is_gt = in && x > T, is_eq = in && x == T;
+      const uint64_t beq = __ballot(is_eq);
+      keep = is_gt || (is_eq && eq_seen + __builtin_popcountll(beq & below) < take_eq);
+      eq_seen += __builtin_popcountll(beq);
+    } else {
+      keep = in && R.bn[j] >= bstar;
+    }
+    const uint64_t bk = __ballot(keep);
+    if (keep) {
+      gmem(rb)[w + __builtin_popcountll(bk & below)] = entry_t{x, R.kb[j]};
+      mn = min(mn, x);
+    }
+    w += __builtin_popcountll(bk);
+  }
+  thr = exact ? T : wave_min_u32(mn);
+  return w;
+}
+
+// finish_row for a row held in registers (same contract).
+__device__ __forceinline__ void finish_regs(const ScoreArgs& a, RowRegs& R, int rho, int qb,
+                            int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int top_k = a.top_k, stride = top_k + 2;
+  const int n_c = max(qb - 1, 0);
+  const size_t row_id = (size_t)rho * a.n_b + qb;
+  int32_t* out = a.sel + row_id * stride;
+  if (n_c <= top_k || top_k == 0) {
+    const bool all = top_k > 0;
+    for (int t = lane; t < stride; t += 64) {
+      int v;
+      if (all) v = t <= qb ? t : -1;
+      else v = t == 0 ? 0 : ((t == 1 && qb >= 1) ? qb : -1);
+      out[t] = v;
+    }
+    if (lane == 0) a.sel_cnt[row_id] = all ? qb + 1 : (qb >= 1 ? 2 : 1);
+    if (a.kth) {
+      uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+      for (int j = 0; j < kRowRegs; ++j) {
+        if (lane + 64 * j < R.c) {
+          mn = min(mn, R.key[j]);
+          mx = max(mx, R.key[j]);
+        }
+      }
+      mn = wave_min_u32(mn);
+      mx = wave_max_u32(mx);
+      if (lane == 0) {
+        put_score(a.kth, row_id * 2 + 0, top_k >= 1 && n_c == top_k, mn);
+        put_score(a.kth, row_id * 2 + 1, top_k == 0 && n_c >= 1, mx);
+      }
+    }
+    return;
+  }
+  // the k-th best key T, then every key above T and the first keys equal
+  // to T, in block order
+  row_bins(R);
+  int bstar, above, nbin;
+  bin_threshold(R, top_k, hist, bstar, above, nbin);
+  const uint32_t T = kth_in_bin(R, bstar, top_k - above, hist);
+  int gt = 0;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) gt += (lane + 64 * j < R.c) && R.key[j] > T;
+  const int take_eq = top_k - wave_sum(gt);
+  const uint64_t below = lanes_below();
+  int pos = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < kRowRegs; ++j) {
+    if (64 * j >= R.c) break;  // wave-uniform
+    const bool in = lane + 64 * j < R.c;
+    const uint32_t x = R.key[j];
+    const bool is_gt = in && x > T, is_eq = in && x == T;
+    const uint64_t beq = __ballot(is_eq);
+    const bool t =
+        is_gt || (is_eq && eq_seen + __builtin_popcountll(beq & below) < take_eq);
+    const uint64_t bt = __ballot(t);
+    if (t) out[1 + pos + __builtin_popcountll(bt & below)] = (int32_t)R.kb[j];
+    pos += __builtin_popcountll(bt);
+    eq_seen += __builtin_popcountll(beq);
+  }
+  if (lane == 0) {
+    out[0] = 0;
+    out[top_k + 1] = qb;
+    a.sel_cnt[row_id] = top_k + 2;
+  }
+  if (a.kth) {
+    int ge = 0;
+    uint32_t bel = 0u;
+#pragma unroll
+    for (int j = 0; j < kRowRegs; ++j) {
+      const uint32_t x = R.key[j];
+      if (lane + 64 * j < R.c) {
+        ge += x >= T;
+        if (x < T) bel = max(bel, x);
+      }
+    }
+    ge = wave_sum(ge);
+    bel = wave_max_u32(bel);
+    if (lane == 0) {
+      put_score(a.kth, row_id * 2 + 0, true, T);
+      put_score(a.kth, row_id * 2 + 1, true, ge >= top_k + 1 ? T : bel);
+    }
+  }
+}
+
+// Final choice of one row from its buffer rb[0..c) (which holds the row's
+// top_k + 1 best candidates, in block order): the layout of the selection
+// row and the k-th / (k+1)-th scores follow rtp_indexer_select.
+__device__ __forceinline__ void finish_row(const ScoreArgs& a, entry_t* rb, int c, int rho,
+                           int qb, int* hist) {
+  const int lane = threadIdx.x & 63;
+  const int top_k = a.top_k, stride = top_k + 2;
+  const int n_c = max(qb - 1, 0);
+  const size_t row_id = (size_t)rho * a.n_b + qb;
+  int32_t* out = a.sel + row_id * stride;
+  if (n_c <= top_k || top_k == 0) {
+    // every candidate kept, or none when top_k == 0
+    const bool all = top_k > 0;
+    for (int t = lane; t < stride; t += 64) {
+      int v;
+      if (all) v = t <= qb ? t : -1;
+      else v = t == 0 ? 0 : ((t == 1 && qb >= 1) ? qb : -1);
+      out[t] = v;
+    }
+    if (lane == 0) a.sel_cnt[row_id] = all ? qb + 1 : (qb >= 1 ? 2 : 1);
+    if (a.kth) {
+      // s_k exists iff 1 <= k <= n_c (here k == n_c: the row minimum); s_{k+1}
+      // iff k + 1 <= n_c (here k == 0: the row maximum). The buffer holds
+      // every candidate (k == n_c) or the best one (k == 0).
+      uint32_t mn = 0xffffffffu, mx = 0u;
+      for (int e = lane; e < c; e += 64) {
+        const uint32_t x = rb[e].x;
+        mn = min(mn, x);
+        mx = max(mx, x);
+      }
+      mn = wave_min_u32(mn);
+      mx = wave_max_u32(mx);
+      if (lane == 0) {
+        put_score(a.kth, row_id * 2 + 0, top_k >= 1 && n_c == top_k, mn);
+        put_score(a.kth, row_id * 2 + 1, top_k == 0 && n_c >= 1, mx);
+      }
+    }
+    return;
+  }
+  // 1 <= top_k < n_c; shrink the buffer first when it is well above need
+  if (c > top_k + 1 + 64) {
+    uint32_t unused;
+    c = compact_row(rb, c, top_k + 1, hist, unused);
+  }
+  const uint32_t T = wave_take(
+      [&](int i) { return rb[i].x; }, c, top_k,
+      [&](int p, int i, uint32_t) { out[1 + p] = (int32_t)rb[i].y; }, hist);
+  if (lane == 0) {
+    out[0] = 0;
+    out[top_k + 1] = qb;
+    a.sel_cnt[row_id] = top_k + 2;
+  }
+  if (a.kth) {
+    // (k+1)-th best: T again if another key ties it, else the best key
+    // below T (the buffer holds the top k + 1)
+    int ge = 0;
+    uint32_t bel = 0u;
+    for (int e = lane; e < c; e += 64) {
+      const uint32_t x = rb[e].x;
+      ge += x >= T;
+      if (x < T) bel = max(bel, x);
+    }
+    ge = wave_sum(ge);
+    bel = wave_max_u32(bel);
+    if (lane == 0) {
+      put_score(a.kth, row_id * 2 + 0, true, T);
+      put_score(a.kth, row_id * 2 + 1, true, ge >= top_k + 1 ? T : bel);
+    }
+  }
+}
+
+// ---- fused block scores and selection: a persistent grid of 4-wave
+// workgroups; each wave repeatedly takes the next work item (one retrieval
+// head's 64 consecutive query blocks: lane l owns query block 64 t + l) from
+// a counter. Items go from the longest rows to the shortest, and four
+// consecutive items are adjacent tiles of one head, so the waves of a
+// workgroup stream the same projected keys at about the same time.
+//
+// Per candidate key block, the wave computes the 64 x 64 dot products of
+// the block's keys with its 64 query-block means as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16, three per tile (bf16 x 3 split), with the keys
+// along M so that the max over a block's keys is a max over a lane's 16
+// accumulator values plus one exchange with the other half of the wave
+// (v_permlane32_swap). Each lane then holds its own row's score. A score
+// that can still enter the row's top k + 1 is appended to the row's
+// candidate buffer; a full buffer is shrunk by compact_row. The operands of
+// the next key blocks are loaded PF blocks ahead; the wave never waits at a
+// barrier, so a wave busy shrinking a buffer delays no other.
+template <int R16, int PF>
+__device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t, entry_t* wbuf,
+                         int* hist) {
+  constexpr int r = 16 * R16;
+  constexpr int NA = 4 * R16;  // 1 KiB operand chunks per key block
+  const int lane = threadIdx.x & 63;
+  const int n_b = a.n_b, cap = a.cap, need = a.top_k + 1;
+  const int R0 = 64 * t;
+  const int qb = R0 + lane;
+  const bool row_ok = qb < n_b;
+  const int qb_max = min(R0 + 63, n_b - 1);  // candidates: kb < qb_max
+  // B operands: the query-block means of rows R0 + 32 nt + l%32
+  bf16x8 bh[2][R16], bl[2][R16];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = R0 + 32 * nt + (lane & 31);
+#pragma unroll
+    for (int rs = 0; rs < R16; ++rs) {
+      bf16x8 z = {};
+      bh[nt][rs] = z;
+      bl[nt][rs] = z;
+      if (row < n_b) {
+        const size_t o = ((size_t)rho * n_b + row) * r + 16 * rs + 8 * (lane >> 5);
+        bh[nt][rs] = *reinterpret_cast<const bf16x8*>(a.qhi + o);
+        bl[nt][rs] = *reinterpret_cast<const bf16x8*>(a.qlo + o);
+      }
+    }
+  }
+  const u16* kop = a.kop + (size_t)rho * n_b * kop_block_elems(r) + lane * 8;
+  entry_t* rowbuf = wbuf + (size_t)lane * cap;
+  int cnt = 0;
+  uint32_t thr = 0u;
+  bool armed = false;
+
+  if (qb_max > 1) {
+    const int last = qb_max - 1;
+    bf16x8 ar[PF][NA];
+    auto load_a = [&](int kb, bf16x8 (&dst)[NA]) {
+      const u16* p = kop + (size_t)kb * kop_block_elems(r);
+#pragma unroll
+      for (int c = 0; c < NA; ++c)
+        dst[c] = *gmem(reinterpret_cast<const bf16x8*>(p + c * 512));
+    };
+    // one key block: scores of the wave's 64 rows, the operands of block
+    // kb + PF loaded into the freed slot, and the append
+    auto step = [&](int kb, bf16x8 (&cur)[NA]) {
+      float mx[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) mx[nt] = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 acc[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          f32x16 z = {};
+          acc[nt] = z;
+        }
+#pragma unroll
+        for (int rs = 0; rs < R16; ++rs) {
+          const bf16x8 ahi = cur[(mt * 2 + 0) * R16 + rs];
+          const bf16x8 alo = cur[(mt * 2 + 1) * R16 + rs];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(alo, bh[nt][rs], acc[nt]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(ahi, bl[nt][rs], acc[nt]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma32(ahi, bh[nt][rs], acc[nt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          float m = mx[nt];
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) m = fmaxf(m, fmaxf(acc[nt][i], acc[nt][i + 1]));
+          mx[nt] = m;
+        }
+      }
+      load_a(min(kb + PF, last), cur);
+      // lanes < 32 hold half-block maxima of rows R0 + l (tile 0) and lanes
+      // >= 32 of rows R0 + 32 + l%32 (tile 1): one swap of the upper half of
+      // mx[0] with the lower half of mx[1] lines the halves up, so lane l
+      // ends with the score of row R0 + l
+      const auto sw = __builtin_amdgcn_permlane32_swap(
+          __float_as_uint(mx[0]), __float_as_uint(mx[1]), false, false);
+      const float score = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const uint32_t key = order_key(score);
+      // (cnt < cap always holds here, as buffers are shrunk to at most
+      // cap - 64 entries before they come within PF of full; the test keeps
+      // every store in bounds regardless)
+      if (row_ok && kb < qb && (!armed || key > thr) && cnt < cap) {
+        gmem(rowbuf)[cnt] = entry_t{key, (uint32_t)kb};
+        ++cnt;
+      }
+    };
+    // buffers that a group of PF more appends could fill are shrunk
+    // between groups, so the groups themselves run without branches
+    auto shrink = [&]() {
+      uint64_t full = __ballot(cnt > cap - PF);
+      if (full) {
+        fence_wg();
+        while (full) {
+          const int rr = (int)__builtin_ctzll(full);
+          full &= full - 1;
+          uint32_t t_new;
+          entry_t* rb = wbuf + (size_t)rr * cap;
+          const int c_old = __builtin_amdgcn_readlane(cnt, rr);
+          int c_new;
+          if (cap <= 64 * kRowRegs) {
+            RowRegs R;
+            load_row(rb, c_old, R);
+            c_new = compact_regs(rb, R, need, hist, t_new);
+          } else {
+            c_new = compact_row(rb, c_old, need, hist, t_new);
+          }
+          if (lane == rr) {
+            cnt = c_new;
+            thr = t_new;
+            armed = true;
+          }
+        }
+        fence_wg();
+        // nothing of this branch stays in flight (it already waited for its
+        // own loads), so the group loop keeps exact wait counts for the ring
+        wait_vm_all();
+      }
+    };
+    // the query-block operands arrive before the ring is filled: the wait
+    // counts inside the loop then cover the ring's loads only
+    wait_vm_all();
+#pragma unroll
+    for (int p = 0; p < PF; ++p) load_a(min(1 + p, last), ar[p]);
+    int kb0 = 1;
+    for (; kb0 + PF <= qb_max; kb0 += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) step(kb0 + p, ar[p]);
+      shrink();
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (kb0 + p < qb_max) step(kb0 + p, ar[p]);
+    shrink();
+  }
+  fence_wg();
+  const int rows = min(64, n_b - R0);
+  for (int rr = 0; rr < rows; ++rr) {
+    const int c = __builtin_amdgcn_readlane(cnt, rr);
+    entry_t* rb = wbuf + (size_t)rr * cap;
+    if (cap <= 64 * kRowRegs) {
+      RowRegs R;
+      load_row(rb, c, R);
+      finish_regs(a, R, rho, R0 + rr, hist);
+    } else {
+      finish_row(a, rb, c, rho, R0 + rr, hist);
+    }
+  }
+  fence_wg();
+}
+
+template <int R16, int PF>
+__global__ __launch_bounds__(256, 2) void score_select_kernel(const ScoreArgs a) {
+  __shared__ int hist_all[4][256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int* hist = hist_all[wave];
+  entry_t* wbuf = a.buf + (size_t)(blockIdx.x * 4 + wave) * 64 * a.cap;
+  const int per_quad = 4 * a.n_ret;
+  for (;;) {
+    int item = 0;
+    if ((threadIdx.x & 63) == 0) item = atomicAdd(a.counter, 1);
+    item = __builtin_amdgcn_readfirstlane(item);
+    if (item >= a.n_items) break;
+    const int u = item / per_quad, rem = item - u * per_quad;
+    const int rho = rem >> 2;
+    const int t = a.n_tiles - 1 - (4 * u + (rem & 3));
+    if (t < 0) continue;
+    run_tile<R16, PF>(a, rho, t, wbuf, hist);
   }
 }
 
@@ -361,43 +1178,99 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
   if (a.n_ret == 0 || a.n_b == 0) return hipSuccess;
   ProjArgs pa;
   pa.S = a.S;
-  pa.S_pad = a.S_pad;
   pa.n_b = a.n_b;
   pa.r = a.r;
+  pa.n_ret = a.n_ret;
   const int G = a.Hq / a.Hkv;
-  for (int i = 0; i < kMaxHeads; ++i) {
-    pa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
-    pa.kvh_of_rho[i] = i < a.n_ret ? a.ret_heads[i] / G : 0;
-  }
-  prof_begin("proj_keys", st);
-  hipLaunchKernelGGL(proj_keys_kernel, dim3(a.n_ret, a.S_pad / 64), dim3(64), 0,
-                     st, a.k, a.p_k, pa, a.khi, a.klo, a.centroids);
-  prof_end(st);
-  if (a.keys_only) return hipGetLastError();
-  prof_begin("proj_qmeans", st);
-  hipLaunchKernelGGL(proj_qmeans_kernel, dim3(a.n_ret, a.n_b), dim3(64), 0, st,
-                     a.q, a.p_q, pa, a.qhi, a.qlo);
-  prof_end(st);
-  if (a.n_b >= 3) {
-    dim3 grid((a.n_b + 127) / 128, (a.n_b + KBC - 1) / KBC, a.n_ret);
-    prof_begin("block_scores", st);
-    switch (a.r / 16) {
-#define RTP_SCORE_CASE(R)                                                    \
-  case R:                                                                    \
-    hipLaunchKernelGGL(block_scores_kernel<R>, grid, dim3(256), 0, st,       \
-                       a.khi, a.klo, a.qhi, a.qlo, a.scores, a.S_pad, a.n_b); \
-    break;
-      RTP_SCORE_CASE(1) RTP_SCORE_CASE(2) RTP_SCORE_CASE(3) RTP_SCORE_CASE(4)
-      RTP_SCORE_CASE(5) RTP_SCORE_CASE(6) RTP_SCORE_CASE(7) RTP_SCORE_CASE(8)
-#undef RTP_SCORE_CASE
-      default: return hipErrorInvalidValue;
+  int n_grp = 0;
+  for (int i = 0; i < a.n_ret; ++i) {
+    pa.head_of_rho[i] = a.ret_heads[i];
+    const int g = a.ret_heads[i] / G;
+    if (n_grp == 0 || pa.grp_kvh[n_grp - 1] != g) {
+      pa.grp_kvh[n_grp] = (uint8_t)g;
+      pa.grp_first[n_grp] = (uint8_t)i;
+      ++n_grp;
     }
-    prof_end(st);
   }
-  prof_begin("topk", st);
-  hipLaunchKernelGGL(topk_kernel, dim3(a.n_b, a.n_ret), dim3(256), 0, st,
-                     a.scores, a.n_b, a.top_k, a.top_k + 2, a.sel, a.sel_cnt,
-                     a.kth);
+  pa.grp_first[n_grp] = (uint8_t)a.n_ret;
+  if (a.keys_only) {  // the centroids alone: no scratch
+    prof_begin("proj_keys", st);
+    hipLaunchKernelGGL(proj_keys_kernel, dim3((a.n_b + 3) / 4, n_grp),
+                       dim3(256), 0, st, a.k, a.p_k, pa, (u16*)nullptr,
+                       a.centroids);
+    prof_end(st);
+    return hipGetLastError();
+  }
+  const IndexerSizes z = indexer_sizes(a.n_ret, a.n_b, a.r, a.top_k);
+  u16* kop = reinterpret_cast<u16*>(a.scratch);
+  u16* qhi = reinterpret_cast<u16*>(a.scratch + z.kop);
+  u16* qlo = reinterpret_cast<u16*>(a.scratch + z.kop + z.qpart);
+  float* scores = reinterpret_cast<float*>(a.scratch + z.kop + 2 * z.qpart);
+  entry_t* buf =
+      reinterpret_cast<entry_t*>(a.scratch + z.kop + 2 * z.qpart + z.scores);
+  int* counter = reinterpret_cast<int*>(a.scratch + z.kop + 2 * z.qpart +
+                                        z.scores + z.buf);
+
+  prof_begin("proj_keys", st);
+  hipLaunchKernelGGL(proj_keys_kernel, dim3((a.n_b + 3) / 4, n_grp), dim3(256),
+                     0, st, a.k, a.p_k, pa, kop, a.centroids);
+  prof_end(st);
+  prof_begin("proj_qmeans", st);
+  hipLaunchKernelGGL(proj_qmeans_kernel, dim3((a.n_b + 3) / 4, a.n_ret),
+                     dim3(256), 0, st, a.q, a.p_q, pa, qhi, qlo, counter);
+  prof_end(st);
+  if (!z.fused) {  // short sequence: score rows, then a top-k per row
+    if (a.n_b >= 3) {
+      dim3 grid((a.n_b + 127) / 128, (a.n_b + KBC - 1) / KBC, a.n_ret);
+      prof_begin("block_scores", st);
+      switch (a.r / 16) {
+#define RTP_SCORE_CASE(R)                                                  \
+  case R:                                                                  \
+    hipLaunchKernelGGL(block_scores_kernel<R>, grid, dim3(256), 0, st, kop, \
+                       qhi, qlo, scores, a.n_b);                           \
+    break;
+        RTP_SCORE_CASE(1) RTP_SCORE_CASE(2) RTP_SCORE_CASE(3) RTP_SCORE_CASE(4)
+        RTP_SCORE_CASE(5) RTP_SCORE_CASE(6) RTP_SCORE_CASE(7) RTP_SCORE_CASE(8)
+#undef RTP_SCORE_CASE
+        default: return hipErrorInvalidValue;
+      }
+      prof_end(st);
+    }
+    prof_begin("topk", st);
+    hipLaunchKernelGGL(topk_kernel, dim3(a.n_b, a.n_ret), dim3(256), 0, st,
+                       scores, a.n_b, a.top_k, a.top_k + 2, a.sel, a.sel_cnt,
+                       a.kth);
+    prof_end(st);
+    return hipGetLastError();
+  }
+  ScoreArgs sa;
+  sa.kop = kop;
+  sa.qhi = qhi;
+  sa.qlo = qlo;
+  sa.buf = buf;
+  sa.counter = counter;
+  sa.sel = a.sel;
+  sa.sel_cnt = a.sel_cnt;
+  sa.kth = a.kth;
+  sa.n_b = a.n_b;
+  sa.n_ret = a.n_ret;
+  sa.top_k = a.top_k;
+  sa.cap = z.cap;
+  sa.n_tiles = (a.n_b + 63) / 64;
+  sa.n_items = z.n_items;
+  prof_begin("score_select", st);
+  switch (a.r / 16) {
+#define RTP_SCORE_CASE(R, PFN)                                                \
+  case R:                                                                     \
+    hipLaunchKernelGGL((score_select_kernel<R, PFN>), dim3(z.n_wg), dim3(256), \
+                       0, st, sa);                                            \
+    break;
+    RTP_SCORE_CASE(1, 4) RTP_SCORE_CASE(2, 2) RTP_SCORE_CASE(3, 1)
+    RTP_SCORE_CASE(4, 1) RTP_SCORE_CASE(5, 1) RTP_SCORE_CASE(6, 1)
+    RTP_SCORE_CASE(7, 1) RTP_SCORE_CASE(8, 1)
+#undef RTP_SCORE_CASE
+    default: return hipErrorInvalidValue;
+  }
   prof_end(st);
   return hipGetLastError();
 }

@@ -62,9 +62,15 @@ def test_workspace_queries():
     S, n_b = 2048, 32
     got = lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 16, 64, 8)
     al = lambda x: (x + 255) // 256 * 256
-    want = (al(1 * 128 * S * 2) + 2 * al(1 * S * 16 * 2) +
-            2 * al(n_b * 16 * 2) + al((n_b - 2) * (n_b - 1) // 2 * 4) +
-            al(n_b * 10 * 4) + al(n_b * 4))
+    # V^T and the indexer's scratch share one region (the indexer runs
+    # first); then the selection and its counts. Indexer scratch of a short
+    # sequence: projected keys (256 r bytes per block), two halves of the
+    # query-block means, the score rows (lower triangle, fp32) and the work
+    # counter.
+    vt = al(1 * 128 * S * 2)
+    idx = (al(n_b * 256 * 16) + 2 * al(n_b * 16 * 2) +
+           al((n_b - 2) * (n_b - 1) // 2 * 4) + 256)
+    want = max(vt, idx) + al(n_b * 10 * 4) + al(n_b * 4)
     assert got == want
     assert lib.rtp_prefill_workspace_bytes(S, 4, 1, 64, mp, 16, 64, 8) == 0
     assert lib.rtp_prefill_workspace_bytes(S, 4, 1, 128, mp, 16, 32, 8) == 0
@@ -129,6 +135,19 @@ def _headwise(lib, mp, windows, **kw):
         P(a["ws"]), a["wsb"], None)
 
 
+def test_long_sequence_workspace_has_no_score_rows():
+    # past 4096 blocks the indexer keeps per-row candidate buffers instead of
+    # score rows: at 1M tokens with 23 retrieval heads the whole prefill
+    # workspace stays under 3 GiB (score rows alone would be 11.5 GiB)
+    lib = rtp.load()
+    hq = [1] * 23 + [0] * 9
+    m, mp = _mask(hq)
+    ws = lib.rtp_prefill_workspace_bytes(1 << 20, 32, 4, 128, mp, 16, 64, 256)
+    assert 0 < ws < 3 * 2 ** 30, ws
+    rows = 23 * (16384 - 2) * (16384 - 1) // 2 * 4
+    assert ws < rows
+
+
 def test_headwise_prefill_validation_and_workspace():
     lib = rtp.load()
     m, mp = _mask([1, 0, 0, 0])
@@ -150,7 +169,8 @@ def test_headwise_prefill_validation_and_workspace():
     al = lambda x: (x + 255) // 256 * 256
     full = lib.rtp_headwise_prefill_workspace_bytes(S, 4, 1, 128, mp, 1, 16,
                                                     64, 8)
-    assert full == al(128 * S * 2) + 2 * al(S * 16 * 2)  # V^T + projected keys
+    assert full == al(128 * S * 2)  # V^T only: no selection, and the
+    # centroid epilogue projects keys straight into the centroids
     assert lib.rtp_headwise_prefill_workspace_bytes(S, 4, 1, 128, mp, 3, 16,
                                                     64, 8) == 0
 
