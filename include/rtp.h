@@ -38,7 +38,9 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream). The library allocates no device memory: scratch space comes
  *    from the caller's workspace `ws` of `ws_bytes` bytes (256-byte aligned),
- *    sized by the matching *_workspace_bytes query. Calls never synchronise.
+ *    sized by the matching *_workspace_bytes query (the one exception,
+ *    rtp_hybrid_attn_decode_noalloc, uses a fixed array loaded with the
+ *    library). Calls never synchronise.
  *    Some calls also run part of their work on a library-owned auxiliary
  *    stream of the device (default priority, created on first use):
  *    rtp_hybrid_attn_decode, and the prefills on sequences of more than
@@ -296,6 +298,38 @@ int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
                            int block, int top_k, int n_recent, float scale,
                            void* out, float* lse, int32_t* sel_out, void* ws,
                            size_t ws_bytes, rtp_stream_t stream);
+
+/* Scratch bytes held by the library for rtp_hybrid_attn_decode_noalloc on
+ * each GPU it runs on (64 MiB). */
+#define RTP_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * rtp_hybrid_attn_decode_noalloc - rtp_hybrid_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same arguments, results
+ * and validation as rtp_hybrid_attn_decode, without ws / ws_bytes: the
+ * scratch space comes from a device array of the library, fixed at
+ * RTP_NOALLOC_SCRATCH_BYTES per GPU, that lives until the process ends.
+ * Nothing is allocated or created: no device memory, and no auxiliary
+ * stream (every kernel runs on `stream`, in order).
+ *
+ *  A step whose scratch need (rtp_decode_workspace_bytes of the same sizes)
+ *  exceeds RTP_NOALLOC_SCRATCH_BYTES returns RTP_EWORKSPACE with nothing
+ *  launched. (For example, 32 sequences of 256K tokens with 32 query / 4 KV
+ *  heads, 5 retrieval heads and top_k 64 need about 7 MB.)
+ *  All calls on one GPU share that GPU's array, and no call needs it to
+ *  start cleared: two calls that overlap in time on one GPU (on different
+ *  streams, or from different threads) race and give undefined results.
+ */
+int rtp_hybrid_attn_decode_noalloc(const void* q, const void* k_cache,
+                                   const void* v_cache,
+                                   const int32_t* cache_len, int B, int Lmax,
+                                   int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int window,
+                                   const float* p_q, const float* centroids,
+                                   int r, int block, int top_k, int n_recent,
+                                   float scale, void* out, float* lse,
+                                   int32_t* sel_out, rtp_stream_t stream);
 
 #ifdef __cplusplus
 }

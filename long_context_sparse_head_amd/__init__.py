@@ -26,7 +26,8 @@ __all__ = [
     "dense_workspace_bytes", "decode_workspace_bytes", "indexer_select",
     "hybrid_attn_prefill", "headwise_prefill", "dense_attn_prefill",
     "build_centroids",
-    "hybrid_attn_decode", "decode_append", "version", "KernelTimer",
+    "hybrid_attn_decode", "hybrid_attn_decode_noalloc", "decode_append",
+    "version", "KernelTimer", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
@@ -70,6 +71,9 @@ _SIGS = {
     "rtp_hybrid_attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _U8P,
                                     _I, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P,
                                     _P, _Z, _P]),
+    "rtp_hybrid_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                            _U8P, _I, _P, _P, _I, _I, _I, _I,
+                                            _F, _P, _P, _P, _P]),
 }
 
 
@@ -464,4 +468,44 @@ def hybrid_attn_decode(q, k_cache, v_cache, cache_len, is_retrieval,
         w.numel(), _stream(dev)), "rtp_hybrid_attn_decode")
     if want_lse or want_sel:
         return out, lse, so
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RTP_NOALLOC_SCRATCH_BYTES
+
+
+def hybrid_attn_decode_noalloc(q, k_cache, v_cache, cache_len, is_retrieval,
+                               window: int, p_q, centroids, top_k: int,
+                               n_recent: int = 2, r: int = 16, block: int = 64,
+                               scale: float = 0.0, out=None, lse=None,
+                               sel=None):
+    """hybrid_attn_decode through rtp_hybrid_attn_decode_noalloc: the
+    library's own static scratch, nothing allocated by the call. Outputs
+    (out, and optionally lse [B,Hq] fp32 and sel [B,n_ret,top_k+1+n_recent]
+    int32) are caller tensors; out is created only when not given."""
+    lib = load()
+    B, Hq, d = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    _dev(q, torch.bfloat16, "q", (B, Hq, d))
+    _dev(k_cache, torch.bfloat16, "k_cache", (B, Hkv, Lmax, d))
+    _dev(v_cache, torch.bfloat16, "v_cache", (B, Hkv, Lmax, d))
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    if n_ret:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, Lmax // block, r))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, torch.bfloat16, "out", (B, Hq, d))
+    if lse is not None:
+        _dev(lse, torch.float32, "lse", (B, Hq))
+    if sel is not None:
+        _dev(sel, torch.int32, "sel", (B, n_ret, top_k + 1 + n_recent))
+    _check(lib.rtp_hybrid_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), B, Lmax, Hq,
+        Hkv, d, mp, int(window), _ptr(p_q), _ptr(centroids), r, block, top_k,
+        n_recent, float(scale), _ptr(out), _ptr(lse), _ptr(sel),
+        _stream(q.device)), "rtp_hybrid_attn_decode_noalloc")
     return out

@@ -598,15 +598,21 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
   return decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent).total;
 }
 
-int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
-                           const void* v_cache, const int32_t* cache_len,
-                           int B, int Lmax, int Hq, int Hkv, int d,
-                           const uint8_t* is_retrieval, int window,
-                           const float* p_q, const float* centroids, int r,
-                           int block, int top_k, int n_recent, float scale,
-                           void* out, float* lse, int32_t* sel_out, void* ws,
-                           size_t ws_bytes, rtp_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+// Shared body of rtp_hybrid_attn_decode (caller's workspace) and
+// rtp_hybrid_attn_decode_noalloc (the library's static scratch). `need`
+// receives the scratch bytes the call uses (0 when nothing is launched);
+// with ws == nullptr the call stops after validation and sizing.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* cache_len, int B, int Lmax, int Hq, int Hkv,
+                int d, const uint8_t* is_retrieval, int window,
+                const float* p_q, const float* centroids, int r, int block,
+                int top_k, int n_recent, float scale, void* out, float* lse,
+                int32_t* sel_out, void* ws, size_t ws_bytes, bool one_stream,
+                size_t* need, rtp_stream_t stream) {
+  *need = 0;
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
@@ -621,6 +627,8 @@ int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
   if (hi.n_ret > 0 && (!p_q || !centroids))
     return fail(RTP_EINVAL, "p_q and centroids must be non-NULL with retrieval heads");
   const DecodeLayout L = decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent);
+  *need = L.total;
+  if (!ws) return RTP_OK;
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
@@ -650,6 +658,7 @@ int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
   a.cscores = reinterpret_cast<float*>(w + L.cs);
   a.part_o = reinterpret_cast<float*>(w + L.po);
   a.part_ml = reinterpret_cast<float*>(w + L.pml);
+  a.one_stream = one_stream;
   hipError_t e = rtp::launch_decode(a, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (sel_out && hi.n_ret > 0) {
@@ -659,6 +668,89 @@ int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
     if (e != hipSuccess) return hip_fail(e, "selection copy");
   }
   return RTP_OK;
+}
+
+// Scratch of rtp_hybrid_attn_decode_noalloc: a device array of the library
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never uses the array's name as an address: its device address
+// is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[RTP_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RTP_EUNSUPPORTED, "device index beyond the library's table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return RTP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int rtp_hybrid_attn_decode(const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* cache_len,
+                           int B, int Lmax, int Hq, int Hkv, int d,
+                           const uint8_t* is_retrieval, int window,
+                           const float* p_q, const float* centroids, int r,
+                           int block, int top_k, int n_recent, float scale,
+                           void* out, float* lse, int32_t* sel_out, void* ws,
+                           size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  size_t need = 0;
+  if (!ws) {  // validate and size first: a missing workspace is EWORKSPACE
+    int e = decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                        is_retrieval, window, p_q, centroids, r, block, top_k,
+                        n_recent, scale, out, lse, sel_out, nullptr, 0, false,
+                        &need, stream);
+    if (e) return e;
+    return check_ws(ws, ws_bytes, need);
+  }
+  return decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                     is_retrieval, window, p_q, centroids, r, block, top_k,
+                     n_recent, scale, out, lse, sel_out, ws, ws_bytes, false,
+                     &need, stream);
+}
+
+int rtp_hybrid_attn_decode_noalloc(const void* q, const void* k_cache,
+                                   const void* v_cache,
+                                   const int32_t* cache_len, int B, int Lmax,
+                                   int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int window,
+                                   const float* p_q, const float* centroids,
+                                   int r, int block, int top_k, int n_recent,
+                                   float scale, void* out, float* lse,
+                                   int32_t* sel_out, rtp_stream_t stream) {
+  g_err.clear();
+  size_t need = 0;
+  int e = decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                      is_retrieval, window, p_q, centroids, r, block, top_k,
+                      n_recent, scale, out, lse, sel_out, nullptr, 0, true,
+                      &need, stream);
+  if (e || need == 0) return e;
+  if (need > RTP_NOALLOC_SCRATCH_BYTES)
+    return fail(RTP_EWORKSPACE,
+                "this decode step needs " + std::to_string(need) +
+                    " bytes of scratch; rtp_hybrid_attn_decode_noalloc has " +
+                    std::to_string((size_t)RTP_NOALLOC_SCRATCH_BYTES) +
+                    " (use rtp_hybrid_attn_decode with a workspace)");
+  void* ptr = nullptr;
+  if ((e = scratch_of_current_device(&ptr))) return e;
+  return decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                     is_retrieval, window, p_q, centroids, r, block, top_k,
+                     n_recent, scale, out, lse, sel_out, ptr,
+                     RTP_NOALLOC_SCRATCH_BYTES, true, &need, stream);
 }
 
 }  // extern "C"

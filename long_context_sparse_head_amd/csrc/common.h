@@ -203,6 +203,8 @@ struct DecodeLaunch {
   const uint8_t* is_ret;     // host [Hq]
   u16* out; float* lse; int32_t* sel; float* cscores; float* part_o;
   float* part_ml;
+  // every kernel on `st` (no auxiliary stream, so nothing is created)
+  bool one_stream = false;
 };
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st);
 

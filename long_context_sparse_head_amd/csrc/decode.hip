@@ -686,7 +686,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     prof_end(on);
   };
   hipError_t e = hipSuccess;
-  if (n_win_units > 0 && n_ret_units > 0) {
+  if (!a.one_stream && n_win_units > 0 && n_ret_units > 0) {
     AuxFork fork(st);
     if ((e = fork.status()) != hipSuccess) return e;
     attend("dec_attn_window", 0, n_win_units, fork.stream());
