@@ -164,6 +164,8 @@ __host__ inline IndexerSizes indexer_sizes(int n_ret, int n_b, int r,
                                            int top_k) {
   IndexerSizes z;
   const int need = top_k + 1;  // the top_k + 1 best are kept (for s_{k+1})
+  // (4 need entries, hence fewer shrinks, measured no faster at 1M tokens:
+  // each shrink then handles more entries)
   const int c = 2 * need > need + 64 ? 2 * need : need + 64;
   z.cap = (c + 63) / 64 * 64;
   // a row has at most n_b - 2 candidates: a buffer with 64 slots more than

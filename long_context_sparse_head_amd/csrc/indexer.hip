@@ -981,11 +981,11 @@ __device__ __forceinline__ void finish_row(const ScoreArgs& a, entry_t* rb, int 
 }
 
 // ---- fused block scores and selection: a persistent grid of 4-wave
-// workgroups; each wave repeatedly takes the next work item (one retrieval
-// head's 64 consecutive query blocks: lane l owns query block 64 t + l) from
-// a counter. Items go from the longest rows to the shortest, and four
-// consecutive items are adjacent tiles of one head, so the waves of a
-// workgroup stream the same projected keys at about the same time.
+// workgroups; each workgroup repeatedly takes the next quad of work items
+// from a counter (an item is one retrieval head's 64 consecutive query
+// blocks, lane l owning query block 64 t + l; a quad is four adjacent items
+// of one head, one per wave). Quads go from the longest rows to the
+// shortest.
 //
 // Per candidate key block, the wave computes the 64 x 64 dot products of
 // the block's keys with its 64 query-block means as 2 x 2 tiles of
@@ -998,8 +998,9 @@ __device__ __forceinline__ void finish_row(const ScoreArgs& a, entry_t* rb, int 
 // the next key blocks are loaded PF blocks ahead; the wave never waits at a
 // barrier, so a wave busy shrinking a buffer delays no other.
 template <int R16, int PF>
-__device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t, entry_t* wbuf,
-                         int* hist) {
+__device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t,
+                                         entry_t* wbuf, int* hist,
+                                         int sync_until) {
   constexpr int r = 16 * R16;
   constexpr int NA = 4 * R16;  // 1 KiB operand chunks per key block
   const int lane = threadIdx.x & 63;
@@ -1127,11 +1128,17 @@ __device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t, ent
     wait_vm_all();
 #pragma unroll
     for (int p = 0; p < PF; ++p) load_a(min(1 + p, last), ar[p]);
+    // The workgroup's four waves meet at a barrier every 4 groups while all
+    // of them are inside their common key range (sync_until, the same for
+    // all four, so all four pass the same barriers): a wave delayed by
+    // shrinking a buffer does not drift away from the others, and the key
+    // blocks they share are still in cache when the last one reads them.
     int kb0 = 1;
-    for (; kb0 + PF <= qb_max; kb0 += PF) {
+    for (int grp = 0; kb0 + PF <= qb_max; kb0 += PF, ++grp) {
 #pragma unroll
       for (int p = 0; p < PF; ++p) step(kb0 + p, ar[p]);
       shrink();
+      if ((grp & 3) == 3 && kb0 + PF <= sync_until) __syncthreads();
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p)
@@ -1157,20 +1164,31 @@ __device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t, ent
 template <int R16, int PF>
 __global__ __launch_bounds__(256, 2) void score_select_kernel(const ScoreArgs a) {
   __shared__ int hist_all[4][256];
+  __shared__ int s_quad;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int* hist = hist_all[wave];
   entry_t* wbuf = a.buf + (size_t)(blockIdx.x * 4 + wave) * 64 * a.cap;
-  const int per_quad = 4 * a.n_ret;
+  // Work is taken a quad at a time: one head's four adjacent 64-row tiles,
+  // one per wave, started together after a barrier. The four waves then
+  // stream the same projected keys at about the same time, so each key
+  // block is fetched from memory about once per workgroup (taken one item
+  // per wave, the waves of a workgroup read unrelated streams and every
+  // read went to memory).
+  const int n_quads = a.n_items / 4;
   for (;;) {
-    int item = 0;
-    if ((threadIdx.x & 63) == 0) item = atomicAdd(a.counter, 1);
-    item = __builtin_amdgcn_readfirstlane(item);
-    if (item >= a.n_items) break;
-    const int u = item / per_quad, rem = item - u * per_quad;
-    const int rho = rem >> 2;
-    const int t = a.n_tiles - 1 - (4 * u + (rem & 3));
-    if (t < 0) continue;
-    run_tile<R16, PF>(a, rho, t, wbuf, hist);
+    if (threadIdx.x == 0) s_quad = atomicAdd(a.counter, 1);
+    __syncthreads();
+    const int quad = s_quad;
+    __syncthreads();  // every wave has read s_quad before it is rewritten
+    if (quad >= n_quads) break;
+    const int u = quad / a.n_ret;
+    const int rho = quad - u * a.n_ret;
+    const int t = a.n_tiles - 1 - (4 * u + wave);
+    // common key range of the quad's four tiles (none when the last quad
+    // has fewer than four)
+    const int t_min = a.n_tiles - 1 - (4 * u + 3);
+    const int sync_until = t_min >= 0 ? min(64 * t_min + 63, a.n_b - 1) : 0;
+    if (t >= 0) run_tile<R16, PF>(a, rho, t, wbuf, hist, sync_until);
   }
 }
 
