@@ -34,39 +34,83 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "hybrid-attn prefill tokens/s at 128K & 1M; decode tok/s; % bf16 MFMA peak"
 
-# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc runs
-# (FETCH_SIZE, then WRITE_SIZE) of
-#   bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-gib 1
-# each divided by what the same counter reads per byte of the run's 1 GiB
-# plain device copy. Valid only for the kernel source it was measured on
-# (sha256 of the sources below, build flags included); after any change to
-# them the figure is reported as null.
-TRAFFIC = {
-    "kernel": "attn_window_kernel",
-    "sources": ["long_context_sparse_head_amd/csrc/attn_window.hip",
-                "long_context_sparse_head_amd/csrc/attn_core.h",
-                "long_context_sparse_head_amd/build.py"],
-    "sha256": "8631befb3ae35fcb19d9f895f862036c91d74cd6b4cd81fae4ba36efa94872b8",
-    "fetch_bytes": 2935474530,
-    "write_bytes": 906254451,
+# HBM bytes per launch, from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of the leg named, with --copy-probe-gib 1: each counter is
+# divided by what it reads per byte of that run's 1 GiB plain device copy
+# (0.5 for FETCH_SIZE, 1.0 for WRITE_SIZE on MI355X). A figure is valid only
+# for the kernel source it was measured on: sha256 over the listed sources
+# and the hipcc flags the build gives the kernel's file. After any change it
+# is reported as null.
+_K = "long_context_sparse_head_amd/csrc/"
+COUNTERS = {
+    # bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1
+    "attn_window@128k": {
+        "kernel": "attn_window", "unit": "attn_window.hip",
+        "sources": [_K + "attn_window.hip", _K + "attn_core.h"],
+        "sha256": "84947ce2ccc820f9d461a8c01a6b3ff6cd451c7f05c754aea2410f88eb4aa194",
+        "fetch_bytes": 2935474530, "write_bytes": 906254451},
+    "attn_sparse@128k": {
+        "kernel": "attn_sparse", "unit": "attn.hip",
+        "sources": [_K + "attn.hip", _K + "attn_core.h"],
+        "sha256": "e97c68e03aa9a9fd389b7a9b76819127d0092e31a63f1c24e61825af99e3e7d0",
+        "fetch_bytes": 16581650227,
+        "write_bytes": 168367411},
+    # bench.py --leg 1m --steps 2 --warmup 1
+    "attn_sparse@1m": {
+        "kernel": "attn_sparse", "unit": "attn.hip",
+        "sources": [_K + "attn.hip", _K + "attn_core.h"],
+        "sha256": "e97c68e03aa9a9fd389b7a9b76819127d0092e31a63f1c24e61825af99e3e7d0",
+        "fetch_bytes": 2761143410073,
+        "write_bytes": 6217822925},
 }
+TRAFFIC_KEY = "attn_window@128k"
 
 
-def traffic_sources_sha256():
+def kernel_sources_sha256(entry):
     import hashlib
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_rtp_build_flags", os.path.join(ROOT, "long_context_sparse_head_amd",
+                                         "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    flags = b.HIPFLAGS + b.EXTRA_FLAGS.get(entry["unit"], [])
     h = hashlib.sha256()
-    for src in TRAFFIC["sources"]:
+    for src in entry["sources"]:
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 
+def counter_bytes(key):
+    """(fetch, write) bytes per launch, or None once the source changed."""
+    e = COUNTERS[key]
+    if e["sha256"] is None or kernel_sources_sha256(e) != e["sha256"]:
+        return None
+    return e["fetch_bytes"], e["write_bytes"]
+
+
 def measured_traffic():
-    if TRAFFIC["sha256"] is None:
-        return None
-    if traffic_sources_sha256() != TRAFFIC["sha256"]:
-        return None
-    return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    fw = counter_bytes(TRAFFIC_KEY)
+    return None if fw is None else fw[0] + fw[1]
+
+
+def hbm_counters(leg, ks):
+    """Counter bytes of this leg's kernels and the rate they imply at the
+    kernel times measured in this run."""
+    out = {}
+    for key, e in COUNTERS.items():
+        if not key.endswith("@" + leg):
+            continue
+        fw = counter_bytes(key)
+        t = ks.get(e["kernel"])
+        if fw is None or not t:
+            out[key] = None
+            continue
+        out[key] = {"fetch_gb": fw[0] / 1e9, "write_gb": fw[1] / 1e9,
+                    "gbs": (fw[0] + fw[1]) / (t["ms_per_launch"] / 1e3) / 1e9}
+    return out
 
 
 def log(msg):
@@ -105,7 +149,8 @@ def kernel_stats(records, steps):
 
 
 # ------------------------------------------------------------ GPU legs
-def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False):
+def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False,
+                  leg=None):
     """dense: every head causal-full (rtp_dense_attn_prefill); full:
     retrieval heads causal-full, streaming heads windowed, with the decode
     centroids as an epilogue (rtp_headwise_prefill, RTP_RETRIEVAL_FULL)."""
@@ -231,6 +276,8 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False):
             res["block_scores_tflops_alg"] = (n_ret * cand_keys * 2 * w.r /
                                               (bs["ms_per_launch"] / 1e3) / 1e12)
         res["workspace_gib"] = ws.numel() / 2**30
+    if leg:
+        res["hbm_counters"] = hbm_counters(leg, ks)
     del x, out, ws
     torch.cuda.empty_cache()
     return res
@@ -440,12 +487,15 @@ def main():
                  "dense1m": PREFILL_1M}[args.leg]
             res = bench_prefill(rtp, torch, w, args.steps, args.warmup,
                                 dense=args.leg in ("dense", "dense1m"),
-                                full=args.leg == "full")
+                                full=args.leg == "full",
+                                leg=args.leg if args.leg in ("1m", "32k")
+                                else None)
         if args.copy_probe_gib > 0:
             copy_probe()
         print(json.dumps({"leg": args.leg, **res}), flush=True)
         return
-    main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup)
+    main = bench_prefill(rtp, torch, PREFILL_128K, args.steps, args.warmup,
+                         leg="128k")
     log(f"[bench] 128K: {main['ms_per_step']:.3f} ms/step, "
         f"{main['tokens_per_s']:.3e} tok/s, window kernel "
         f"{main['window_kernel_tflops']:.0f} TF/s, sparse kernel "
@@ -453,7 +503,8 @@ def main():
     extra = {}
     if not args.only_main:
         extra["prefill_1m"] = bench_prefill(rtp, torch, PREFILL_1M,
-                                            max(2, args.steps // 4), 1)
+                                            max(2, args.steps // 4), 1,
+                                            leg="1m")
         log(f"[bench] 1M: {extra['prefill_1m']['ms_per_step']:.1f} ms/step")
         extra["prefill_32k"] = bench_prefill(rtp, torch, PREFILL_32K,
                                              args.steps, args.warmup)
