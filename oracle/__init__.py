@@ -13,7 +13,9 @@ Sources (the pages are web articles; cited by title and section):
   attention, the rest use sliding-window attention (scheme one).
 * "阿里RTPurboV2：Transformer再次崛起，百步训练实现10倍稀少把稳", paragraphs
   on the low-rank projector (D -> r = 16), on clustering in the low-rank space,
-  on K-cache clustering for decode, and on the all-sparse variant.
+  on K-cache clustering for decode, and on the all-sparse variant
+  (``cluster.py``: k-means of the projected keys and the decode step that
+  chooses among clusters).
 * aitop.news summary of "Full Attention Strikes Back": a 16-dimensional
   indexer guesses which earlier tokens matter, and the real attention then
   runs only on that selected set.
@@ -34,3 +36,7 @@ from .prefill import (  # noqa: F401
     hybrid_prefill,
 )
 from .decode import decode_centroids, decode_select, hybrid_decode  # noqa: F401
+from .cluster import (  # noqa: F401
+    cluster_count, cluster_keys, lloyd_step, nearest_centroid, group_members,
+    clustered_select, kept_tokens, clustered_decode,
+)

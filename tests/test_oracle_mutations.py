@@ -203,3 +203,128 @@ def test_pins_reject_mutation(monkeypatch, mod, name, fn):
             caught += 1
             break
     assert caught, f"no pin rejects mutation {fn.__name__}"
+
+
+# ------------------------------------------------------------- clustering
+import oracle.cluster as oc  # noqa: E402
+from tests import test_oracle_cluster_pins as cpins  # noqa: E402
+
+_orig_nearest = oc.nearest_centroid
+_orig_cselect = oc.clustered_select
+
+
+def _nearest_by_dot(x, cents):
+    # largest dot product instead of smallest distance (drops -|c|^2 / 2)
+    return np.argmax(x @ cents.T, axis=1)
+
+
+def _nearest_ties_high(x, cents):
+    d2 = ((x[:, None, :] - cents[None, :, :]) ** 2).sum(axis=2)
+    return d2.shape[1] - 1 - np.argmin(d2[:, ::-1], axis=1)
+
+
+def _lloyd_empty_to_zero(x, cents):
+    m = cents.shape[0]
+    assign = oc.nearest_centroid(x, cents[1:]) + 1
+    counts = np.bincount(assign, minlength=m)
+    new = np.zeros_like(cents)
+    for c in range(1, m):
+        if counts[c]:
+            new[c] = x[assign == c].mean(axis=0)
+    return assign, new, counts
+
+
+def _lloyd_sum_not_mean(x, cents):
+    m = cents.shape[0]
+    assign = oc.nearest_centroid(x, cents[1:]) + 1
+    counts = np.bincount(assign, minlength=m)
+    new = cents.copy()
+    for c in range(1, m):
+        if counts[c]:
+            new[c] = x[assign == c].sum(axis=0)
+    return assign, new, counts
+
+
+def _count_off_by_one(L, block, n_recent):
+    return max(-(-L // block) - n_recent + 1, 1)
+
+
+def _group_members_descending(assign, m, first_token):
+    off, mem = _orig_group(assign, m, first_token)
+    mem = mem.copy()
+    for c in range(1, m):
+        mem[off[c]:off[c + 1]] = mem[off[c]:off[c + 1]][::-1]
+    return off, mem
+
+
+def _seeds_first_key(x, m, block):
+    out = np.full((m, x.shape[1]), np.nan)
+    for c in range(1, m):
+        out[c] = x[(c - 1) * block]
+    return out
+
+
+def _select_ignores_empty(q_tilde, cent_of, valid_of, n_b, k, n_recent):
+    return _orig_cselect(q_tilde, cent_of, lambda c: True, n_b, k, n_recent)
+
+
+def _select_ties_high(q_tilde, cent_of, valid_of, n_b, k, n_recent):
+    n_c = max(n_b - n_recent - 1, 0)
+    cand = np.array([c for c in range(1, 1 + n_c) if valid_of(c)], np.int64)
+    if len(cand) > k:
+        sc = (np.stack([cent_of(c) for c in cand]).astype(F32) @
+              q_tilde.astype(F32)).astype(F32)
+        top = cand[np.lexsort((-cand, -sc))[:k]]
+    else:
+        top = cand
+    recent = np.arange(n_b - n_recent, n_b, dtype=np.int64)
+    sel = np.concatenate([[0], top, recent]).astype(np.int64)
+    return np.unique(sel[sel >= 0])
+
+
+def _kept_tokens_blocks_only(sel, m, offsets, members, L, block):
+    parts = [np.arange(int(c) * block, min(L, (int(c) + 1) * block))
+             for c in sel]
+    return np.sort(np.concatenate(parts).astype(np.int64))
+
+
+_orig_group = oc.group_members
+
+CLUSTER_MUTATIONS = [
+    (oc, "nearest_centroid", _nearest_by_dot),
+    (oc, "nearest_centroid", _nearest_ties_high),
+    (oc, "lloyd_step", _lloyd_empty_to_zero),
+    (oc, "lloyd_step", _lloyd_sum_not_mean),
+    (oc, "cluster_count", _count_off_by_one),
+    (oc, "group_members", _group_members_descending),
+    (oc, "block_means", _seeds_first_key),
+    (oc, "clustered_select", _select_ignores_empty),
+    (oc, "clustered_select", _select_ties_high),
+    (oc, "kept_tokens", _kept_tokens_blocks_only),
+]
+
+CLUSTER_PIN_TESTS = [
+    lambda: cpins.test_lloyd_matches_sklearn_kmeans(2),
+    cpins.test_lloyd_brute_force_ties_and_empty_clusters,
+    cpins.test_kmeans_objective_never_increases,
+    cpins.test_planted_topics_are_recovered,
+    cpins.test_cluster_range_and_tables,
+    cpins.test_cluster_seeds_equal_decode_centroids,
+    cpins.test_clustered_decode_with_block_clusters_equals_block_decode,
+    cpins.test_clustered_decode_fp64_brute_force,
+]
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("mod,name,fn", CLUSTER_MUTATIONS,
+                         ids=[m[2].__name__ for m in CLUSTER_MUTATIONS])
+def test_cluster_pins_reject_mutation(monkeypatch, mod, name, fn):
+    monkeypatch.setattr(mod, name, fn)
+    caught = 0
+    for t in CLUSTER_PIN_TESTS:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError, KeyError):
+            caught += 1
+            break
+    assert caught, f"no pin rejects mutation {fn.__name__}"
