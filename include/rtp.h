@@ -331,6 +331,99 @@ int rtp_hybrid_attn_decode_noalloc(const void* q, const void* k_cache,
                                    float scale, void* out, float* lse,
                                    int32_t* sel_out, rtp_stream_t stream);
 
+/* Workspace bytes for rtp_cluster_keys (0 on invalid arguments). */
+size_t rtp_cluster_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int r,
+                                   int block);
+
+/*
+ * rtp_cluster_keys - semantic clustering of the decode K cache
+ * ("阿里RTPurboV2：Transformer再次崛起，百步训练实现10倍稀少把稳", paragraph
+ * on the synergy of feature and sequence compression: after the low-rank
+ * projection, related keys lie close together and unrelated ones far apart,
+ * so the sequence can be compressed by clustering; Qwen3-Coder recipe
+ * paragraph: the K cache is clustered during prefill and decode runs
+ * sparsely). The pages give no algorithm; this library's reading is k-means
+ * by Lloyd's algorithm, seeded by the blocks:
+ *
+ *  For sequence b and retrieval head rho, with L = cache_len[b],
+ *  n_b = ceil(L / block) and m = max(n_b - n_recent, 1): the points are the
+ *  projected keys x_t = P_k[rho] k_cache[b,g,t] of tokens block .. block*m-1
+ *  (blocks 1 .. m-1; the sink block and the last n_recent blocks are always
+ *  attended and are not clustered). Cluster ids are 1 .. m-1; cluster c
+ *  starts from centroids[b,rho,c,:] (its block centroid after
+ *  rtp_build_centroids, or the result of an earlier call). Each of the
+ *  `iters` steps assigns every point to the nearest centroid (squared
+ *  Euclidean distance; ties: the lower id), then moves every cluster that
+ *  has members to their mean; a cluster without members keeps its
+ *  centroid. With iters = 0 the clusters are the blocks.
+ *
+ *  k_cache [B,Hkv,Lmax,d] bf16; cache_len [B] int32 DEVICE array;
+ *  p_k [n_ret,r,d] fp32 with r in {16, 32, 48, 64}; n_recent >= 1;
+ *  0 <= iters <= 1000.
+ *  centroids [B,n_ret,Lmax/block,r] fp32 (in/out): entries 1 .. m-1 become
+ *    the cluster centroids (each the mean of its members); others untouched.
+ *  cl_m [B] int32 (out): m of each sequence.
+ *  cl_off [B,n_ret,Lmax/block+1] int32 (out): the members of cluster c are
+ *    cl_members[b,rho, cl_off[c] .. cl_off[c+1]-1]; cl_off[0] = cl_off[1] =
+ *    0, and the entries from m on hold the number of clustered tokens.
+ *  cl_members [B,n_ret,Lmax] int32 (out): token ids grouped by cluster,
+ *    ascending within each cluster.
+ *  ws: rtp_cluster_workspace_bytes bytes (may be NULL when iters = 0).
+ *
+ *  Precision: the nearest centroid is taken as the largest
+ *  x . mu_c - |mu_c|^2 / 2, with the products formed from split bf16 parts
+ *  (about 2^-16 of |x| |mu_c|), so a point that close to equidistant from
+ *  two centroids may take either; the means are summed in fp64. Results are
+ *  deterministic.
+ */
+int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
+                     int Lmax, int Hq, int Hkv, int d,
+                     const uint8_t* is_retrieval, const float* p_k, int r,
+                     int block, int n_recent, int iters, float* centroids,
+                     int32_t* cl_m, int32_t* cl_off, int32_t* cl_members,
+                     void* ws, size_t ws_bytes, rtp_stream_t stream);
+
+/* Workspace bytes for rtp_hybrid_attn_decode_clustered. */
+size_t rtp_decode_clustered_workspace_bytes(int B, int Lmax, int Hq, int Hkv,
+                                            int d, const uint8_t* is_retrieval,
+                                            int r, int block, int top_k,
+                                            int n_recent);
+
+/*
+ * rtp_hybrid_attn_decode_clustered - rtp_hybrid_attn_decode whose retrieval
+ * heads choose among the clusters of rtp_cluster_keys (same RTPurboV2
+ * paragraphs: decode skips whole groups of unrelated tokens and attends the
+ * kept ones exactly).
+ *
+ *  Retrieval head rho of sequence b, with L = cache_len[b] (which may have
+ *  grown since the clustering), n_b = ceil(L/block) and m = cl_m[b]: the
+ *  candidates are 1 .. n_b-n_recent-1; a candidate c < m is cluster c,
+ *  scored by q~ . centroids[b,rho,c] where q~ = P_q[rho] q, and is skipped
+ *  when it has no members; a candidate c >= m (a block that left the recent
+ *  window after the clustering) is block c with its block centroid (kept
+ *  current by rtp_decode_append). The sink block 0, the top_k candidates
+ *  (ties: lower id) and the blocks n_b-n_recent .. n_b-1 are kept; the head
+ *  attends every member token of a kept cluster and every token of a kept
+ *  block, exactly. Streaming heads as in rtp_hybrid_attn_decode.
+ *
+ *  cl_m, cl_off, cl_members: the tables of rtp_cluster_keys. sel_out
+ *  [B,n_ret,top_k+1+n_recent] (may be NULL): kept ids ascending, -1 padded
+ *  (an empty cluster appears only when fewer than top_k candidates have
+ *  members; it adds no token). Other arguments, streams and validation as
+ *  in rtp_hybrid_attn_decode; ws of rtp_decode_clustered_workspace_bytes
+ *  bytes. With the tables of iters = 0 the result equals
+ *  rtp_hybrid_attn_decode bit for bit.
+ */
+int rtp_hybrid_attn_decode_clustered(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* cache_len, int B, int Lmax, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, const int32_t* cl_m, const int32_t* cl_off,
+    const int32_t* cl_members, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

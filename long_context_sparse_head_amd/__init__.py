@@ -28,6 +28,8 @@ __all__ = [
     "build_centroids",
     "hybrid_attn_decode", "hybrid_attn_decode_noalloc", "decode_append",
     "version", "KernelTimer", "NOALLOC_SCRATCH_BYTES",
+    "cluster_workspace_bytes", "cluster_keys",
+    "decode_clustered_workspace_bytes", "hybrid_attn_decode_clustered",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
@@ -74,6 +76,15 @@ _SIGS = {
     "rtp_hybrid_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I,
                                             _U8P, _I, _P, _P, _I, _I, _I, _I,
                                             _F, _P, _P, _P, _P]),
+    "rtp_cluster_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _U8P, _I, _I]),
+    "rtp_cluster_keys": (_I, [_P, _P, _I, _I, _I, _I, _I, _U8P, _P, _I, _I,
+                              _I, _I, _P, _P, _P, _P, _P, _Z, _P]),
+    "rtp_decode_clustered_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _U8P,
+                                                  _I, _I, _I, _I]),
+    "rtp_hybrid_attn_decode_clustered": (_I, [_P, _P, _P, _P, _I, _I, _I, _I,
+                                              _I, _U8P, _I, _P, _P, _P, _P, _P,
+                                              _I, _I, _I, _I, _F, _P, _P, _P,
+                                              _P, _Z, _P]),
 }
 
 
@@ -508,4 +519,102 @@ def hybrid_attn_decode_noalloc(q, k_cache, v_cache, cache_len, is_retrieval,
         Hkv, d, mp, int(window), _ptr(p_q), _ptr(centroids), r, block, top_k,
         n_recent, float(scale), _ptr(out), _ptr(lse), _ptr(sel),
         _stream(q.device)), "rtp_hybrid_attn_decode_noalloc")
+    return out
+
+
+def cluster_workspace_bytes(B: int, Lmax: int, Hq: int, Hkv: int,
+                            is_retrieval, r: int = 16, d: int = 128,
+                            block: int = 64) -> int:
+    _, mp = _mask(is_retrieval, Hq)
+    return int(load().rtp_cluster_workspace_bytes(B, Lmax, Hq, Hkv, d, mp, r,
+                                                  block))
+
+
+def cluster_keys(k_cache, cache_len, is_retrieval, p_k, centroids,
+                 iters: int = 1, n_recent: int = 2, r: int = 16,
+                 block: int = 64, ws=None, tables=None):
+    """k-means of the projected keys, seeded by `centroids` (updated in
+    place). Returns the tables (cl_m [B], cl_off [B,n_ret,Lmax/block+1],
+    cl_members [B,n_ret,Lmax]); `tables` may hold them already allocated."""
+    lib = load()
+    B, Hkv, Lmax, d = k_cache.shape
+    Hq = len(is_retrieval)
+    _dev(k_cache, torch.bfloat16, "k_cache")
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    _proj(p_k, n_ret, r, d, "p_k")
+    _dev(centroids, torch.float32, "centroids", (B, n_ret, Lmax // block, r))
+    dev = k_cache.device
+    if tables is None:
+        tables = (torch.zeros(B, dtype=torch.int32, device=dev),
+                  torch.zeros((B, n_ret, Lmax // block + 1), dtype=torch.int32,
+                              device=dev),
+                  torch.zeros((B, n_ret, Lmax), dtype=torch.int32, device=dev))
+    cl_m, cl_off, cl_mem = tables
+    _dev(cl_m, torch.int32, "cl_m", (B,))
+    _dev(cl_off, torch.int32, "cl_off", (B, n_ret, Lmax // block + 1))
+    _dev(cl_mem, torch.int32, "cl_members", (B, n_ret, Lmax))
+    nb = lib.rtp_cluster_workspace_bytes(B, Lmax, Hq, Hkv, d, mp, r, block)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_cluster_keys(
+        _ptr(k_cache), _ptr(cache_len), B, Lmax, Hq, Hkv, d, mp, _ptr(p_k), r,
+        block, n_recent, int(iters), _ptr(centroids), _ptr(cl_m),
+        _ptr(cl_off), _ptr(cl_mem), _ptr(w), w.numel(), _stream(dev)),
+        "rtp_cluster_keys")
+    return tables
+
+
+def decode_clustered_workspace_bytes(B: int, Lmax: int, Hq: int, Hkv: int,
+                                     is_retrieval, top_k: int,
+                                     n_recent: int = 2, r: int = 16,
+                                     d: int = 128, block: int = 64) -> int:
+    _, mp = _mask(is_retrieval, Hq)
+    return int(load().rtp_decode_clustered_workspace_bytes(
+        B, Lmax, Hq, Hkv, d, mp, r, block, top_k, n_recent))
+
+
+def hybrid_attn_decode_clustered(q, k_cache, v_cache, cache_len, is_retrieval,
+                                 window: int, p_q, centroids, tables,
+                                 top_k: int, n_recent: int = 2, r: int = 16,
+                                 block: int = 64, scale: float = 0.0,
+                                 want_lse: bool = False,
+                                 want_sel: bool = False, ws=None, out=None):
+    """One decode step choosing among the clusters of cluster_keys.
+    Returns out, or (out, lse, sel) when asked."""
+    lib = load()
+    B, Hq, d = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    _dev(q, torch.bfloat16, "q", (B, Hq, d))
+    _dev(k_cache, torch.bfloat16, "k_cache", (B, Hkv, Lmax, d))
+    _dev(v_cache, torch.bfloat16, "v_cache", (B, Hkv, Lmax, d))
+    _dev(cache_len, torch.int32, "cache_len", (B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    cl_m, cl_off, cl_mem = tables
+    if n_ret:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, Lmax // block, r))
+        _dev(cl_m, torch.int32, "cl_m", (B,))
+        _dev(cl_off, torch.int32, "cl_off", (B, n_ret, Lmax // block + 1))
+        _dev(cl_mem, torch.int32, "cl_members", (B, n_ret, Lmax))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    so = torch.full((B, n_ret, top_k + 1 + n_recent), -1, dtype=torch.int32,
+                    device=dev) if want_sel else None
+    nb = lib.rtp_decode_clustered_workspace_bytes(B, Lmax, Hq, Hkv, d, mp, r,
+                                                  block, top_k, n_recent)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_hybrid_attn_decode_clustered(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), B, Lmax, Hq,
+        Hkv, d, mp, int(window), _ptr(p_q), _ptr(centroids), _ptr(cl_m),
+        _ptr(cl_off), _ptr(cl_mem), r, block, top_k, n_recent, float(scale),
+        _ptr(out), _ptr(lse), _ptr(so), _ptr(w), w.numel(), _stream(dev)),
+        "rtp_hybrid_attn_decode_clustered")
+    if want_lse or want_sel:
+        return out, lse, so
     return out

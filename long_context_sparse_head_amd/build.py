@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "librtp.so")
 SOURCES = ["attn_window.hip", "attn.hip", "indexer.hip", "decode.hip",
-           "api.hip"]
+           "cluster.hip", "api.hip"]
 
 # Packed-FP32 VALU ops are turned off for all device code.
 HIPFLAGS = [

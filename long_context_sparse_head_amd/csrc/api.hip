@@ -570,11 +570,12 @@ int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
 static const int kDecSplit = 8;
 
 struct DecodeLayout {
-  size_t cs, sel, po, pml, total;
+  size_t cs, sel, po, pml, tok, tcnt, total;
 };
 
+// clustered: room for the token lists of the clustered decode
 static DecodeLayout decode_layout(int B, int Lmax, int Hq, int n_ret, int top_k,
-                                  int n_recent) {
+                                  int n_recent, bool clustered = false) {
   using rtp::align256;
   const size_t nbmax = (size_t)Lmax / 64, width = (size_t)top_k + 1 + n_recent;
   DecodeLayout L;
@@ -583,6 +584,11 @@ static DecodeLayout decode_layout(int B, int Lmax, int Hq, int n_ret, int top_k,
   L.sel = off; off += align256((size_t)B * n_ret * (width + 1) * 4);
   L.po = off;  off += align256((size_t)B * Hq * kDecSplit * rtp::kD * 4);
   L.pml = off; off += align256((size_t)B * Hq * kDecSplit * 2 * 4);
+  L.tok = L.tcnt = off;
+  if (clustered) {
+    L.tok = off;  off += align256((size_t)B * n_ret * Lmax * 4);
+    L.tcnt = off; off += align256((size_t)B * n_ret * 4);
+  }
   L.total = off;
   return L;
 }
@@ -598,6 +604,74 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
   return decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent).total;
 }
 
+size_t rtp_decode_clustered_workspace_bytes(int B, int Lmax, int Hq, int Hkv,
+                                            int d, const uint8_t* is_retrieval,
+                                            int r, int block, int top_k,
+                                            int n_recent) {
+  if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0 ||
+      n_recent < 1)
+    return 0;
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
+  return decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent, true).total;
+}
+
+size_t rtp_cluster_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
+                                   const uint8_t* is_retrieval, int r,
+                                   int block) {
+  if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0)
+    return 0;
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (check_indexer(hi.n_ret, r, block, 0) || r > 64) return 0;
+  return rtp::cluster_sizes(B, Lmax, hi.n_ret, r).total;
+}
+
+int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
+                     int Lmax, int Hq, int Hkv, int d,
+                     const uint8_t* is_retrieval, const float* p_k, int r,
+                     int block, int n_recent, int iters, float* centroids,
+                     int32_t* cl_m, int32_t* cl_off, int32_t* cl_members,
+                     void* ws, size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  if (int e = check_shape(0, Hq, Hkv, d)) return e;
+  if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
+  if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
+  const HeadInfo hi = scan_mask(is_retrieval, Hq);
+  if (int e = check_indexer(hi.n_ret, r, block, 0)) return e;
+  if (hi.n_ret > 0 && r > 64)
+    return fail(RTP_EUNSUPPORTED, "clustering supports r in {16, 32, 48, 64}");
+  if (n_recent < 1) return fail(RTP_EINVAL, "n_recent must be >= 1");
+  if (iters < 0 || iters > 1000) return fail(RTP_EINVAL, "iters must be in [0, 1000]");
+  if (B == 0 || hi.n_ret == 0 || Lmax < 64) return RTP_OK;
+  if (!k_cache || !cache_len || !p_k || !centroids || !cl_m || !cl_off ||
+      !cl_members)
+    return fail(RTP_EINVAL, "k_cache, cache_len, p_k, centroids and the cluster tables must be non-NULL");
+  const rtp::ClusterSizes z = rtp::cluster_sizes(B, Lmax, hi.n_ret, r);
+  if (iters > 0)
+    if (int e = check_ws(ws, ws_bytes, z.total)) return e;
+  rtp::ClusterLaunch a;
+  a.kc = static_cast<const rtp::u16*>(k_cache);
+  a.cache_len = cache_len;
+  a.p_k = p_k;
+  a.cent = centroids;
+  a.cl_m = cl_m;
+  a.cl_off = cl_off;
+  a.cl_mem = cl_members;
+  a.B = B;
+  a.Lmax = Lmax;
+  a.Hkv = Hkv;
+  a.n_ret = hi.n_ret;
+  a.r = r;
+  a.n_recent = n_recent;
+  a.iters = iters;
+  a.G = Hq / Hkv;
+  a.ret_heads = hi.ret_heads.data();
+  a.scratch = static_cast<char*>(ws);
+  hipError_t e = rtp::launch_cluster(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cluster launch");
+  return RTP_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -611,7 +685,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 const float* p_q, const float* centroids, int r, int block,
                 int top_k, int n_recent, float scale, void* out, float* lse,
                 int32_t* sel_out, void* ws, size_t ws_bytes, bool one_stream,
-                size_t* need, rtp_stream_t stream) {
+                size_t* need, rtp_stream_t stream,
+                const int32_t* cl_m = nullptr, const int32_t* cl_off = nullptr,
+                const int32_t* cl_mem = nullptr, bool clustered = false) {
   *need = 0;
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
@@ -626,7 +702,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     return fail(RTP_EINVAL, "q, k_cache, v_cache, cache_len and out must be non-NULL");
   if (hi.n_ret > 0 && (!p_q || !centroids))
     return fail(RTP_EINVAL, "p_q and centroids must be non-NULL with retrieval heads");
-  const DecodeLayout L = decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent);
+  if (clustered && hi.n_ret > 0 && (!cl_m || !cl_off || !cl_mem))
+    return fail(RTP_EINVAL, "the cluster tables must be non-NULL with retrieval heads");
+  const DecodeLayout L = decode_layout(B, Lmax, Hq, hi.n_ret, top_k, n_recent,
+                                       clustered);
   *need = L.total;
   if (!ws) return RTP_OK;
   if (int e = check_ws(ws, ws_bytes, L.total)) return e;
@@ -659,6 +738,13 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.part_o = reinterpret_cast<float*>(w + L.po);
   a.part_ml = reinterpret_cast<float*>(w + L.pml);
   a.one_stream = one_stream;
+  if (clustered && hi.n_ret > 0) {
+    a.cl_m = cl_m;
+    a.cl_off = cl_off;
+    a.cl_mem = cl_mem;
+    a.tok = reinterpret_cast<int32_t*>(w + L.tok);
+    a.tok_cnt = reinterpret_cast<int32_t*>(w + L.tcnt);
+  }
   hipError_t e = rtp::launch_decode(a, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (sel_out && hi.n_ret > 0) {
@@ -751,6 +837,30 @@ int rtp_hybrid_attn_decode_noalloc(const void* q, const void* k_cache,
                      is_retrieval, window, p_q, centroids, r, block, top_k,
                      n_recent, scale, out, lse, sel_out, ptr,
                      RTP_NOALLOC_SCRATCH_BYTES, true, &need, stream);
+}
+
+int rtp_hybrid_attn_decode_clustered(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* cache_len, int B, int Lmax, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, const int32_t* cl_m, const int32_t* cl_off,
+    const int32_t* cl_members, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  size_t need = 0;
+  if (!ws) {
+    int e = decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                        is_retrieval, window, p_q, centroids, r, block, top_k,
+                        n_recent, scale, out, lse, sel_out, nullptr, 0, false,
+                        &need, stream, cl_m, cl_off, cl_members, true);
+    if (e) return e;
+    return check_ws(ws, ws_bytes, need);
+  }
+  return decode_impl(q, k_cache, v_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                     is_retrieval, window, p_q, centroids, r, block, top_k,
+                     n_recent, scale, out, lse, sel_out, ws, ws_bytes, false,
+                     &need, stream, cl_m, cl_off, cl_members, true);
 }
 
 }  // extern "C"

@@ -207,7 +207,38 @@ struct DecodeLaunch {
   float* part_ml;
   // every kernel on `st` (no auxiliary stream, so nothing is created)
   bool one_stream = false;
+  // clustered decode (cl_off != nullptr): the cluster tables of
+  // launch_cluster, and space for the token lists [B, n_ret, Lmax] and
+  // their lengths [B, n_ret]
+  const int32_t* cl_m = nullptr; const int32_t* cl_off = nullptr;
+  const int32_t* cl_mem = nullptr;
+  int32_t* tok = nullptr; int32_t* tok_cnt = nullptr;
 };
+
+// K-cache clustering: the clustered tokens of one (sequence, retrieval
+// head) are split into at most kClChunks chunks for the stable grouping.
+constexpr int kClChunks = 64;
+struct ClusterSizes {
+  size_t x, assign, hist, total;  // byte offsets in the workspace
+};
+inline ClusterSizes cluster_sizes(int B, int Lmax, int n_ret, int r) {
+  const size_t rows = (size_t)B * n_ret * Lmax, nbmax = (size_t)Lmax / 64;
+  ClusterSizes z;
+  size_t off = 0;
+  z.x = off;      off += align256(rows * r * 4);
+  z.assign = off; off += align256(rows * 4);
+  z.hist = off;   off += align256((size_t)B * n_ret * kClChunks * nbmax * 4);
+  z.total = off;
+  return z;
+}
+struct ClusterLaunch {
+  const u16* kc; const int32_t* cache_len; const float* p_k;
+  float* cent; int32_t* cl_m; int32_t* cl_off; int32_t* cl_mem;
+  int B, Lmax, Hkv, n_ret, r, n_recent, iters, G;
+  const uint8_t* ret_heads;  // host
+  char* scratch;             // cluster_sizes(...).total bytes, 256-aligned
+};
+hipError_t launch_cluster(const ClusterLaunch& a, hipStream_t st);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st);
 
 hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,

@@ -163,6 +163,10 @@ hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
 // ------------------------------------------------------------- block choice
 struct DecSelArgs {
   int Hq, Lmax, n_ret, r, nbmax, top_k, n_recent, width;
+  // clustered decode: cluster ids 1 .. cl_m[b]-1 with offsets cl_off
+  // [B, n_ret, nbmax + 1]; an empty cluster is never chosen ahead of a
+  // non-empty candidate (nullptr: block decode)
+  const int32_t* cl_m; const int32_t* cl_off;
   uint8_t head_of_rho[kMaxHeads];
 };
 
@@ -222,12 +226,19 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   const float* cb = cent + row_id * a.nbmax * a.r;
   float* srow = cscores + row_id * a.nbmax;
   const bool in_lds = n_c <= TK_LDS;
+  // clustered decode: candidate e (id e + 1) is an empty cluster when
+  // e + 1 < m and its offsets are equal; it then gets the lowest key (0,
+  // the order key of the NaN bit pattern 0xffffffff), below every score
+  const int32_t* coff = a.cl_off ? a.cl_off + row_id * (a.nbmax + 1) : nullptr;
+  const int cm = a.cl_off ? min(a.cl_m[b], n_b - a.n_recent) : 0;
   // Candidate scores, several candidates per thread in flight; a centroid
   // row is r floats read as float4 (consecutive lanes read consecutive
   // rows). For r = 16 every load of a group of candidates is issued before
   // the first is used, so the row costs a few memory latencies, not one per
   // float4.
   auto put = [&](int e, float v) {
+    if (coff && e + 1 < cm && coff[e + 2] == coff[e + 1])
+      v = __uint_as_float(0xffffffffu);
     if (in_lds) keys[e + (e >> 5)] = order_key(v);
     else srow[e] = v;
   };
@@ -297,6 +308,70 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   for (int j = tid; j < n_rec; j += 256) out[1 + a.top_k + j] = n_c + 1 + j;
 }
 
+// --------------------------------------------------- clustered token list
+struct DecTokArgs {
+  const int32_t* cache_len; const int32_t* sel; const int32_t* sel_cnt;
+  const int32_t* cl_m; const int32_t* cl_off; const int32_t* cl_mem;
+  int32_t* tok; int32_t* tok_cnt;
+  int Lmax, nbmax, n_ret, width, n_recent;
+};
+
+// grid (n_ret, B), 256 threads: the tokens a retrieval head attends in the
+// clustered decode, in the order of its kept ids (ascending): the members
+// of a kept cluster (1 <= id < m, in ascending token order) or every token
+// of a kept block (the sink, blocks that left the recent window after the
+// clustering, the recent blocks). Segment starts come from a block-wide
+// scan of the segment lengths; each wave then copies whole segments.
+__global__ __launch_bounds__(256) void dec_tokens_kernel(const DecTokArgs a) {
+  __shared__ int tmp[4];
+  __shared__ int sid[256], spos[256], slen[256];
+  __shared__ int carry_s;
+  const int rho = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int L = a.cache_len[b];
+  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
+  const int n_b = (L + 63) / 64;
+  const size_t row = (size_t)b * a.n_ret + rho;
+  const int n_sel = a.sel_cnt[row];
+  const int32_t* ids = a.sel + row * a.width;
+  const int m = min(a.cl_m[b], n_b - a.n_recent);  // recent blocks stay blocks
+  const int32_t* off = a.cl_off + row * (a.nbmax + 1);
+  const int32_t* mem = a.cl_mem + row * a.Lmax;
+  int32_t* out = a.tok + row * a.Lmax;
+  int carry = 0;
+  for (int s0 = 0; s0 < n_sel; s0 += 256) {
+    const int e = s0 + tid;
+    const int id = e < n_sel ? ids[e] : -1;
+    int len = 0;
+    if (id >= 0) {
+      if (id >= 1 && id < m) len = min(max(off[id + 1] - off[id], 0), a.Lmax);
+      else len = max(0, min(L, 64 * id + 64) - 64 * id);
+    }
+    const int incl = block_incl_scan(len, tmp);
+    sid[tid] = id;
+    spos[tid] = carry + incl - len;
+    slen[tid] = len;
+    if (tid == 255) carry_s = carry + incl;
+    __syncthreads();
+    const int nseg = min(256, n_sel - s0);
+    // (the list holds at most Lmax ids and every id is a cached token, also
+    // for tables that do not match this cache)
+    for (int si = wave; si < nseg; si += 4) {
+      const int id = sid[si], pos = spos[si], len = slen[si];
+      const int n_w = max(0, min(len, a.Lmax - pos));
+      if (id >= 1 && id < m) {
+        const int32_t* src = mem + min(max(off[id], 0), a.Lmax - len);
+        for (int i = lane; i < n_w; i += 64) out[pos + i] = min(max(src[i], 0), L - 1);
+      } else {
+        for (int i = lane; i < n_w; i += 64) out[pos + i] = 64 * id + i;
+      }
+    }
+    carry = carry_s;
+    __syncthreads();
+  }
+  if (tid == 0) a.tok_cnt[row] = min(carry, a.Lmax);
+}
+
 // ---------------------------------------------------------------- attention
 struct DecAttnArgs {
   const u16* q; const u16* kc; const u16* vc; const int32_t* cache_len;
@@ -308,6 +383,9 @@ struct DecAttnArgs {
   // unit u: bits 0-1 kind (0 window heads of one KV group, 1 retrieval
   // head), bits 8-15 KV head, bits 16-23 head count, bits 24-31 first index
   // into hlist
+  // clustered decode: per (sequence, retrieval head) a list of tok_width
+  // token ids, tok_cnt of them used (read by the token-list instance)
+  const int32_t* tok; const int32_t* tok_cnt; int tok_width;
   uint32_t desc[2 * kMaxHeads];
   uint8_t rho[2 * kMaxHeads];
   uint8_t hlist[kMaxHeads];
@@ -334,6 +412,14 @@ constexpr int kDecTile = 32 * kD * 2;
 // registers (a whole iteration ahead) and written to LDS at the start of
 // the next iteration; plain loads, not LDS DMA, keep the compiler's wait
 // counts exact.
+//
+// kTok (clustered decode, retrieval units only): the keys are a list of
+// token ids instead of blocks. Tile t of the list is entries 32 t .. 32 t +
+// 31; splits take whole pairs of tiles, so with clusters equal to blocks
+// every tile, split and wave sees exactly the keys of the block walk. Row r
+// of a tile is gathered from token id (entry r), the ids of the next tile
+// having been loaded one iteration ahead.
+template <bool kTok>
 __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char kvbuf[4][2][kDecTile];
   __shared__ float red_ml[4][kDecMaxUnitHeads][2];
@@ -360,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     k_begin = min(lo + s * per, L);
     k_end = min(lo + (s + 1) * per, L);
     nt = (k_end - k_begin + 31) / 32;
-  } else {
+  } else if (!kTok) {
     const int rho = a.rho[u];
     const int nsel = a.sel_cnt[(size_t)b * a.n_ret + rho];
     list = (const_i32_ptr)(a.sel + ((size_t)b * a.n_ret + rho) * a.sel_width);
@@ -368,6 +454,18 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     blk0 = min(s * bps, nsel);
     const int blk1 = min(blk0 + bps, nsel);
     nt = 2 * (blk1 - blk0);
+  }
+  // token-list mode: entries T0*32 .. of a list of n_tok token ids
+  const int32_t* tl = nullptr;
+  int n_tok = 0, T0 = 0;
+  if (kTok && kind == 1) {
+    const size_t row = (size_t)b * a.n_ret + a.rho[u];
+    n_tok = a.tok_cnt[row];
+    tl = a.tok + row * a.tok_width;
+    const int ntile = (n_tok + 31) / 32;
+    const int per = 2 * (((ntile + 1) / 2 + a.n_split - 1) / a.n_split);
+    T0 = min(s * per, ntile);
+    nt = min(per, ntile - T0);
   }
 
   const size_t kv_off = ((size_t)b * a.Hkv + kvh) * a.Lmax * kD;
@@ -392,7 +490,9 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     base = 0;
     nvalid = 0;
     if (t < nt) {
-      if (kind == 0) {
+      if (kTok) {
+        nvalid = min(32, n_tok - 32 * (T0 + t));
+      } else if (kind == 0) {
         base = k_begin + 32 * t;
         nvalid = min(32, k_end - base);
       } else {
@@ -439,6 +539,22 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
       }
     }
   };
+  // token-list mode: lane l < 32 holds the id of entry l of tile t (past
+  // the list: the last entry, a valid row whose weight is 0); ids of the 32
+  // rows of a tile then come from that lane by a cross-lane read
+  auto ids_of = [&](int t) -> int {
+    if (t >= nt) return 0;
+    return tl[min(32 * (T0 + t) + (lane & 31), n_tok - 1)];
+  };
+  auto load_rows_tok = [&](const u16* src, int idv, bool kswz, u32x4 (&st)[8]) {
+#pragma unroll
+    for (int ins = 0; ins < 8; ++ins) {
+      const int r = 4 * ins + (lane >> 4);
+      const int id = __shfl(idv, r);
+      const int chunk = (lane & 15) ^ (kswz ? (r & 15) : 4 * ((r >> 3) & 1));
+      st[ins] = *reinterpret_cast<const u32x4*>(src + (size_t)id * kD + chunk * 8);
+    }
+  };
   char* const ktile = kvbuf[wave][0];
   char* const vtile = kvbuf[wave][1];
   auto store_rows = [&](char* tile, const u32x4 (&st)[8]) {
@@ -475,8 +591,16 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
   int base, nvalid;
   tile_at(wave, base, nvalid);
   u32x4 kst[8], vst[8];
-  load_rows(kbase, base, nvalid, true, kst);
-  load_rows(vbase, base, nvalid, false, vst);
+  int idn = 0;
+  if (kTok) {
+    const int idv = ids_of(wave);
+    load_rows_tok(kbase, idv, true, kst);
+    load_rows_tok(vbase, idv, false, vst);
+    idn = ids_of(4 + wave);
+  } else {
+    load_rows(kbase, base, nvalid, true, kst);
+    load_rows(vbase, base, nvalid, false, vst);
+  }
   const int iters = (nt + 3) / 4;
   for (int it = 0; it < iters; ++it) {
     // this tile to LDS (the previous tile's reads are done: a wave's LDS
@@ -487,8 +611,14 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     store_rows(vtile, vst);
     int nbase, nnvalid;
     tile_at((it + 1) * 4 + wave, nbase, nnvalid);
-    load_rows(kbase, nbase, nnvalid, true, kst);
-    load_rows(vbase, nbase, nnvalid, false, vst);
+    if (kTok) {
+      load_rows_tok(kbase, idn, true, kst);
+      load_rows_tok(vbase, idn, false, vst);
+      idn = ids_of((it + 2) * 4 + wave);
+    } else {
+      load_rows(kbase, nbase, nnvalid, true, kst);
+      load_rows(vbase, nbase, nnvalid, false, vst);
+    }
     if (nvalid > 0) {  // wave-uniform
       f32x16 sacc = {};
 #pragma unroll
@@ -622,7 +752,10 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   sa.top_k = a.top_k;
   sa.n_recent = a.n_recent;
   sa.width = width;
+  sa.cl_m = a.cl_m;
+  sa.cl_off = a.cl_off;
   for (int i = 0; i < kMaxHeads; ++i) sa.head_of_rho[i] = i < a.n_ret ? a.ret_heads[i] : 0;
+  const bool clustered = a.cl_off != nullptr;
   DecAttnArgs da;
   da.q = a.q;
   da.kc = a.kc;
@@ -640,6 +773,9 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   da.n_split = a.n_split;
   da.sel_width = width;
   da.c = a.scale * 1.4426950408889634f;
+  da.tok = a.tok;
+  da.tok_cnt = a.tok_cnt;
+  da.tok_width = a.Lmax;
   // units: window heads of each KV group (up to kDecMaxUnitHeads per unit)
   // first, then one unit per retrieval head
   int nu = 0, nl = 0, rho = 0;
@@ -677,12 +813,36 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
                        a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
                        a.sel + (size_t)a.B * a.n_ret * width);
     prof_end(st);
+    if (clustered) {
+      DecTokArgs ta;
+      ta.cache_len = a.cache_len;
+      ta.sel = a.sel;
+      ta.sel_cnt = a.sel + (size_t)a.B * a.n_ret * width;
+      ta.cl_m = a.cl_m;
+      ta.cl_off = a.cl_off;
+      ta.cl_mem = a.cl_mem;
+      ta.tok = a.tok;
+      ta.tok_cnt = a.tok_cnt;
+      ta.Lmax = a.Lmax;
+      ta.nbmax = nbmax;
+      ta.n_ret = a.n_ret;
+      ta.width = width;
+      ta.n_recent = a.n_recent;
+      prof_begin("dec_tokens", st);
+      hipLaunchKernelGGL(dec_tokens_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st, ta);
+      prof_end(st);
+    }
   };
   auto attend = [&](const char* name, int base, int n, hipStream_t on) {
     DecAttnArgs d = da;
     d.unit_base = base;
     prof_begin(name, on);
-    hipLaunchKernelGGL(dec_attn_kernel, dim3(a.n_split, n, a.B), dim3(256), 0, on, d);
+    if (clustered && base >= n_win_units)  // retrieval units: token lists
+      hipLaunchKernelGGL(dec_attn_kernel<true>, dim3(a.n_split, n, a.B), dim3(256), 0,
+                         on, d);
+    else
+      hipLaunchKernelGGL(dec_attn_kernel<false>, dim3(a.n_split, n, a.B), dim3(256), 0,
+                         on, d);
     prof_end(on);
   };
   hipError_t e = hipSuccess;

@@ -217,3 +217,47 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(4, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         rtp.dense_attn_prefill(q, q[:1], q[:1])
+
+
+def test_cluster_workspace_and_validation():
+    lib = rtp.load()
+    al = lambda x: (x + 255) // 256 * 256
+    m, mp = _mask([0, 1, 1, 0])
+    B, Lmax = 3, 64 * 50 + 7
+    nb = Lmax // 64
+    want = al(B * 2 * Lmax * 16 * 4) + al(B * 2 * Lmax * 4) + \
+        al(B * 2 * 64 * nb * 4)
+    assert lib.rtp_cluster_workspace_bytes(B, Lmax, 4, 2, 128, mp, 16, 64) \
+        == want
+    assert lib.rtp_cluster_workspace_bytes(B, Lmax, 4, 2, 128, mp, 80, 64) \
+        == 0  # r > 64 is not clustered
+    # the clustered decode adds the token lists to the decode workspace
+    dec = lib.rtp_decode_workspace_bytes(B, Lmax, 4, 2, 128, mp, 16, 64, 8, 2)
+    assert lib.rtp_decode_clustered_workspace_bytes(
+        B, Lmax, 4, 2, 128, mp, 16, 64, 8, 2) == \
+        dec + al(B * 2 * Lmax * 4) + al(B * 2 * 4)
+    P = ctypes.c_void_p
+    args = lambda **kw: dict(dict(kc=P(1), cl=P(1), r=16, nrec=2, it=1,
+                                  tab=P(1), ws=P(256)), **kw)
+
+    def call(a):
+        return lib.rtp_cluster_keys(a["kc"], a["cl"], B, Lmax, 4, 2, 128, mp,
+                                    P(1), a["r"], 64, a["nrec"], a["it"],
+                                    P(1), a["tab"], a["tab"], a["tab"],
+                                    a["ws"], 1 << 40, None)
+    assert call(args(r=80)) == -2
+    assert call(args(nrec=0)) == -1
+    assert call(args(it=-1)) == -1
+    assert call(args(kc=None)) == -1
+    assert call(args(tab=None)) == -1
+    assert call(args(ws=None)) == -3
+    # clustered decode: tables missing with a retrieval head
+    st = lib.rtp_hybrid_attn_decode_clustered(
+        P(1), P(1), P(1), P(1), 2, 4096, 4, 2, 128, mp, 64, P(1), P(1), None,
+        P(1), P(1), 16, 64, 8, 2, 0.0, P(1), None, None, P(256), 1 << 40,
+        None)
+    assert st == -1
+    st = lib.rtp_hybrid_attn_decode_clustered(
+        P(1), P(1), P(1), P(1), 2, 4096, 4, 2, 128, mp, 64, P(1), P(1), P(1),
+        P(1), P(1), 16, 64, 8, 2, 0.0, P(1), None, None, None, 0, None)
+    assert st == -3
