@@ -63,6 +63,20 @@ COUNTERS = {
         "fetch_bytes": 2761143410073,
         "write_bytes": 6217822925},
 }
+_IDX = {"unit": "indexer.hip",
+        "sources": [_K + "indexer.hip", _K + "select.h"],
+        "sha256": "dbf64923fbc772b3963dfc0396a8a5f5f91c34f12abaea8a340abd38226277b8"}
+for _key, _kern, _f, _w in (
+        # bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1
+        ("proj_keys@128k", "proj_keys", 68690125, 41943040),
+        ("proj_qmeans@128k", "proj_qmeans", 168186675, 656282),
+        ("block_scores@128k", "block_scores", 263329382, 42321715),
+        ("topk@128k", "topk", 43197235, 5898240),
+        # bench.py --leg 1m --steps 2 --warmup 1
+        ("proj_keys@1m", "proj_keys", 1112170086, 1543504589),
+        ("proj_qmeans@1m", "proj_qmeans", 6175680307, 24130867),
+        ("score_select@1m", "score_select", 57258742374, 15278940160)):
+    COUNTERS[_key] = dict(_IDX, kernel=_kern, fetch_bytes=_f, write_bytes=_w)
 TRAFFIC_KEY = "attn_window@128k"
 
 
@@ -354,6 +368,112 @@ def bench_decode(rtp, torch, w, steps, warmup):
     return res
 
 
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # 32-bit VALU lane-ops/s
+CLUSTER_ITERS = 2
+
+
+def bench_cluster(rtp, torch, w, steps, warmup):
+    """K-cache clustering (Lloyd steps seeded by the block centroids) and
+    the clustered decode step on the decode workload."""
+    from workloads import make_decode
+    dev = "cuda"
+    y = make_decode(w, device=dev)
+    cl = torch.from_numpy(y["cache_len"]).to(dev)
+    pq = torch.from_numpy(y["p_q"]).to(dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    B, Hq, Hkv, L = w.batch, w.Hq, w.Hkv, w.L
+    cent0 = rtp.build_centroids(y["k_cache"], cl, y["is_retrieval"], pk)
+    cent = cent0.clone()
+    cws = torch.empty(rtp.cluster_workspace_bytes(B, L, Hq, Hkv,
+                                                  y["is_retrieval"], w.r),
+                      dtype=torch.uint8, device=dev)
+    tables = rtp.cluster_keys(y["k_cache"], cl, y["is_retrieval"], pk, cent,
+                              iters=CLUSTER_ITERS, n_recent=w.n_recent, ws=cws)
+    torch.cuda.synchronize()
+    reps = 3
+    with rtp.KernelTimer() as kc:
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            cent.copy_(cent0)
+            rtp.cluster_keys(y["k_cache"], cl, y["is_retrieval"], pk, cent,
+                             iters=CLUSTER_ITERS, n_recent=w.n_recent, ws=cws,
+                             tables=tables)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+    cks = kernel_stats(kc.records, reps)
+    cl_ms = sum(v["ms_total"] for k, v in cks.items()
+                if k.startswith("cl_")) / reps
+    ws = torch.empty(rtp.decode_clustered_workspace_bytes(
+        B, L, Hq, Hkv, y["is_retrieval"], w.top_k, w.n_recent, w.r),
+        dtype=torch.uint8, device=dev)
+    out = torch.empty_like(y["q"])
+
+    def call(want_sel=False):
+        return rtp.hybrid_attn_decode_clustered(
+            y["q"], y["k_cache"], y["v_cache"], cl, y["is_retrieval"],
+            w.window, pq, cent, tables, w.top_k, n_recent=w.n_recent, ws=ws,
+            out=out, want_sel=want_sel)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    with rtp.KernelTimer() as kt:
+        t3 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        t4 = time.perf_counter()
+    ms = (t4 - t3) * 1e3 / steps
+    ks = kernel_stats(kt.records, steps)
+    _, _, sel = call(want_sel=True)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    m = tables[0].cpu().numpy()
+    off = tables[1].cpu().numpy()
+    n_b = -(-L // 64)
+    kept = 0
+    for b in range(B):
+        for rho in range(sel.shape[1]):
+            for c in sel[b, rho]:
+                if c < 0:
+                    continue
+                c = int(c)
+                kept += int(off[b, rho, c + 1] - off[b, rho, c]) \
+                    if 1 <= c < m[b] else min(L, 64 * c + 64) - 64 * c
+    G = Hq // Hkv
+    swa_groups = sum(1 for g in range(Hkv)
+                     if any(not y["is_retrieval"][h]
+                            for h in range(g * G, (g + 1) * G)))
+    kv_row = 2 * 128 * 2
+    win_bytes = B * swa_groups * min(w.window, L) * kv_row
+    ret_bytes = kept * kv_row
+    cen_bytes = B * sel.shape[1] * (n_b - w.n_recent - 1) * w.r * 4
+    byt = win_bytes + ret_bytes + cen_bytes
+    # nearest-centroid search: (token, cluster) pairs of every (sequence,
+    # head) per step, 3 VALU ops each (compare, two selects)
+    C = m.astype(np.int64) - 1
+    pairs = int(sel.shape[1] * (64 * C * C).sum())
+    res = {
+        "workload": w.name, "iters": CLUSTER_ITERS,
+        "cluster_ms": cl_ms,
+        "cluster_wall_ms": (t2 - t1) * 1e3 / reps,
+        "cluster_kernels_ms": {k: round(v["ms_total"] / reps, 4)
+                               for k, v in cks.items()},
+        "assign_pairs_per_step": pairs,
+        "decode_ms_per_step": ms, "decode_tokens_per_s": B / (ms / 1e3),
+        "decode_kept_tokens": kept,
+        "decode_bytes_per_step_alg": byt,
+        "decode_step_gbs_alg": byt / (ms / 1e3) / 1e9,
+        "decode_kernels_ms_per_step": {k: round(v["ms_per_step"], 4)
+                                       for k, v in ks.items()},
+    }
+    if "cl_assign" in cks:
+        t = cks["cl_assign"]["ms_per_launch"] / 1e3
+        res["assign_valu_frac"] = 3 * pairs / t / 1e12 / PEAK_VALU_TOPS
+    del y, ws, out, cent, cent0, cws, tables
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ CPU oracle
 def cpu_baseline(w, ret_pairs_total, budget_s=15.0):
     """Time the oracle on a bounded sample of the workload and scale it to
@@ -447,7 +567,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--leg", choices=["1m", "32k", "decode", "dense", "full",
-                                      "dense1m"],
+                                      "dense1m", "cluster"],
                     help="run only this secondary leg and print its detail "
                          "(for profiling); no bench line")
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -481,6 +601,9 @@ def main():
         if args.leg == "decode":
             res = bench_decode(rtp, torch, DECODE_32x256K, args.steps,
                                args.warmup)
+        elif args.leg == "cluster":
+            res = bench_cluster(rtp, torch, DECODE_32x256K, args.steps,
+                                args.warmup)
         else:
             w = {"1m": PREFILL_1M, "32k": PREFILL_32K,
                  "dense": PREFILL_128K, "full": PREFILL_128K,
@@ -512,6 +635,11 @@ def main():
         extra["decode"] = bench_decode(rtp, torch, DECODE_32x256K, args.steps,
                                        args.warmup)
         log(f"[bench] decode: {extra['decode']['ms_per_step']:.3f} ms/step")
+        extra["cluster"] = bench_cluster(rtp, torch, DECODE_32x256K,
+                                         args.steps, args.warmup)
+        log(f"[bench] clustering ({CLUSTER_ITERS} steps): "
+            f"{extra['cluster']['cluster_ms']:.2f} ms; clustered decode "
+            f"{extra['cluster']['decode_ms_per_step']:.3f} ms/step")
         extra["dense_128k"] = bench_prefill(rtp, torch, PREFILL_128K,
                                             max(2, args.steps // 4), 1,
                                             dense=True)
