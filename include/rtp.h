@@ -23,6 +23,11 @@
  *    and on the decode recipe: decode scores per-block key centroids
  *    c_kb = mean_{j in kb} P_k k_j with the projected query, keeps the sink,
  *    the last n_recent blocks and the top_k candidates, and attends exactly.
+ *  - Same article, paragraph on feature and sequence compression working
+ *    together (related keys gather in the low-rank space): rtp_cluster_keys
+ *    groups the projected keys by k-means (Lloyd's algorithm, seeded by the
+ *    blocks), and rtp_hybrid_attn_decode_clustered lets the retrieval heads
+ *    choose among those clusters instead of blocks.
  *
  * Softmax everywhere: s_j = scale * q.k_j, lse = log sum_j exp(s_j),
  * out = sum_j exp(s_j - lse) v_j, computed with fp32 accumulation.
