@@ -429,6 +429,74 @@ int rtp_hybrid_attn_decode_clustered(
     float scale, void* out, float* lse, int32_t* sel_out, void* ws,
     size_t ws_bytes, rtp_stream_t stream);
 
+/*
+ * Paged decode cache (the survey's incremental-cache step with paged KV; a
+ * serving engine keeps the K/V of many sequences in fixed-size pages). The
+ * *_paged calls below are the calls of the same name without the suffix,
+ * with the contiguous cache [B,Hkv,Lmax,d] replaced by:
+ *
+ *  k_pages, v_pages [n_pages,Hkv,block,d] bf16: a pool of pages, each
+ *    holding `block` (= 64) consecutive tokens of every KV head;
+ *  block_table [B,max_blocks] int32 DEVICE array: entry (b, j) is the page
+ *    holding tokens 64 j .. 64 j + 63 of sequence b (the caller owns page
+ *    allocation; entries past the sequence's last block are not read);
+ *  Lmax = 64 * max_blocks everywhere the unpaged call uses it (centroid
+ *    table [B,n_ret,max_blocks,r], cluster tables, workspace queries).
+ *
+ *  Page ids outside [0, n_pages) are clamped into the pool, so a bad table
+ *  gives wrong results but no access outside the pool. Results equal those
+ *  of the unpaged call on the cache the table describes, bit for bit.
+ *  Extra errors: RTP_EINVAL for a NULL block_table, max_blocks < 1 or
+ *  n_pages < 1 (when B > 0).
+ */
+int rtp_build_centroids_paged(const void* k_pages, const int32_t* block_table,
+                              int max_blocks, int n_pages,
+                              const int32_t* cache_len, int B, int Hq, int Hkv,
+                              int d, const uint8_t* is_retrieval,
+                              const float* p_k, int r, int block,
+                              float* centroids, rtp_stream_t stream);
+
+/* Appends at token cache_len[b], i.e. into page block_table[b, L_b / 64]
+ * at row L_b % 64 (that page must be allocated in the table). */
+int rtp_decode_append_paged(void* k_pages, void* v_pages,
+                            const int32_t* block_table, int max_blocks,
+                            int n_pages, int32_t* cache_len, const void* k_new,
+                            const void* v_new, int B, int Hq, int Hkv, int d,
+                            const uint8_t* is_retrieval, const float* p_k,
+                            int r, int block, float* centroids,
+                            rtp_stream_t stream);
+
+/* ws: rtp_decode_workspace_bytes(B, 64 * max_blocks, ...) bytes. */
+int rtp_hybrid_attn_decode_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, int max_blocks, int n_pages,
+    const int32_t* cache_len, int B, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream);
+
+/* ws: rtp_cluster_workspace_bytes(B, 64 * max_blocks, ...) bytes. */
+int rtp_cluster_keys_paged(const void* k_pages, const int32_t* block_table,
+                           int max_blocks, int n_pages,
+                           const int32_t* cache_len, int B, int Hq, int Hkv,
+                           int d, const uint8_t* is_retrieval,
+                           const float* p_k, int r, int block, int n_recent,
+                           int iters, float* centroids, int32_t* cl_m,
+                           int32_t* cl_off, int32_t* cl_members, void* ws,
+                           size_t ws_bytes, rtp_stream_t stream);
+
+/* ws: rtp_decode_clustered_workspace_bytes(B, 64 * max_blocks, ...) bytes. */
+int rtp_hybrid_attn_decode_clustered_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, int max_blocks, int n_pages,
+    const int32_t* cache_len, int B, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, const int32_t* cl_m, const int32_t* cl_off,
+    const int32_t* cl_members, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

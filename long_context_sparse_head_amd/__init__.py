@@ -30,6 +30,9 @@ __all__ = [
     "version", "KernelTimer", "NOALLOC_SCRATCH_BYTES",
     "cluster_workspace_bytes", "cluster_keys",
     "decode_clustered_workspace_bytes", "hybrid_attn_decode_clustered",
+    "PagedCache", "build_centroids_paged", "decode_append_paged",
+    "hybrid_attn_decode_paged", "cluster_keys_paged",
+    "hybrid_attn_decode_clustered_paged",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
@@ -85,6 +88,19 @@ _SIGS = {
                                               _I, _U8P, _I, _P, _P, _P, _P, _P,
                                               _I, _I, _I, _I, _F, _P, _P, _P,
                                               _P, _Z, _P]),
+    "rtp_build_centroids_paged": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I,
+                                       _U8P, _P, _I, _I, _P, _P]),
+    "rtp_decode_append_paged": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I,
+                                     _I, _I, _U8P, _P, _I, _I, _P, _P]),
+    "rtp_hybrid_attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I,
+                                          _I, _I, _U8P, _I, _P, _P, _I, _I,
+                                          _I, _I, _F, _P, _P, _P, _P, _Z, _P]),
+    "rtp_cluster_keys_paged": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _U8P,
+                                    _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _Z,
+                                    _P]),
+    "rtp_hybrid_attn_decode_clustered_paged": (_I, [
+        _P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _U8P, _I, _P, _P, _P, _P,
+        _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z, _P]),
 }
 
 
@@ -615,6 +631,175 @@ def hybrid_attn_decode_clustered(q, k_cache, v_cache, cache_len, is_retrieval,
         _ptr(cl_off), _ptr(cl_mem), r, block, top_k, n_recent, float(scale),
         _ptr(out), _ptr(lse), _ptr(so), _ptr(w), w.numel(), _stream(dev)),
         "rtp_hybrid_attn_decode_clustered")
+    if want_lse or want_sel:
+        return out, lse, so
+    return out
+
+
+class PagedCache:
+    """A paged decode cache: k_pages / v_pages [n_pages, Hkv, 64, d] bf16 and
+    a block table [B, max_blocks] int32 of page ids (device tensors)."""
+
+    def __init__(self, k_pages, v_pages, block_table):
+        n_pages, Hkv, blk, d = k_pages.shape
+        _dev(k_pages, torch.bfloat16, "k_pages")
+        _dev(v_pages, torch.bfloat16, "v_pages", (n_pages, Hkv, blk, d))
+        _dev(block_table, torch.int32, "block_table")
+        if blk != 64 or block_table.dim() != 2:
+            raise ValueError("pages hold 64 tokens; block_table is [B, max_blocks]")
+        self.k, self.v, self.table = k_pages, v_pages, block_table
+        self.n_pages, self.Hkv, self.d = n_pages, Hkv, d
+        self.B, self.max_blocks = block_table.shape
+        self.Lmax = 64 * self.max_blocks
+
+
+def build_centroids_paged(pc: PagedCache, cache_len, is_retrieval, p_k,
+                          r: int = 16, block: int = 64, out=None):
+    """build_centroids over a paged cache: [B, n_ret, max_blocks, r]."""
+    lib = load()
+    Hq = len(is_retrieval)
+    _dev(cache_len, torch.int32, "cache_len", (pc.B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    _proj(p_k, n_ret, r, pc.d, "p_k")
+    if out is None:
+        out = torch.zeros((pc.B, n_ret, pc.max_blocks, r), dtype=torch.float32,
+                          device=pc.k.device)
+    _check(lib.rtp_build_centroids_paged(
+        _ptr(pc.k), _ptr(pc.table), pc.max_blocks, pc.n_pages, _ptr(cache_len),
+        pc.B, Hq, pc.Hkv, pc.d, mp, _ptr(p_k), r, block, _ptr(out),
+        _stream(pc.k.device)), "rtp_build_centroids_paged")
+    return out
+
+
+def decode_append_paged(pc: PagedCache, cache_len, k_new, v_new,
+                        is_retrieval, p_k=None, centroids=None, r: int = 16,
+                        block: int = 64):
+    lib = load()
+    Hq = len(is_retrieval)
+    _dev(cache_len, torch.int32, "cache_len", (pc.B,))
+    _dev(k_new, torch.bfloat16, "k_new", (pc.B, pc.Hkv, pc.d))
+    _dev(v_new, torch.bfloat16, "v_new", (pc.B, pc.Hkv, pc.d))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    if n_ret:
+        _proj(p_k, n_ret, r, pc.d, "p_k")
+        _dev(centroids, torch.float32, "centroids",
+             (pc.B, n_ret, pc.max_blocks, r))
+    _check(lib.rtp_decode_append_paged(
+        _ptr(pc.k), _ptr(pc.v), _ptr(pc.table), pc.max_blocks, pc.n_pages,
+        _ptr(cache_len), _ptr(k_new), _ptr(v_new), pc.B, Hq, pc.Hkv, pc.d, mp,
+        _ptr(p_k) if n_ret else None, r, block,
+        _ptr(centroids) if n_ret else None, _stream(pc.k.device)),
+        "rtp_decode_append_paged")
+
+
+def _decode_outputs(q, n_ret, top_k, n_recent, want_lse, want_sel, out):
+    B, Hq, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) \
+        if want_lse else None
+    so = torch.full((B, n_ret, top_k + 1 + n_recent), -1, dtype=torch.int32,
+                    device=dev) if want_sel else None
+    return out, lse, so
+
+
+def hybrid_attn_decode_paged(q, pc: PagedCache, cache_len, is_retrieval,
+                             window: int, p_q, centroids, top_k: int,
+                             n_recent: int = 2, r: int = 16, block: int = 64,
+                             scale: float = 0.0, want_lse: bool = False,
+                             want_sel: bool = False, ws=None, out=None):
+    lib = load()
+    B, Hq, d = q.shape
+    _dev(q, torch.bfloat16, "q", (pc.B, Hq, pc.d))
+    _dev(cache_len, torch.int32, "cache_len", (pc.B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    if n_ret:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, pc.max_blocks, r))
+    out, lse, so = _decode_outputs(q, n_ret, top_k, n_recent, want_lse,
+                                   want_sel, out)
+    nb = lib.rtp_decode_workspace_bytes(B, pc.Lmax, Hq, pc.Hkv, d, mp, r,
+                                        block, top_k, n_recent)
+    w = _workspace(nb, q.device, ws)
+    _check(lib.rtp_hybrid_attn_decode_paged(
+        _ptr(q), _ptr(pc.k), _ptr(pc.v), _ptr(pc.table), pc.max_blocks,
+        pc.n_pages, _ptr(cache_len), B, Hq, pc.Hkv, d, mp, int(window),
+        _ptr(p_q), _ptr(centroids), r, block, top_k, n_recent, float(scale),
+        _ptr(out), _ptr(lse), _ptr(so), _ptr(w), w.numel(),
+        _stream(q.device)), "rtp_hybrid_attn_decode_paged")
+    if want_lse or want_sel:
+        return out, lse, so
+    return out
+
+
+def cluster_keys_paged(pc: PagedCache, cache_len, is_retrieval, p_k,
+                       centroids, iters: int = 1, n_recent: int = 2,
+                       r: int = 16, block: int = 64, ws=None, tables=None):
+    lib = load()
+    Hq = len(is_retrieval)
+    _dev(cache_len, torch.int32, "cache_len", (pc.B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    _proj(p_k, n_ret, r, pc.d, "p_k")
+    _dev(centroids, torch.float32, "centroids",
+         (pc.B, n_ret, pc.max_blocks, r))
+    dev = pc.k.device
+    if tables is None:
+        tables = (torch.zeros(pc.B, dtype=torch.int32, device=dev),
+                  torch.zeros((pc.B, n_ret, pc.max_blocks + 1),
+                              dtype=torch.int32, device=dev),
+                  torch.zeros((pc.B, n_ret, pc.Lmax), dtype=torch.int32,
+                              device=dev))
+    cl_m, cl_off, cl_mem = tables
+    nb = lib.rtp_cluster_workspace_bytes(pc.B, pc.Lmax, Hq, pc.Hkv, pc.d, mp,
+                                         r, block)
+    w = _workspace(nb, dev, ws)
+    _check(lib.rtp_cluster_keys_paged(
+        _ptr(pc.k), _ptr(pc.table), pc.max_blocks, pc.n_pages,
+        _ptr(cache_len), pc.B, Hq, pc.Hkv, pc.d, mp, _ptr(p_k), r, block,
+        n_recent, int(iters), _ptr(centroids), _ptr(cl_m), _ptr(cl_off),
+        _ptr(cl_mem), _ptr(w), w.numel(), _stream(dev)),
+        "rtp_cluster_keys_paged")
+    return tables
+
+
+def hybrid_attn_decode_clustered_paged(q, pc: PagedCache, cache_len,
+                                       is_retrieval, window: int, p_q,
+                                       centroids, tables, top_k: int,
+                                       n_recent: int = 2, r: int = 16,
+                                       block: int = 64, scale: float = 0.0,
+                                       want_lse: bool = False,
+                                       want_sel: bool = False, ws=None,
+                                       out=None):
+    lib = load()
+    B, Hq, d = q.shape
+    _dev(q, torch.bfloat16, "q", (pc.B, Hq, pc.d))
+    _dev(cache_len, torch.int32, "cache_len", (pc.B,))
+    m, mp = _mask(is_retrieval, Hq)
+    n_ret = int(m.astype(bool).sum())
+    cl_m, cl_off, cl_mem = tables
+    if n_ret:
+        _proj(p_q, n_ret, r, d, "p_q")
+        _dev(centroids, torch.float32, "centroids",
+             (B, n_ret, pc.max_blocks, r))
+    out, lse, so = _decode_outputs(q, n_ret, top_k, n_recent, want_lse,
+                                   want_sel, out)
+    nb = lib.rtp_decode_clustered_workspace_bytes(B, pc.Lmax, Hq, pc.Hkv, d,
+                                                  mp, r, block, top_k,
+                                                  n_recent)
+    w = _workspace(nb, q.device, ws)
+    _check(lib.rtp_hybrid_attn_decode_clustered_paged(
+        _ptr(q), _ptr(pc.k), _ptr(pc.v), _ptr(pc.table), pc.max_blocks,
+        pc.n_pages, _ptr(cache_len), B, Hq, pc.Hkv, d, mp, int(window),
+        _ptr(p_q), _ptr(centroids), _ptr(cl_m), _ptr(cl_off), _ptr(cl_mem),
+        r, block, top_k, n_recent, float(scale), _ptr(out), _ptr(lse),
+        _ptr(so), _ptr(w), w.numel(), _stream(q.device)),
+        "rtp_hybrid_attn_decode_clustered_paged")
     if want_lse or want_sel:
         return out, lse, so
     return out

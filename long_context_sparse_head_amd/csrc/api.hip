@@ -520,11 +520,25 @@ int rtp_dense_attn_prefill(const void* q, const void* k, const void* v,
   return RTP_OK;
 }
 
-int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
-                        int Lmax, int Hq, int Hkv, int d,
-                        const uint8_t* is_retrieval, const float* p_k, int r,
-                        int block, float* centroids, rtp_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+// Paged-cache arguments: a block table [B, max_blocks] of page ids into a
+// pool of n_pages pages (64 tokens of every KV head each).
+int check_pages(const int32_t* table, int max_blocks, int n_pages) {
+  if (!table) return fail(RTP_EINVAL, "block_table is NULL");
+  if (max_blocks < 1 || n_pages < 1)
+    return fail(RTP_EINVAL, "max_blocks and n_pages must be >= 1");
+  if ((int64_t)max_blocks * 64 > INT32_MAX)
+    return fail(RTP_EUNSUPPORTED, "max_blocks * 64 must fit an int");
+  return RTP_OK;
+}
+
+int build_centroids_impl(const void* k_cache, const int32_t* cache_len, int B,
+                         int Lmax, int Hq, int Hkv, int d,
+                         const uint8_t* is_retrieval, const float* p_k, int r,
+                         int block, float* centroids, rtp_stream_t stream,
+                         rtp::KvView kv) {
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
@@ -536,17 +550,16 @@ int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
   hipError_t e = rtp::launch_build_centroids(
       static_cast<const rtp::u16*>(k_cache), cache_len, p_k, centroids, B, Lmax,
       Hkv, hi.n_ret, r, Hq / Hkv, hi.ret_heads.data(),
-      reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<hipStream_t>(stream), kv);
   if (e != hipSuccess) return hip_fail(e, "centroid launch");
   return RTP_OK;
 }
 
-int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
-                      const void* k_new, const void* v_new, int B, int Lmax,
-                      int Hq, int Hkv, int d, const uint8_t* is_retrieval,
-                      const float* p_k, int r, int block, float* centroids,
-                      rtp_stream_t stream) {
-  g_err.clear();
+int decode_append_impl(void* k_cache, void* v_cache, int32_t* cache_len,
+                       const void* k_new, const void* v_new, int B, int Lmax,
+                       int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                       const float* p_k, int r, int block, float* centroids,
+                       rtp_stream_t stream, rtp::KvView kv) {
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
@@ -562,9 +575,70 @@ int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
       cache_len, static_cast<const rtp::u16*>(k_new),
       static_cast<const rtp::u16*>(v_new), p_k, centroids, B, Lmax, Hkv,
       hi.n_ret, r, Hq / Hkv, hi.ret_heads.data(),
-      reinterpret_cast<hipStream_t>(stream));
+      reinterpret_cast<hipStream_t>(stream), kv);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return RTP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int rtp_build_centroids(const void* k_cache, const int32_t* cache_len, int B,
+                        int Lmax, int Hq, int Hkv, int d,
+                        const uint8_t* is_retrieval, const float* p_k, int r,
+                        int block, float* centroids, rtp_stream_t stream) {
+  g_err.clear();
+  return build_centroids_impl(k_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                              is_retrieval, p_k, r, block, centroids, stream,
+                              rtp::KvView());
+}
+
+int rtp_build_centroids_paged(const void* k_pages, const int32_t* block_table,
+                              int max_blocks, int n_pages,
+                              const int32_t* cache_len, int B, int Hq, int Hkv,
+                              int d, const uint8_t* is_retrieval,
+                              const float* p_k, int r, int block,
+                              float* centroids, rtp_stream_t stream) {
+  g_err.clear();
+  if (B > 0)
+    if (int e = check_pages(block_table, max_blocks, n_pages)) return e;
+  rtp::KvView kv;
+  kv.table = block_table;
+  kv.max_blocks = max_blocks;
+  kv.n_pages = n_pages;
+  return build_centroids_impl(k_pages, cache_len, B, 64 * max_blocks, Hq, Hkv,
+                              d, is_retrieval, p_k, r, block, centroids,
+                              stream, kv);
+}
+
+int rtp_decode_append(void* k_cache, void* v_cache, int32_t* cache_len,
+                      const void* k_new, const void* v_new, int B, int Lmax,
+                      int Hq, int Hkv, int d, const uint8_t* is_retrieval,
+                      const float* p_k, int r, int block, float* centroids,
+                      rtp_stream_t stream) {
+  g_err.clear();
+  return decode_append_impl(k_cache, v_cache, cache_len, k_new, v_new, B, Lmax,
+                            Hq, Hkv, d, is_retrieval, p_k, r, block, centroids,
+                            stream, rtp::KvView());
+}
+
+int rtp_decode_append_paged(void* k_pages, void* v_pages,
+                            const int32_t* block_table, int max_blocks,
+                            int n_pages, int32_t* cache_len, const void* k_new,
+                            const void* v_new, int B, int Hq, int Hkv, int d,
+                            const uint8_t* is_retrieval, const float* p_k,
+                            int r, int block, float* centroids,
+                            rtp_stream_t stream) {
+  g_err.clear();
+  if (B > 0)
+    if (int e = check_pages(block_table, max_blocks, n_pages)) return e;
+  rtp::KvView kv;
+  kv.table = block_table;
+  kv.max_blocks = max_blocks;
+  kv.n_pages = n_pages;
+  return decode_append_impl(k_pages, v_pages, cache_len, k_new, v_new, B,
+                            64 * max_blocks, Hq, Hkv, d, is_retrieval, p_k, r,
+                            block, centroids, stream, kv);
 }
 
 static const int kDecSplit = 8;
@@ -626,13 +700,16 @@ size_t rtp_cluster_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
   return rtp::cluster_sizes(B, Lmax, hi.n_ret, r).total;
 }
 
-int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
-                     int Lmax, int Hq, int Hkv, int d,
-                     const uint8_t* is_retrieval, const float* p_k, int r,
-                     int block, int n_recent, int iters, float* centroids,
-                     int32_t* cl_m, int32_t* cl_off, int32_t* cl_members,
-                     void* ws, size_t ws_bytes, rtp_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+int cluster_keys_impl(const void* k_cache, const int32_t* cache_len, int B,
+                      int Lmax, int Hq, int Hkv, int d,
+                      const uint8_t* is_retrieval, const float* p_k, int r,
+                      int block, int n_recent, int iters, float* centroids,
+                      int32_t* cl_m, int32_t* cl_off, int32_t* cl_members,
+                      void* ws, size_t ws_bytes, rtp_stream_t stream,
+                      rtp::KvView kv) {
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 0) return fail(RTP_EINVAL, "B and Lmax must be >= 0");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
@@ -651,6 +728,7 @@ int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
     if (int e = check_ws(ws, ws_bytes, z.total)) return e;
   rtp::ClusterLaunch a;
   a.kc = static_cast<const rtp::u16*>(k_cache);
+  a.kv = kv;
   a.cache_len = cache_len;
   a.p_k = p_k;
   a.cent = centroids;
@@ -671,6 +749,43 @@ int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
   if (e != hipSuccess) return hip_fail(e, "cluster launch");
   return RTP_OK;
 }
+}  // namespace
+
+extern "C" {
+
+int rtp_cluster_keys(const void* k_cache, const int32_t* cache_len, int B,
+                     int Lmax, int Hq, int Hkv, int d,
+                     const uint8_t* is_retrieval, const float* p_k, int r,
+                     int block, int n_recent, int iters, float* centroids,
+                     int32_t* cl_m, int32_t* cl_off, int32_t* cl_members,
+                     void* ws, size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  return cluster_keys_impl(k_cache, cache_len, B, Lmax, Hq, Hkv, d,
+                           is_retrieval, p_k, r, block, n_recent, iters,
+                           centroids, cl_m, cl_off, cl_members, ws, ws_bytes,
+                           stream, rtp::KvView());
+}
+
+int rtp_cluster_keys_paged(const void* k_pages, const int32_t* block_table,
+                           int max_blocks, int n_pages,
+                           const int32_t* cache_len, int B, int Hq, int Hkv,
+                           int d, const uint8_t* is_retrieval,
+                           const float* p_k, int r, int block, int n_recent,
+                           int iters, float* centroids, int32_t* cl_m,
+                           int32_t* cl_off, int32_t* cl_members, void* ws,
+                           size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  if (B > 0)
+    if (int e = check_pages(block_table, max_blocks, n_pages)) return e;
+  rtp::KvView kv;
+  kv.table = block_table;
+  kv.max_blocks = max_blocks;
+  kv.n_pages = n_pages;
+  return cluster_keys_impl(k_pages, cache_len, B, 64 * max_blocks, Hq, Hkv, d,
+                           is_retrieval, p_k, r, block, n_recent, iters,
+                           centroids, cl_m, cl_off, cl_members, ws, ws_bytes,
+                           stream, kv);
+}
 
 }  // extern "C"
 
@@ -687,7 +802,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                 int32_t* sel_out, void* ws, size_t ws_bytes, bool one_stream,
                 size_t* need, rtp_stream_t stream,
                 const int32_t* cl_m = nullptr, const int32_t* cl_off = nullptr,
-                const int32_t* cl_mem = nullptr, bool clustered = false) {
+                const int32_t* cl_mem = nullptr, bool clustered = false,
+                rtp::KvView kv = rtp::KvView()) {
   *need = 0;
   if (int e = check_shape(0, Hq, Hkv, d)) return e;
   if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
@@ -738,6 +854,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.part_o = reinterpret_cast<float*>(w + L.po);
   a.part_ml = reinterpret_cast<float*>(w + L.pml);
   a.one_stream = one_stream;
+  a.kv = kv;
   if (clustered && hi.n_ret > 0) {
     a.cl_m = cl_m;
     a.cl_off = cl_off;
@@ -861,6 +978,74 @@ int rtp_hybrid_attn_decode_clustered(
                      is_retrieval, window, p_q, centroids, r, block, top_k,
                      n_recent, scale, out, lse, sel_out, ws, ws_bytes, false,
                      &need, stream, cl_m, cl_off, cl_members, true);
+}
+
+// Paged twins: the cache is a pool of pages and a block table; Lmax is
+// 64 * max_blocks. cl_m == nullptr: the block decode.
+static int decode_paged(const void* q, const void* k_pages,
+                        const void* v_pages, const int32_t* block_table,
+                        int max_blocks, int n_pages, const int32_t* cache_len,
+                        int B, int Hq, int Hkv, int d,
+                        const uint8_t* is_retrieval, int window,
+                        const float* p_q, const float* centroids,
+                        const int32_t* cl_m, const int32_t* cl_off,
+                        const int32_t* cl_members, bool clustered, int r,
+                        int block, int top_k, int n_recent, float scale,
+                        void* out, float* lse, int32_t* sel_out, void* ws,
+                        size_t ws_bytes, rtp_stream_t stream) {
+  if (B > 0)
+    if (int e = check_pages(block_table, max_blocks, n_pages)) return e;
+  rtp::KvView kv;
+  kv.table = block_table;
+  kv.max_blocks = max_blocks;
+  kv.n_pages = n_pages;
+  const int Lmax = 64 * max_blocks;
+  size_t need = 0;
+  if (!ws) {
+    int e = decode_impl(q, k_pages, v_pages, cache_len, B, Lmax, Hq, Hkv, d,
+                        is_retrieval, window, p_q, centroids, r, block, top_k,
+                        n_recent, scale, out, lse, sel_out, nullptr, 0, false,
+                        &need, stream, cl_m, cl_off, cl_members, clustered, kv);
+    if (e) return e;
+    return check_ws(ws, ws_bytes, need);
+  }
+  return decode_impl(q, k_pages, v_pages, cache_len, B, Lmax, Hq, Hkv, d,
+                     is_retrieval, window, p_q, centroids, r, block, top_k,
+                     n_recent, scale, out, lse, sel_out, ws, ws_bytes, false,
+                     &need, stream, cl_m, cl_off, cl_members, clustered, kv);
+}
+
+int rtp_hybrid_attn_decode_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, int max_blocks, int n_pages,
+    const int32_t* cache_len, int B, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  return decode_paged(q, k_pages, v_pages, block_table, max_blocks, n_pages,
+                      cache_len, B, Hq, Hkv, d, is_retrieval, window, p_q,
+                      centroids, nullptr, nullptr, nullptr, false, r, block,
+                      top_k, n_recent, scale, out, lse, sel_out, ws, ws_bytes,
+                      stream);
+}
+
+int rtp_hybrid_attn_decode_clustered_paged(
+    const void* q, const void* k_pages, const void* v_pages,
+    const int32_t* block_table, int max_blocks, int n_pages,
+    const int32_t* cache_len, int B, int Hq, int Hkv, int d,
+    const uint8_t* is_retrieval, int window, const float* p_q,
+    const float* centroids, const int32_t* cl_m, const int32_t* cl_off,
+    const int32_t* cl_members, int r, int block, int top_k, int n_recent,
+    float scale, void* out, float* lse, int32_t* sel_out, void* ws,
+    size_t ws_bytes, rtp_stream_t stream) {
+  g_err.clear();
+  return decode_paged(q, k_pages, v_pages, block_table, max_blocks, n_pages,
+                      cache_len, B, Hq, Hkv, d, is_retrieval, window, p_q,
+                      centroids, cl_m, cl_off, cl_members, true, r, block,
+                      top_k, n_recent, scale, out, lse, sel_out, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"

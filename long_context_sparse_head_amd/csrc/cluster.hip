@@ -38,6 +38,7 @@ namespace rtp {
 
 struct ClArgs {
   const u16* kc; const int32_t* cache_len; const float* p_k;
+  KvView kv;
   float* x;         // [B, n_ret, Lmax, r] projected keys (rows of clustered tokens)
   int32_t* assign;  // [B, n_ret, Lmax] cluster id of each clustered token
   int32_t* hist;    // [B, n_ret, kClChunks, nbmax] counts, then first slots
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void cl_project_kernel(const ClArgs a) {
   const int m = cl_count(a, b);
   if (kb < 1 || kb >= m) return;
   const uint32_t* krow = reinterpret_cast<const uint32_t*>(
-      a.kc + (((size_t)b * a.Hkv + a.kvh_of_rho[rho]) * a.Lmax + (size_t)kb * 64) * kD);
+      a.kc + kv_row(a.kv, b, a.Hkv, a.kvh_of_rho[rho], a.Lmax, kb * 64));
   for (int i = tid; i < 64 * kD / 2; i += 256) {
     const uint32_t w = krow[i];
     const int row = (2 * i) / kD, col = (2 * i) % kD;
@@ -452,6 +453,7 @@ hipError_t launch_cluster(const ClusterLaunch& L, hipStream_t st) {
   if (L.B == 0 || L.n_ret == 0 || L.Lmax < 64) return hipSuccess;
   ClArgs a;
   a.kc = L.kc;
+  a.kv = L.kv;
   a.cache_len = L.cache_len;
   a.p_k = L.p_k;
   a.cent = L.cent;

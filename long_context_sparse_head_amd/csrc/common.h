@@ -196,6 +196,24 @@ struct IndexerLaunch {
 };
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st);
 
+// Decode K/V cache view. Contiguous (table == nullptr): [B, Hkv, Lmax, d].
+// Paged: pages of 64 tokens [n_pages, Hkv, 64, d] and a block table
+// [B, max_blocks] whose entry (b, j) is the page holding tokens 64 j ..
+// 64 j + 63 of sequence b (Lmax = 64 max_blocks). Page ids outside
+// [0, n_pages) are clamped, so a bad table stays inside the pool.
+struct KvView {
+  const int32_t* table = nullptr;
+  int max_blocks = 0, n_pages = 0;
+};
+// element offset of token j of (sequence b, KV head g)
+__device__ __forceinline__ size_t kv_row(const KvView& v, int b, int Hkv,
+                                         int g, int Lmax, int j) {
+  if (!v.table) return (((size_t)b * Hkv + g) * Lmax + j) * kD;
+  int page = v.table[(size_t)b * v.max_blocks + (j >> 6)];
+  page = min(max(page, 0), v.n_pages - 1);
+  return (((size_t)page * Hkv + g) * 64 + (j & 63)) * kD;
+}
+
 struct DecodeLaunch {
   const u16* q; const u16* kc; const u16* vc; const int32_t* cache_len;
   const float* p_q; const float* cent;
@@ -213,6 +231,7 @@ struct DecodeLaunch {
   const int32_t* cl_m = nullptr; const int32_t* cl_off = nullptr;
   const int32_t* cl_mem = nullptr;
   int32_t* tok = nullptr; int32_t* tok_cnt = nullptr;
+  KvView kv;  // paged cache when kv.table is set
 };
 
 // K-cache clustering: the clustered tokens of one (sequence, retrieval
@@ -233,6 +252,7 @@ inline ClusterSizes cluster_sizes(int B, int Lmax, int n_ret, int r) {
 }
 struct ClusterLaunch {
   const u16* kc; const int32_t* cache_len; const float* p_k;
+  KvView kv;  // paged cache when kv.table is set
   float* cent; int32_t* cl_m; int32_t* cl_off; int32_t* cl_mem;
   int B, Lmax, Hkv, n_ret, r, n_recent, iters, G;
   const uint8_t* ret_heads;  // host
@@ -244,13 +264,15 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st);
 hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
                                   const float* p_k, float* cent, int B,
                                   int Lmax, int Hkv, int n_ret, int r, int G,
-                                  const uint8_t* ret_heads, hipStream_t st);
+                                  const uint8_t* ret_heads, hipStream_t st,
+                                  KvView kv = KvView());
 
 hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
                                 const u16* k_new, const u16* v_new,
                                 const float* p_k, float* cent, int B,
                                 int Lmax, int Hkv, int n_ret, int r, int G,
-                                const uint8_t* ret_heads, hipStream_t st);
+                                const uint8_t* ret_heads, hipStream_t st,
+                                KvView kv = KvView());
 
 
 }  // namespace rtp

@@ -28,6 +28,7 @@ constexpr int kDecMaxUnitHeads = 32;
 // ---------------------------------------------------------------- centroids
 struct CentArgs {
   int Hkv, Lmax, n_ret, r, nbmax;
+  KvView kv;
   uint8_t kvh_of_rho[kMaxHeads];
 };
 
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(64) void build_centroids_kernel(
   L = L < 0 ? 0 : (L > ca.Lmax ? ca.Lmax : L);
   if ((kb + 1) * 64 > L) return;
   const int g = ca.kvh_of_rho[rho];
-  block_centroid(kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD,
+  block_centroid(kc + kv_row(ca.kv, b, ca.Hkv, g, ca.Lmax, kb * 64),
                  p_k + (size_t)rho * ca.r * kD, ca.r, mean,
                  cent + (((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r,
                  lane);
@@ -80,12 +81,12 @@ __global__ __launch_bounds__(64) void build_centroids_kernel(
 __global__ __launch_bounds__(64) void append_kv_kernel(
     u16* __restrict__ kc, u16* __restrict__ vc,
     const int32_t* __restrict__ cache_len, const u16* __restrict__ k_new,
-    const u16* __restrict__ v_new, int Hkv, int Lmax) {
+    const u16* __restrict__ v_new, int Hkv, int Lmax, const KvView kv) {
   const int b = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
   const int L = cache_len[b];
   if (L < 0 || L >= Lmax) return;
   const size_t src = ((size_t)b * Hkv + g) * kD;
-  const size_t dst = (((size_t)b * Hkv + g) * Lmax + L) * kD;
+  const size_t dst = kv_row(kv, b, Hkv, g, Lmax, L);
   reinterpret_cast<uint32_t*>(kc + dst)[lane] =
       reinterpret_cast<const uint32_t*>(k_new + src)[lane];
   reinterpret_cast<uint32_t*>(vc + dst)[lane] =
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(64) void append_centroids_kernel(
     for (int rho = 0; rho < ca.n_ret; ++rho) {
       const int g = ca.kvh_of_rho[rho];
       block_centroid(
-          kc + (((size_t)b * ca.Hkv + g) * ca.Lmax + (size_t)kb * 64) * kD,
+          kc + kv_row(ca.kv, b, ca.Hkv, g, ca.Lmax, kb * 64),
           p_k + (size_t)rho * ca.r * kD, ca.r, mean,
           cent + (((size_t)b * ca.n_ret + rho) * ca.nbmax + kb) * ca.r, lane);
     }
@@ -118,9 +119,11 @@ hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
                                 const u16* k_new, const u16* v_new,
                                 const float* p_k, float* cent, int B,
                                 int Lmax, int Hkv, int n_ret, int r, int G,
-                                const uint8_t* ret_heads, hipStream_t st) {
+                                const uint8_t* ret_heads, hipStream_t st,
+                                KvView kv) {
   if (B == 0) return hipSuccess;
   CentArgs ca;
+  ca.kv = kv;
   ca.Hkv = Hkv;
   ca.Lmax = Lmax;
   ca.n_ret = n_ret;
@@ -130,7 +133,7 @@ hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
     ca.kvh_of_rho[i] = i < n_ret ? ret_heads[i] / G : 0;
   prof_begin("append_kv", st);
   hipLaunchKernelGGL(append_kv_kernel, dim3(B, Hkv), dim3(64), 0, st, kc, vc,
-                     cache_len, k_new, v_new, Hkv, Lmax);
+                     cache_len, k_new, v_new, Hkv, Lmax, kv);
   prof_end(st);
   prof_begin("append_centroids", st);
   hipLaunchKernelGGL(append_centroids_kernel, dim3(B), dim3(64), 0, st, kc,
@@ -142,10 +145,12 @@ hipError_t launch_decode_append(u16* kc, u16* vc, int32_t* cache_len,
 hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
                                   const float* p_k, float* cent, int B,
                                   int Lmax, int Hkv, int n_ret, int r, int G,
-                                  const uint8_t* ret_heads, hipStream_t st) {
+                                  const uint8_t* ret_heads, hipStream_t st,
+                                  KvView kv) {
   const int nbmax = Lmax / 64;
   if (B == 0 || n_ret == 0 || nbmax == 0) return hipSuccess;
   CentArgs ca;
+  ca.kv = kv;
   ca.Hkv = Hkv;
   ca.Lmax = Lmax;
   ca.n_ret = n_ret;
@@ -386,6 +391,7 @@ struct DecAttnArgs {
   // clustered decode: per (sequence, retrieval head) a list of tok_width
   // token ids, tok_cnt of them used (read by the token-list instance)
   const int32_t* tok; const int32_t* tok_cnt; int tok_width;
+  KvView kv;  // paged cache (read by the kPaged instances)
   uint32_t desc[2 * kMaxHeads];
   uint8_t rho[2 * kMaxHeads];
   uint8_t hlist[kMaxHeads];
@@ -419,7 +425,10 @@ constexpr int kDecTile = 32 * kD * 2;
 // every tile, split and wave sees exactly the keys of the block walk. Row r
 // of a tile is gathered from token id (entry r), the ids of the next tile
 // having been loaded one iteration ahead.
-template <bool kTok>
+//
+// kPaged: the cache is paged (KvView); a row's address goes through the
+// block table, and a tile that straddles two pages takes the per-row loads.
+template <bool kTok, bool kPaged>
 __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char kvbuf[4][2][kDecTile];
   __shared__ float red_ml[4][kDecMaxUnitHeads][2];
@@ -468,9 +477,15 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     nt = min(per, ntile - T0);
   }
 
-  const size_t kv_off = ((size_t)b * a.Hkv + kvh) * a.Lmax * kD;
+  // rows: contiguous, kbase + key * kD; paged, the pool base plus the
+  // offset of the key's page row
+  const size_t kv_off = kPaged ? 0 : ((size_t)b * a.Hkv + kvh) * a.Lmax * kD;
   const u16* kbase = a.kc + kv_off;
   const u16* vbase = a.vc + kv_off;
+  auto roff = [&](int key) -> size_t {
+    if constexpr (kPaged) return kv_row(a.kv, b, a.Hkv, kvh, a.Lmax, key);
+    else return (size_t)key * kD;
+  };
 
   // B operand of S^T: Q^T, column n = head n of the unit (zero beyond nh)
   bf16x8 qf[8];
@@ -520,8 +535,9 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
     voff[j] = (uint32_t)((lane >> 4) * 256 + (((lane & 15) ^ (4 * j)) << 4));
   auto load_rows = [&](const u16* src, int base, int nvalid, bool kswz,
                        u32x4 (&st)[8]) {
-    if (nvalid == 32) {  // wave-uniform
-      const char* t = reinterpret_cast<const char*>(src + (size_t)base * kD);
+    // wave-uniform: a full tile inside one page (always, unpaged)
+    if (nvalid == 32 && (!kPaged || (base & 63) <= 32)) {
+      const char* t = reinterpret_cast<const char*>(src + roff(base));
 #pragma unroll
       for (int ins = 0; ins < 8; ++ins) {
         const uint32_t off = kswz ? koff[ins & 3] + (ins >> 2) * 4096
@@ -534,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
       for (int ins = 0; ins < 8; ++ins) {
         const int r = 4 * ins + (lane >> 4);
         const int chunk = (lane & 15) ^ (kswz ? (r & 15) : 4 * ((r >> 3) & 1));
-        const u16* p = src + (size_t)(r < nvalid ? base + r : base) * kD + chunk * 8;
+        const u16* p = src + roff(r < nvalid ? base + r : base) + chunk * 8;
         st[ins] = *reinterpret_cast<const u32x4*>(p);
       }
     }
@@ -552,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void dec_attn_kernel(const DecAttnArgs a) {
       const int r = 4 * ins + (lane >> 4);
       const int id = __shfl(idv, r);
       const int chunk = (lane & 15) ^ (kswz ? (r & 15) : 4 * ((r >> 3) & 1));
-      st[ins] = *reinterpret_cast<const u32x4*>(src + (size_t)id * kD + chunk * 8);
+      st[ins] = *reinterpret_cast<const u32x4*>(src + roff(id) + chunk * 8);
     }
   };
   char* const ktile = kvbuf[wave][0];
@@ -776,6 +792,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   da.tok = a.tok;
   da.tok_cnt = a.tok_cnt;
   da.tok_width = a.Lmax;
+  da.kv = a.kv;
+  const bool paged = a.kv.table != nullptr;
   // units: window heads of each KV group (up to kDecMaxUnitHeads per unit)
   // first, then one unit per retrieval head
   int nu = 0, nl = 0, rho = 0;
@@ -837,12 +855,16 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
     DecAttnArgs d = da;
     d.unit_base = base;
     prof_begin(name, on);
-    if (clustered && base >= n_win_units)  // retrieval units: token lists
-      hipLaunchKernelGGL(dec_attn_kernel<true>, dim3(a.n_split, n, a.B), dim3(256), 0,
-                         on, d);
+    const dim3 grid(a.n_split, n, a.B);
+    const bool tok = clustered && base >= n_win_units;  // retrieval units
+    if (tok && paged)
+      hipLaunchKernelGGL((dec_attn_kernel<true, true>), grid, dim3(256), 0, on, d);
+    else if (tok)
+      hipLaunchKernelGGL((dec_attn_kernel<true, false>), grid, dim3(256), 0, on, d);
+    else if (paged)
+      hipLaunchKernelGGL((dec_attn_kernel<false, true>), grid, dim3(256), 0, on, d);
     else
-      hipLaunchKernelGGL(dec_attn_kernel<false>, dim3(a.n_split, n, a.B), dim3(256), 0,
-                         on, d);
+      hipLaunchKernelGGL((dec_attn_kernel<false, false>), grid, dim3(256), 0, on, d);
     prof_end(on);
   };
   hipError_t e = hipSuccess;

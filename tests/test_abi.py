@@ -261,3 +261,24 @@ def test_cluster_workspace_and_validation():
         P(1), P(1), P(1), P(1), 2, 4096, 4, 2, 128, mp, 64, P(1), P(1), P(1),
         P(1), P(1), 16, 64, 8, 2, 0.0, P(1), None, None, None, 0, None)
     assert st == -3
+
+
+def test_paged_validation():
+    lib = rtp.load()
+    m, mp = _mask([0, 1, 1, 0])
+    P = ctypes.c_void_p
+    # NULL block table, zero max_blocks, zero pages
+    for table, mb, npg in ((None, 4, 8), (P(1), 0, 8), (P(1), 4, 0)):
+        st = lib.rtp_hybrid_attn_decode_paged(
+            P(1), P(1), P(1), table, mb, npg, P(1), 2, 4, 2, 128, mp, 64,
+            P(1), P(1), 16, 64, 8, 2, 0.0, P(1), None, None, P(256), 1 << 40,
+            None)
+        assert st == -1
+        assert lib.rtp_build_centroids_paged(
+            P(1), table, mb, npg, P(1), 2, 4, 2, 128, mp, P(1), 16, 64, P(1),
+            None) == -1
+    # a valid table with no workspace: sized like the unpaged decode
+    st = lib.rtp_hybrid_attn_decode_paged(
+        P(1), P(1), P(1), P(1), 4, 8, P(1), 2, 4, 2, 128, mp, 64, P(1), P(1),
+        16, 64, 8, 2, 0.0, P(1), None, None, None, 0, None)
+    assert st == -3
