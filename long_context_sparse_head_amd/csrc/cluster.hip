@@ -8,6 +8,7 @@
 // cache is clustered in prefill and decode runs sparsely). The pages give no
 // algorithm; this library's reading:
 //   points   x_t = P_k k_t, t in blocks 1 .. m-1, m = max(n_b - n_recent, 1)
+//            (fp32, projected on the matrix cores as in the indexer)
 //   clusters ids 1 .. m-1, id c starting from the centroid table's entry c
 //            (the block centroid after rtp_build_centroids)
 //   one step assign every point to the nearest centroid (Euclidean; ties:
@@ -32,6 +33,7 @@
 // Everything is deterministic: no atomic takes part in a floating-point sum
 // or decides an order.
 #include "common.h"
+#include "proj.h"
 #include "select.h"
 
 namespace rtp {
@@ -63,49 +65,48 @@ __device__ __forceinline__ int cl_chunk_len(int m) {
 }
 
 // ------------------------------------------------------------ projection
-// grid (nbmax, n_ret, B), 256 threads: x_t = P_k k_t in fp32 for the 64
-// tokens of block kb (1 <= kb < m). Thread (token j = tid / 4, part p)
-// computes dims 4 R16 p .. 4 R16 p + 4 R16 - 1 of token j.
-template <int R16>
+// grid (ceil(nbmax / 4), n_ret, B), 4 waves, a wave per 64-token block kb
+// (1 <= kb < m): x_t = P_k k_t in fp32, as in the indexer's projection: the
+// head's rows of P_k staged 32 at a time in LDS as three bf16 parts and
+// multiplied with the block's keys on the matrix cores (proj.h).
 __global__ __launch_bounds__(256) void cl_project_kernel(const ClArgs a) {
-  constexpr int R = 16 * R16, PER = 4 * R16;
-  __shared__ __attribute__((aligned(16))) float ks[64][kD + 4];
-  __shared__ __attribute__((aligned(16))) float ps[R][kD + 4];
-  const int kb = blockIdx.x, rho = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) char ptile[kProjTileB];
+  const int rho = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kb = 4 * blockIdx.x + wave;
   const int m = cl_count(a, b);
-  if (kb < 1 || kb >= m) return;
-  const uint32_t* krow = reinterpret_cast<const uint32_t*>(
-      a.kc + kv_row(a.kv, b, a.Hkv, a.kvh_of_rho[rho], a.Lmax, kb * 64));
-  for (int i = tid; i < 64 * kD / 2; i += 256) {
-    const uint32_t w = krow[i];
-    const int row = (2 * i) / kD, col = (2 * i) % kD;
-    ks[row][col] = __uint_as_float(w << 16);
-    ks[row][col + 1] = __uint_as_float(w & 0xffff0000u);
-  }
-  const float* prow = a.p_k + (size_t)rho * R * kD;
-  for (int i = tid; i < R * kD; i += 256) ps[i / kD][i % kD] = prow[i];
-  __syncthreads();
-  const int j = tid >> 2, p = tid & 3;
-  float acc[PER];
+  if (4 * blockIdx.x >= m) return;  // whole workgroup
+  const bool ok = kb >= 1 && kb < m;
+  bf16x8 kbop[2][8];
+  proj_keys_operands(a.kc + kv_row(a.kv, b, a.Hkv, a.kvh_of_rho[rho], a.Lmax,
+                                   ok ? kb * 64 : 0),
+                     ok ? 64 : 0, kbop);
+  const float* P = a.p_k + (size_t)rho * a.r * kD;
+  const int gq = lane >> 5, n = lane & 31;
+  for (int m0 = 0; m0 < a.r; m0 += 32) {
+    __syncthreads();
+    proj_stage(P, m0, a.r, ptile);
+    __syncthreads();
+    if (!ok) continue;
+    f32x16 acc[2];
+    proj_tile(ptile, kbop, acc);
 #pragma unroll
-  for (int o = 0; o < PER; ++o) acc[o] = 0.f;
-  for (int d = 0; d < kD; d += 4) {
-    const float4 kv = *reinterpret_cast<const float4*>(&ks[j][d]);
+    for (int half = 0; half < 2; ++half) {
+      const int R = m0 + 16 * half;
+      if (R >= a.r) break;
 #pragma unroll
-    for (int o = 0; o < PER; ++o) {
-      const float4 pv = *reinterpret_cast<const float4*>(&ps[p * PER + o][d]);
-      acc[o] = fmaf(pv.x, kv.x, acc[o]);
-      acc[o] = fmaf(pv.y, kv.y, acc[o]);
-      acc[o] = fmaf(pv.z, kv.z, acc[o]);
-      acc[o] = fmaf(pv.w, kv.w, acc[o]);
+      for (int mt = 0; mt < 2; ++mt) {
+        float* xo = a.x + (((size_t)b * a.n_ret + rho) * a.Lmax + (size_t)kb * 64 +
+                           32 * mt + n) * a.r + R + 8 * gq;
+        *reinterpret_cast<float4*>(xo) =
+            make_float4(acc[mt][8 * half], acc[mt][8 * half + 1],
+                        acc[mt][8 * half + 2], acc[mt][8 * half + 3]);
+        *reinterpret_cast<float4*>(xo + 4) =
+            make_float4(acc[mt][8 * half + 4], acc[mt][8 * half + 5],
+                        acc[mt][8 * half + 6], acc[mt][8 * half + 7]);
+      }
     }
   }
-  float* xo = a.x + (((size_t)b * a.n_ret + rho) * a.Lmax + (size_t)kb * 64 + j) * R +
-              p * PER;
-#pragma unroll
-  for (int o = 0; o < PER; o += 4)
-    *reinterpret_cast<float4*>(xo + o) = make_float4(acc[o], acc[o + 1], acc[o + 2], acc[o + 3]);
 }
 
 // -------------------------------------------------------------- E-step
@@ -423,8 +424,7 @@ template <int R16>
 static void launch_steps(const ClArgs& a, int B, int iters, hipStream_t st) {
   const int gb = (a.nbmax + 3) / 4;
   prof_begin("cl_project", st);
-  hipLaunchKernelGGL(cl_project_kernel<R16>, dim3(a.nbmax, a.n_ret, B), dim3(256),
-                     0, st, a);
+  hipLaunchKernelGGL(cl_project_kernel, dim3(gb, a.n_ret, B), dim3(256), 0, st, a);
   prof_end(st);
   const size_t nh = (size_t)B * a.n_ret * kClChunks * a.nbmax;
   for (int it = 0; it < iters; ++it) {

@@ -24,6 +24,7 @@
 // candidate buffer (see score_select_kernel). At 1M tokens that replaces
 // 11.5 GiB of score rows by about 0.6 GB of buffers.
 #include "common.h"
+#include "proj.h"
 #include "select.h"
 
 namespace rtp {
@@ -57,104 +58,79 @@ __device__ __forceinline__ void put_score(float* kth, size_t i, bool have,
 __host__ __device__ inline size_t kop_block_elems(int r) { return 2048 * (r / 16); }
 
 // ---- projection of keys: grid (ceil(n_b/4), groups), 4 waves, a wave per
-// key block and a lane per key. The group's K is read once; every retrieval
-// head of the group projects it (fp32 VALU, P staged in LDS 16 rows at a
-// time). Optionally also the per-block centroids (mean of the projected
-// keys over the block's tokens).
+// key block. The group's K is read once. The rows of P_k of the group's
+// retrieval heads (r per head, heads in index order) are taken 32 at a
+// time: each tile is staged in LDS as three bf16 parts and multiplied with
+// the block's keys on the matrix cores (proj.h), which leaves each lane the
+// eight consecutive projected values its slot of the operand layout holds.
+// Optionally also the per-block centroids (mean of the projected keys over
+// the block's tokens).
 __global__ __launch_bounds__(256) void proj_keys_kernel(
     const u16* __restrict__ k, const float* __restrict__ p_k, const ProjArgs pa,
     u16* __restrict__ kop, float* __restrict__ cent) {
-  __shared__ __attribute__((aligned(16))) float P[16 * kD];
+  __shared__ __attribute__((aligned(16))) char ptile[kProjTileB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kb = blockIdx.x * 4 + wave;
   const int j = blockIdx.y;
   const int S = pa.S, r = pa.r, n_b = pa.n_b;
   const int g = pa.grp_kvh[j];
-  const int key = kb * 64 + lane;
   const bool kb_ok = kb < n_b;
-  const bool valid = kb_ok && key < S;
-  uint4 kr[16];
-  {
-    const u16* krow = k + ((size_t)g * S + (valid ? key : 0)) * kD;
+  const int nvalid = kb_ok ? min(64, S - kb * 64) : 0;
+  bf16x8 kbop[2][8];
+  proj_keys_operands(k + ((size_t)g * S + (kb_ok ? (size_t)kb * 64 : 0)) * kD,
+                     nvalid, kbop);
+  const int rho0 = pa.grp_first[j];
+  const int n_rows = (pa.grp_first[j + 1] - rho0) * r;
+  const float* P = p_k + (size_t)rho0 * r * kD;
+  const int R16 = r / 16, gq = lane >> 5, n = lane & 31;
+  for (int m0 = 0; m0 < n_rows; m0 += 32) {
+    __syncthreads();  // the previous tile is no longer read
+    proj_stage(P, m0, n_rows, ptile);
+    __syncthreads();
+    if (!kb_ok) continue;
+    f32x16 acc[2];
+    proj_tile(ptile, kbop, acc);
 #pragma unroll
-    for (int dc = 0; dc < 16; ++dc)
-      kr[dc] = valid ? reinterpret_cast<const uint4*>(krow)[dc]
-                     : make_uint4(0, 0, 0, 0);
-  }
-  const int mt = lane >> 5, L0 = lane & 31;
-  const int R16 = r / 16;
-  for (int rho = pa.grp_first[j]; rho < pa.grp_first[j + 1]; ++rho) {
-    u16* kout = kop ? kop + ((size_t)rho * n_b + (kb_ok ? kb : 0)) * kop_block_elems(r)
-                    : nullptr;
-    for (int rc = 0; rc < r; rc += 16) {
-      __syncthreads();  // the previous rows of P are no longer read
-      const float* src = p_k + ((size_t)rho * r + rc) * kD;
+    for (int half = 0; half < 2; ++half) {
+      const int R = m0 + 16 * half;  // first row of this half (16 | r)
+      if (R >= n_rows) break;
+      const int rho = rho0 + R / r, rs = (R % r) / 16;
+      float cs[8];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        reinterpret_cast<float4*>(P)[threadIdx.x + 256 * i] =
-            reinterpret_cast<const float4*>(src)[threadIdx.x + 256 * i];
-      __syncthreads();
-      if (!kb_ok) continue;
-      float acc[16];
+      for (int e = 0; e < 8; ++e) cs[e] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int mt = 0; mt < 2; ++mt) {
+        float v[8];
 #pragma unroll
-      for (int dc = 0; dc < 16; ++dc) {
-        const uint32_t w[4] = {kr[dc].x, kr[dc].y, kr[dc].z, kr[dc].w};
-        float kf[8];
+        for (int e = 0; e < 8; ++e) v[e] = acc[mt][8 * half + e];
+        if (kop) {
+          uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = __uint_as_float(w[e] << 16);
-          kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+          for (int e = 0; e < 4; ++e) {
+            const u16 h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
+            hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lw[e] = pack_bf16x2(v[2 * e] - bf2f(h0), v[2 * e + 1] - bf2f(h1));
+          }
+          u16* kout = kop + ((size_t)rho * n_b + kb) * kop_block_elems(r);
+          *reinterpret_cast<uint4*>(kout + (size_t)(((mt * 2 + 0) * R16 + rs) * 64 + lane) * 8) =
+              make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint4*>(kout + (size_t)(((mt * 2 + 1) * R16 + rs) * 64 + lane) * 8) =
+              make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
+        if (cent) {  // keys past S project to 0
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float4 p0 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8);
-          const float4 p1 = *reinterpret_cast<const float4*>(P + rr * kD + dc * 8 + 4);
-          float x = acc[rr];
-          x = fmaf(p0.x, kf[0], x); x = fmaf(p0.y, kf[1], x);
-          x = fmaf(p0.z, kf[2], x); x = fmaf(p0.w, kf[3], x);
-          x = fmaf(p1.x, kf[4], x); x = fmaf(p1.y, kf[5], x);
-          x = fmaf(p1.z, kf[6], x); x = fmaf(p1.w, kf[7], x);
-          acc[rr] = x;
-        }
-      }
-      // hi / lo bf16 parts, written in the operand order (not needed when
-      // only the centroids are asked for)
-      if (kop) {
-        uint32_t hw[8], lw[8];
+          for (int e = 0; e < 8; ++e) {
+            float x = v[e];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const u16 h0 = f2bf(acc[2 * i]), h1 = f2bf(acc[2 * i + 1]);
-          const u16 l0 = f2bf(acc[2 * i] - bf2f(h0));
-          const u16 l1 = f2bf(acc[2 * i + 1] - bf2f(h1));
-          hw[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          lw[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        const int rs = rc / 16;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int L = L0 + 32 * half;
-          uint4* dh = reinterpret_cast<uint4*>(
-              kout + (size_t)(((mt * 2 + 0) * R16 + rs) * 64 + L) * 8);
-          uint4* dl = reinterpret_cast<uint4*>(
-              kout + (size_t)(((mt * 2 + 1) * R16 + rs) * 64 + L) * 8);
-          *dh = make_uint4(hw[4 * half], hw[4 * half + 1], hw[4 * half + 2],
-                           hw[4 * half + 3]);
-          *dl = make_uint4(lw[4 * half], lw[4 * half + 1], lw[4 * half + 2],
-                           lw[4 * half + 3]);
+            for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            cs[e] += x;
+          }
         }
       }
-      if (cent) {
-        const int cnt = min(64, S - kb * 64);
+      if (cent && n == 0) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          float v = key < S ? acc[rr] : 0.f;
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-          if (lane == 0)
-            cent[((size_t)rho * n_b + kb) * r + rc + rr] = v / (float)cnt;
-        }
+        for (int e = 0; e < 8; ++e)
+          cent[((size_t)rho * n_b + kb) * r + 16 * rs + 8 * gq + e] = cs[e] / (float)nvalid;
       }
     }
   }
@@ -1043,7 +1019,7 @@ __device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t,
     };
     // one key block: scores of the wave's 64 rows, the operands of block
     // kb + PF loaded into the freed slot, and the append
-    auto step = [&](int kb, bf16x8 (&cur)[NA]) {
+    auto step = [&](int kb, bf16x8 (&cur)[NA]) -> uint32_t {
       float mx[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) mx[nt] = -INFINITY;
@@ -1082,17 +1058,23 @@ __device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t,
       const auto sw = __builtin_amdgcn_permlane32_swap(
           __float_as_uint(mx[0]), __float_as_uint(mx[1]), false, false);
       const float score = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      const uint32_t key = order_key(score);
-      // (cnt < cap always holds here, as buffers are shrunk to at most
-      // cap - 64 entries before they come within PF of full; the test keeps
-      // every store in bounds regardless)
+      return order_key(score);
+    };
+    // (cnt < cap always holds here, as buffers are shrunk to at most
+    // cap - 64 entries before they come within PF of full; the test keeps
+    // every store in bounds regardless)
+    auto append = [&](int kb, uint32_t key) {
       if (row_ok && kb < qb && (!armed || key > thr) && cnt < cap) {
         gmem(rowbuf)[cnt] = entry_t{key, (uint32_t)kb};
         ++cnt;
       }
     };
     // buffers that a group of PF more appends could fill are shrunk
-    // between groups, so the groups themselves run without branches
+    // between groups, so the groups themselves run without branches; the
+    // group's appends come after all of its scores (in key-block order, so
+    // the buffers hold what per-block appends would), which leaves the
+    // group's 12 PF MFMAs and max reductions one scheduling region instead
+    // of one per key block
     auto shrink = [&]() {
       uint64_t full = __ballot(cnt > cap - PF);
       if (full) {
@@ -1135,14 +1117,17 @@ __device__ __forceinline__ void run_tile(const ScoreArgs& a, int rho, int t,
     // blocks they share are still in cache when the last one reads them.
     int kb0 = 1;
     for (int grp = 0; kb0 + PF <= qb_max; kb0 += PF, ++grp) {
+      uint32_t keys[PF];
 #pragma unroll
-      for (int p = 0; p < PF; ++p) step(kb0 + p, ar[p]);
+      for (int p = 0; p < PF; ++p) keys[p] = step(kb0 + p, ar[p]);
+#pragma unroll
+      for (int p = 0; p < PF; ++p) append(kb0 + p, keys[p]);
       shrink();
       if ((grp & 3) == 3 && kb0 + PF <= sync_until) __syncthreads();
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-      if (kb0 + p < qb_max) step(kb0 + p, ar[p]);
+      if (kb0 + p < qb_max) append(kb0 + p, step(kb0 + p, ar[p]));
     shrink();
   }
   fence_wg();
