@@ -165,6 +165,88 @@ hipError_t launch_build_centroids(const u16* kc, const int32_t* cache_len,
   return hipGetLastError();
 }
 
+// --------------------------------------------------- clustered token list
+struct DecTokArgs {
+  const int32_t* cl_m; const int32_t* cl_off; const int32_t* cl_mem;
+  int32_t* tok; int32_t* tok_cnt;  // tok == nullptr: block decode
+};
+struct TokShared {
+  int tmp[4];
+  int sid[256], spos[256];
+  int carry;
+};
+
+// The tokens a retrieval head attends in the clustered decode, in the
+// order of its kept ids (ascending): the members of a kept cluster
+// (1 <= id < m, ascending token order) or every token of a kept block (the
+// sink, blocks that left the recent window after the clustering, the recent
+// blocks). Segment starts come from a block-wide scan of the segment
+// lengths; then each thread fills output positions tid, tid + 256, ...:
+// the segment of a position by binary search over the starts in LDS, and
+// eight members' loads in flight before their stores. Run by the
+// selection's 256 threads once the kept ids are written (ids, n_sel),
+// after a barrier.
+__device__ void build_token_list(const DecTokArgs& a, const int32_t* ids,
+                                 int n_sel, int L, int n_b, int n_recent,
+                                 int Lmax, int nbmax, size_t row, int b,
+                                 TokShared& sh) {
+  const int tid = threadIdx.x;
+  const int m = min(a.cl_m[b], n_b - n_recent);  // recent blocks stay blocks
+  const int32_t* off = a.cl_off + row * (nbmax + 1);
+  const int32_t* mem = a.cl_mem + row * Lmax;
+  int32_t* out = a.tok + row * Lmax;
+  int carry = 0;
+  for (int s0 = 0; s0 < n_sel; s0 += 256) {
+    const int e = s0 + tid;
+    const int id = e < n_sel ? ids[e] : -1;
+    int len = 0, src = 0;  // src: first member slot, or first token
+    if (id >= 0) {
+      if (id >= 1 && id < m) {
+        len = min(max(off[id + 1] - off[id], 0), Lmax);
+        src = min(max(off[id], 0), Lmax - len);
+      } else {
+        len = max(0, min(L, 64 * id + 64) - 64 * id);
+        src = 64 * id;
+      }
+    }
+    const int incl = block_incl_scan(len, sh.tmp);
+    sh.sid[tid] = (id >= 1 && id < m) ? src : -1 - src;  // member slot / ~token
+    sh.spos[tid] = incl - len;
+    if (tid == 255) sh.carry = incl;
+    __syncthreads();
+    const int nseg = min(256, n_sel - s0);
+    const int total = sh.carry;
+    // (the list holds at most Lmax ids and every id is a cached token, also
+    // for tables that do not match this cache)
+    for (int q0 = 0; q0 < total; q0 += 8 * 256) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + 256 * u + tid;
+        v[u] = 0;
+        if (q < total) {
+          int lo = 0, hi = nseg;  // last segment starting at or before q
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (sh.spos[mid] <= q) lo = mid; else hi = mid;
+          }
+          const int sv = sh.sid[lo], i = q - sh.spos[lo];
+          v[u] = sv >= 0 ? mem[sv + i] : (-1 - sv) + i;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pos = carry + q0 + 256 * u + tid;
+        if (q0 + 256 * u + tid < total && pos < Lmax)
+          out[pos] = min(max(v[u], 0), L - 1);
+      }
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) a.tok_cnt[row] = min(carry, Lmax);
+}
+
 // ------------------------------------------------------------- block choice
 struct DecSelArgs {
   int Hq, Lmax, n_ret, r, nbmax, top_k, n_recent, width;
@@ -180,13 +262,15 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     const u16* __restrict__ q, const float* __restrict__ p_q,
     const float* __restrict__ cent, const int32_t* __restrict__ cache_len,
     const DecSelArgs a, float* __restrict__ cscores, int32_t* __restrict__ sel,
-    int32_t* __restrict__ sel_cnt) {
+    int32_t* __restrict__ sel_cnt, const DecTokArgs ta) {
   __shared__ uint32_t keys[TK_LDS + TK_LDS / 32];
   __shared__ float qt[kD];
-  // the two selection workspaces are never used by the same call
+  // the selection workspaces and the token-list scan are never in use at
+  // the same time
   __shared__ union {
     TopkShared block;
     WaveTopkShared wave;
+    TokShared tok;
   } tsh;
   TopkShared& sh = tsh.block;
   WaveTopkShared& wsh = tsh.wave;
@@ -200,6 +284,11 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   if (n_c <= a.top_k) {  // short cache: every block
     for (int t = tid; t < a.width; t += 256) out[t] = t < n_b ? t : -1;
     if (tid == 0) sel_cnt[row_id] = n_b;
+    if (ta.tok) {
+      __syncthreads();  // the kept ids are written (read back by this block)
+      build_token_list(ta, out, n_b, L, n_b, a.n_recent, a.Lmax, a.nbmax,
+                       row_id, b, tsh.tok);
+    }
     return;
   }
   const int h = a.head_of_rho[rho];
@@ -241,9 +330,11 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
   // rows). For r = 16 every load of a group of candidates is issued before
   // the first is used, so the row costs a few memory latencies, not one per
   // float4.
-  auto put = [&](int e, float v) {
-    if (coff && e + 1 < cm && coff[e + 2] == coff[e + 1])
-      v = __uint_as_float(0xffffffffu);
+  auto empty_at = [&](int e) {
+    return coff && e + 1 < cm && coff[e + 2] == coff[e + 1];
+  };
+  auto put = [&](int e, float v, bool empty) {
+    if (empty) v = __uint_as_float(0xffffffffu);
     if (in_lds) keys[e + (e >> 5)] = order_key(v);
     else srow[e] = v;
   };
@@ -251,12 +342,14 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     constexpr int U = 8;
     for (int e0 = tid; e0 < n_c; e0 += U * 256) {
       float4 cv[U][4];
+      bool emp[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = min(e0 + 256 * u, n_c - 1);
         const float4* crow = reinterpret_cast<const float4*>(cb + (size_t)(e + 1) * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) cv[u][i] = crow[i];
+        emp[u] = empty_at(e);  // loaded with the centroids
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -269,7 +362,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
           sc = fmaf(qt[4 * i + 3], cv[u][i].w, sc);
         }
         const int e = e0 + 256 * u;
-        if (e < n_c) put(e, sc);
+        if (e < n_c) put(e, sc, emp[u]);
       }
     }
   } else {
@@ -293,7 +386,7 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int e = e0 + 256 * u;
-        if (e < n_c) put(e, sc[u]);
+        if (e < n_c) put(e, sc[u], empty_at(e));
       }
     }
   }
@@ -311,70 +404,13 @@ __global__ __launch_bounds__(256) void dec_select_kernel(
     sel_cnt[row_id] = 1 + a.top_k + n_rec;
   }
   for (int j = tid; j < n_rec; j += 256) out[1 + a.top_k + j] = n_c + 1 + j;
-}
-
-// --------------------------------------------------- clustered token list
-struct DecTokArgs {
-  const int32_t* cache_len; const int32_t* sel; const int32_t* sel_cnt;
-  const int32_t* cl_m; const int32_t* cl_off; const int32_t* cl_mem;
-  int32_t* tok; int32_t* tok_cnt;
-  int Lmax, nbmax, n_ret, width, n_recent;
-};
-
-// grid (n_ret, B), 256 threads: the tokens a retrieval head attends in the
-// clustered decode, in the order of its kept ids (ascending): the members
-// of a kept cluster (1 <= id < m, in ascending token order) or every token
-// of a kept block (the sink, blocks that left the recent window after the
-// clustering, the recent blocks). Segment starts come from a block-wide
-// scan of the segment lengths; each wave then copies whole segments.
-__global__ __launch_bounds__(256) void dec_tokens_kernel(const DecTokArgs a) {
-  __shared__ int tmp[4];
-  __shared__ int sid[256], spos[256], slen[256];
-  __shared__ int carry_s;
-  const int rho = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  int L = a.cache_len[b];
-  L = L < 1 ? 1 : (L > a.Lmax ? a.Lmax : L);
-  const int n_b = (L + 63) / 64;
-  const size_t row = (size_t)b * a.n_ret + rho;
-  const int n_sel = a.sel_cnt[row];
-  const int32_t* ids = a.sel + row * a.width;
-  const int m = min(a.cl_m[b], n_b - a.n_recent);  // recent blocks stay blocks
-  const int32_t* off = a.cl_off + row * (a.nbmax + 1);
-  const int32_t* mem = a.cl_mem + row * a.Lmax;
-  int32_t* out = a.tok + row * a.Lmax;
-  int carry = 0;
-  for (int s0 = 0; s0 < n_sel; s0 += 256) {
-    const int e = s0 + tid;
-    const int id = e < n_sel ? ids[e] : -1;
-    int len = 0;
-    if (id >= 0) {
-      if (id >= 1 && id < m) len = min(max(off[id + 1] - off[id], 0), a.Lmax);
-      else len = max(0, min(L, 64 * id + 64) - 64 * id);
-    }
-    const int incl = block_incl_scan(len, tmp);
-    sid[tid] = id;
-    spos[tid] = carry + incl - len;
-    slen[tid] = len;
-    if (tid == 255) carry_s = carry + incl;
+  if (ta.tok) {
+    // the kept ids are written by this block: after the barrier its waves
+    // read them back (one CU, one L1), and turn them into the token list
     __syncthreads();
-    const int nseg = min(256, n_sel - s0);
-    // (the list holds at most Lmax ids and every id is a cached token, also
-    // for tables that do not match this cache)
-    for (int si = wave; si < nseg; si += 4) {
-      const int id = sid[si], pos = spos[si], len = slen[si];
-      const int n_w = max(0, min(len, a.Lmax - pos));
-      if (id >= 1 && id < m) {
-        const int32_t* src = mem + min(max(off[id], 0), a.Lmax - len);
-        for (int i = lane; i < n_w; i += 64) out[pos + i] = min(max(src[i], 0), L - 1);
-      } else {
-        for (int i = lane; i < n_w; i += 64) out[pos + i] = 64 * id + i;
-      }
-    }
-    carry = carry_s;
-    __syncthreads();
+    build_token_list(ta, out, 1 + a.top_k + n_rec, L, n_b, a.n_recent, a.Lmax,
+                     a.nbmax, row_id, b, tsh.tok);
   }
-  if (tid == 0) a.tok_cnt[row] = min(carry, a.Lmax);
 }
 
 // ---------------------------------------------------------------- attention
@@ -825,31 +861,18 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t st) {
   da.n_units = nu;
   const int n_ret_units = nu - n_win_units;
 
+  DecTokArgs ta;
+  ta.cl_m = a.cl_m;
+  ta.cl_off = a.cl_off;
+  ta.cl_mem = a.cl_mem;
+  ta.tok = clustered ? a.tok : nullptr;
+  ta.tok_cnt = a.tok_cnt;
   auto select = [&]() {
     prof_begin("dec_select", st);
     hipLaunchKernelGGL(dec_select_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st,
                        a.q, a.p_q, a.cent, a.cache_len, sa, a.cscores, a.sel,
-                       a.sel + (size_t)a.B * a.n_ret * width);
+                       a.sel + (size_t)a.B * a.n_ret * width, ta);
     prof_end(st);
-    if (clustered) {
-      DecTokArgs ta;
-      ta.cache_len = a.cache_len;
-      ta.sel = a.sel;
-      ta.sel_cnt = a.sel + (size_t)a.B * a.n_ret * width;
-      ta.cl_m = a.cl_m;
-      ta.cl_off = a.cl_off;
-      ta.cl_mem = a.cl_mem;
-      ta.tok = a.tok;
-      ta.tok_cnt = a.tok_cnt;
-      ta.Lmax = a.Lmax;
-      ta.nbmax = nbmax;
-      ta.n_ret = a.n_ret;
-      ta.width = width;
-      ta.n_recent = a.n_recent;
-      prof_begin("dec_tokens", st);
-      hipLaunchKernelGGL(dec_tokens_kernel, dim3(a.n_ret, a.B), dim3(256), 0, st, ta);
-      prof_end(st);
-    }
   };
   auto attend = [&](const char* name, int base, int n, hipStream_t on) {
     DecAttnArgs d = da;
