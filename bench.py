@@ -64,19 +64,30 @@ COUNTERS = {
         "write_bytes": 6217822925},
 }
 _IDX = {"unit": "indexer.hip",
-        "sources": [_K + "indexer.hip", _K + "select.h"],
-        "sha256": "dbf64923fbc772b3963dfc0396a8a5f5f91c34f12abaea8a340abd38226277b8"}
-for _key, _kern, _f, _w in (
+        "sources": [_K + "indexer.hip", _K + "proj.h", _K + "select.h"],
+        "sha256": "c2db51d848f9447bab3ecb5bd178cf0557c57d8a3c8f5de32a8844a30ed7f013"}
+_CL = {"unit": "cluster.hip", "sources": [_K + "cluster.hip", _K + "proj.h"],
+       "sha256": "4909d7ada22d4370f545ea56ee46ba2f0a1e014964cd583820e60cf8a796a1c7"}
+_DEC = {"unit": "decode.hip", "sources": [_K + "decode.hip", _K + "select.h"],
+        "sha256": "baf70ffab5a270962dfac5930a881915017b3b38de9b3f542797acb1c77b26aa"}
+for _base, _key, _kern, _f, _w in (
         # bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1
-        ("proj_keys@128k", "proj_keys", 68690125, 41943040),
-        ("proj_qmeans@128k", "proj_qmeans", 168186675, 656282),
-        ("block_scores@128k", "block_scores", 263329382, 42321715),
-        ("topk@128k", "topk", 43197235, 5898240),
+        (_IDX, "proj_keys@128k", "proj_keys", 68202906, 41943040),
+        (_IDX, "proj_qmeans@128k", "proj_qmeans", 168183603, 656384),
+        (_IDX, "block_scores@128k", "block_scores", 263554867, 42320896),
+        (_IDX, "topk@128k", "topk", 43121254, 5898240),
         # bench.py --leg 1m --steps 2 --warmup 1
-        ("proj_keys@1m", "proj_keys", 1112170086, 1543504589),
-        ("proj_qmeans@1m", "proj_qmeans", 6175680307, 24130867),
-        ("score_select@1m", "score_select", 57258742374, 15278940160)):
-    COUNTERS[_key] = dict(_IDX, kernel=_kern, fetch_bytes=_f, write_bytes=_w)
+        (_IDX, "proj_keys@1m", "proj_keys", 1091617178, 1543503974),
+        (_IDX, "proj_qmeans@1m", "proj_qmeans", 6175664742, 24131174),
+        (_IDX, "score_select@1m", "score_select", 57276927181, 14497168384),
+        # bench.py --leg cluster --steps 4 --warmup 1 (per launch: one
+        # projection and one Lloyd step's kernels)
+        (_CL, "cl_project@cluster", "cl_project", 10740339507, 2682495181),
+        (_CL, "cl_assign@cluster", "cl_assign", 3018200269, 1475449651),
+        (_CL, "cl_update@cluster", "cl_update", 5420282880, 31043072),
+        (_DEC, "dec_attn_retrieval@cluster", "dec_attn_retrieval", 523299430,
+         698573)):
+    COUNTERS[_key] = dict(_base, kernel=_kern, fetch_bytes=_f, write_bytes=_w)
 TRAFFIC_KEY = "attn_window@128k"
 
 
@@ -469,6 +480,7 @@ def bench_cluster(rtp, torch, w, steps, warmup):
     if "cl_assign" in cks:
         t = cks["cl_assign"]["ms_per_launch"] / 1e3
         res["assign_valu_frac"] = 3 * pairs / t / 1e12 / PEAK_VALU_TOPS
+    res["hbm_counters"] = hbm_counters("cluster", {**cks, **ks})
     del y, ws, out, cent, cent0, cws, tables
     torch.cuda.empty_cache()
     return res
