@@ -365,3 +365,15 @@ def test_clustered_decode_full_size_sampled(gpu_lib):
     check_clustered_decode(gs, sub, "full")
     out_sub = gs.decode()[0]
     assert torch.equal(out_sub.view(torch.int16), out_all[seqs].view(torch.int16))
+
+
+def test_clustered_decode_rank_32(gpu_lib):
+    # r = 32: the selection's general scoring loop (with the empty-cluster
+    # check) and two 16-row halves per projection tile
+    lens = [64 * 150 + 40, 64 * 33 + 1]
+    y = make_decode(_wl(2, max(lens), Hq=4, Hkv=1, ret=(0, 2), window=128,
+                        top_k=9, r=32, seed=17), cache_len=lens)
+    g = Gpu(gpu_lib, y, r=32)
+    for it in range(2):
+        _gpu_and_oracle_step(g, y, it, "r32 decode")
+    check_clustered_decode(g, y, "r32")

@@ -169,3 +169,36 @@ def test_decode_equal_scores_past_32k_candidates(gpu_lib):
     got = [int(v) for v in sel.cpu().numpy()[0, 0] if v >= 0]
     assert got == [0] + list(range(1, top_k + 1)) + [n_b - 2, n_b - 1], \
         (got[:4], got[-4:])
+
+
+@pytest.mark.parametrize("r", [32, 48, 128])
+def test_prefill_streaming_select_other_ranks(gpu_lib, r):
+    # the fused scoring-and-selection kernel for every operand width it is
+    # built for beyond r = 16 (two key-block groups per load for r = 32, one
+    # for wider), on a sequence just past 4096 blocks
+    S = 64 * 4100 + 29
+    w = PrefillWorkload("long", S=S, Hq=2, Hkv=1, d=128, n_ret=1, window=64,
+                        r=r, block=64, top_k=40, seed=r,
+                        retrieval_heads=(1,))
+    print(f"[long] streaming select r={r} S={S}", flush=True)
+    x = make_prefill(w, device="cuda")
+    pq = torch.from_numpy(x["p_q"]).cuda()
+    pk = torch.from_numpy(x["p_k"]).cuda()
+    sel, cnt, kth, _ = gpu_lib.indexer_select(x["q"], x["k"], x["is_retrieval"],
+                                              pq, pk, w.top_k, r=r, kth=True)
+    torch.cuda.synchronize()
+    n_b = w.n_blocks
+    rows = _rows(n_b, 100 + r, stride=48)
+    qbits = np.empty((2, S, 128), np.uint16)
+    qbits[1] = bf16_bits(x["q"][1])
+    kbits = bf16_bits(x["k"])
+    ora = oracle.hybrid_prefill(qbits, kbits, kbits, x["is_retrieval"], 64,
+                                x["p_q"], x["p_k"], 64, w.top_k, heads=[1],
+                                query_blocks=[], sel_rows=rows)
+    g_sel, g_cnt = sel.cpu().numpy()[0], cnt.cpu().numpy()[0]
+    fn = parity.prefill_rows_fn(x, qbits, kbits, 0, 1)
+    ties = parity.compare_selection(
+        g_sel[rows], g_cnt[rows], ora["sel"][0][rows], ora["sel_count"][0][rows],
+        ora["kth"][0][rows], lambda i: fn(rows[i]),
+        parity.prefill_required(lambda i: rows[i]), f"stream r={r}")
+    parity.assert_tie_rate(ties, len(rows), f"stream r={r}")
