@@ -100,7 +100,12 @@ int rtp_profile(int enable);
 int rtp_profile_read(const char** names, float* ms, int max);
 
 /* Workspace bytes needed by rtp_indexer_select / rtp_hybrid_attn_prefill
- * for these sizes (0 on invalid arguments). */
+ * for these sizes (0 on invalid arguments). Linear in S: V^T of every KV
+ * head, the projected keys (4 r bytes per token per retrieval head) and
+ * the selections; up to 4096 blocks also the score rows of each retrieval
+ * head (a lower triangle, at most 33.5 MB per head), past them fixed-size
+ * candidate buffers instead (0.56 GiB for top_k = 256). For example 0.13 GiB
+ * at S = 128K with 5 retrieval heads and 2.39 GiB at S = 1M with 23. */
 size_t rtp_prefill_workspace_bytes(int S, int Hq, int Hkv, int d,
                                    const uint8_t* is_retrieval, int r,
                                    int block, int top_k);
