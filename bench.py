@@ -308,6 +308,50 @@ def bench_prefill(rtp, torch, w, steps, warmup, dense=False, full=False,
     return res
 
 
+def gemm_reference(torch):
+    """The vendor GEMM on the same device and clock: torch.matmul in bf16
+    (hipBLASLt) at 16384 x 16384 x 8192. A practical matrix-core ceiling to
+    read the attention kernels' fractions of the published peak against."""
+    m, n, k = 16384, 16384, 8192
+    a = torch.randn(m, k, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(k, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"gemm": f"torch.matmul bf16 {m}x{n}x{k}", "ms": ms,
+            "tflops": 2 * m * n * k / (ms / 1e3) / 1e12}
+
+
+def timed_steps(rtp, torch, call, steps, warmup):
+    """Decode steps: the wall time per step from a loop without the
+    per-kernel event timer (at a fraction of a millisecond per step, the
+    events recorded around every kernel would add about a tenth), then the
+    per-kernel times from a second, timed loop of as many steps."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / steps
+    with rtp.KernelTimer() as kt:
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+    return ms, kernel_stats(kt.records, steps)
+
+
 def bench_decode(rtp, torch, w, steps, warmup):
     from workloads import make_decode
     dev = "cuda"
@@ -333,17 +377,7 @@ def bench_decode(rtp, torch, w, steps, warmup):
                                       out=out, want_sel=want_sel)
     torch.cuda.synchronize()
     log(f"[bench] {w.name}: inputs + centroids ready in {time.time() - t0:.1f}s")
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    with rtp.KernelTimer() as kt:
-        t1 = time.perf_counter()
-        for _ in range(steps):
-            call()
-        torch.cuda.synchronize()
-        t2 = time.perf_counter()
-    ms = (t2 - t1) * 1e3 / steps
-    ks = kernel_stats(kt.records, steps)
+    ms, ks = timed_steps(rtp, torch, call, steps, warmup)
     _, _, sel = call(want_sel=True)
     torch.cuda.synchronize()
     sel = sel.cpu().numpy()
@@ -424,17 +458,7 @@ def bench_cluster(rtp, torch, w, steps, warmup):
             y["q"], y["k_cache"], y["v_cache"], cl, y["is_retrieval"],
             w.window, pq, cent, tables, w.top_k, n_recent=w.n_recent, ws=ws,
             out=out, want_sel=want_sel)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    with rtp.KernelTimer() as kt:
-        t3 = time.perf_counter()
-        for _ in range(steps):
-            call()
-        torch.cuda.synchronize()
-        t4 = time.perf_counter()
-    ms = (t4 - t3) * 1e3 / steps
-    ks = kernel_stats(kt.records, steps)
+    ms, ks = timed_steps(rtp, torch, call, steps, warmup)
     _, _, sel = call(want_sel=True)
     torch.cuda.synchronize()
     sel = sel.cpu().numpy()
@@ -679,6 +703,10 @@ def main():
             rtp, torch, PREFILL_128K, max(2, args.steps // 2), 1, full=True)
         log(f"[bench] 128K with full retrieval heads: "
             f"{extra['full_retrieval_128k']['ms_per_step']:.2f} ms/step")
+    gemm = gemm_reference(torch)
+    gemm["window_kernel_frac"] = main["window_kernel_tflops"] / gemm["tflops"]
+    log(f"[bench] vendor bf16 GEMM on this device: {gemm['tflops']:.0f} TF/s "
+        f"(window kernel at {gemm['window_kernel_frac']:.2f} of it)")
     if args.copy_probe_gib > 0:
         copy_probe()
     cpu = None
@@ -711,7 +739,7 @@ def main():
                      "frac": main["window_kernel_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic()},
         "cpu_baseline": cpu,
-        "detail": {"prefill_128k": main, **extra},
+        "detail": {"prefill_128k": main, "gemm_reference": gemm, **extra},
     }
     print(json.dumps(line), flush=True)
 
