@@ -130,6 +130,14 @@ def test_decode_many_heads_per_group(gpu_lib, Hq):
     check(gpu_lib, y, f"gqa{Hq}")
 
 
+def test_decode_at_the_head_limit(gpu_lib):
+    # 128 query heads over 2 KV heads: each group's 62 or 63 streaming heads
+    # take two units, and the retrieval heads sit far apart
+    y = make_decode(_wl(2, 1500, Hq=128, Hkv=2, ret=(5, 100), window=300,
+                        top_k=6), cache_len=[1500, 1000])
+    check(gpu_lib, y, "heads128")
+
+
 def test_decode_runs_after_earlier_work_on_the_callers_stream(gpu_lib):
     # Streaming heads run on a stream of the library's own; they must still
     # see what the caller's stream wrote just before the call. V = 1 is made

@@ -97,6 +97,19 @@ def test_indexer_ranks(gpu_lib, r):
     full_check(gpu_lib, x, f"r{r}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,ret,S", [
+    (40, 2, (0, 21, 39), 64 * 19 + 9),
+    (128, 8, (0, 17, 64, 127), 64 * 5 + 1),
+])
+def test_wide_groups_and_the_head_limit(gpu_lib, Hq, Hkv, ret, S):
+    # 20 heads per KV group (window-kernel work items then span query
+    # blocks), and the largest head count the library takes (128, groups of
+    # 16, retrieval heads at both ends)
+    x = make_prefill(_wl(S, Hq=Hq, Hkv=Hkv, ret=ret, window=333, top_k=3,
+                         seed=Hq))
+    full_check(gpu_lib, x, f"Hq{Hq}")
+
+
 def test_every_head_retrieval_one_head_per_group(gpu_lib):
     # G = 1 and no streaming heads: only the sparse kernel runs
     x = make_prefill(_wl(64 * 21 + 3, Hq=3, Hkv=3, ret=(0, 1, 2), window=64,
