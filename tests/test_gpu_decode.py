@@ -130,6 +130,45 @@ def test_decode_many_heads_per_group(gpu_lib, Hq):
     check(gpu_lib, y, f"gqa{Hq}")
 
 
+def test_cache_rows_past_each_length_are_never_read(gpu_lib):
+    # NaN in every K/V row at or past a sequence's length: a row read there
+    # would reach the output even with weight 0 (0 x NaN), so the outputs
+    # must equal those of the clean cache bit for bit, in the block and the
+    # clustered decode
+    rtp = gpu_lib
+    lens = [64 * 40 + 17, 64 * 9, 5, 64 * 63 + 63]
+    y = make_decode(_wl(4, 64 * 64, Hq=8, Hkv=2, ret=(2, 5), window=200,
+                        top_k=6), cache_len=lens)
+    dev = "cuda"
+    kc, vc = y["k_cache"].to(dev), y["v_cache"].to(dev)
+    kn, vn = kc.clone(), vc.clone()
+    for b, L in enumerate(lens):
+        kn[b, :, L:] = float("nan")
+        vn[b, :, L:] = float("nan")
+    cl = torch.from_numpy(y["cache_len"]).to(dev)
+    pk = torch.from_numpy(y["p_k"]).to(dev)
+    pq = torch.from_numpy(y["p_q"]).to(dev)
+    q = y["q"].to(dev)
+    outs = []
+    for k_, v_ in ((kc, vc), (kn, vn)):
+        cent = rtp.build_centroids(k_, cl, y["is_retrieval"], pk)
+        o1, l1, s1 = rtp.hybrid_attn_decode(
+            q, k_, v_, cl, y["is_retrieval"], y["window"], pq, cent,
+            y["top_k"], want_lse=True, want_sel=True)
+        t = rtp.cluster_keys(k_, cl, y["is_retrieval"], pk, cent, iters=2)
+        o2, l2, s2 = rtp.hybrid_attn_decode_clustered(
+            q, k_, v_, cl, y["is_retrieval"], y["window"], pq, cent, t,
+            y["top_k"], want_lse=True, want_sel=True)
+        torch.cuda.synchronize()
+        outs.append((o1, l1, s1, o2, l2, s2))
+    for a, b in zip(*outs):
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b)
+    assert not torch.isnan(outs[1][0].float()).any()
+    assert not torch.isnan(outs[1][3].float()).any()
+
+
 def test_decode_at_the_head_limit(gpu_lib):
     # 128 query heads over 2 KV heads: each group's 62 or 63 streaming heads
     # take two units, and the retrieval heads sit far apart
