@@ -110,6 +110,29 @@ def test_wide_groups_and_the_head_limit(gpu_lib, Hq, Hkv, ret, S):
     full_check(gpu_lib, x, f"Hq{Hq}")
 
 
+def test_nothing_is_read_past_the_inputs(gpu_lib):
+    # Q, K and V as the front of buffers whose remainder is NaN: a read past
+    # any of them (the ragged last block of the last head) would reach the
+    # output even with weight 0, so the results must equal those of plain
+    # tensors bit for bit
+    x = make_prefill(_wl(64 * 30 + 5, Hq=4, Hkv=2, ret=(1, 3), window=100,
+                         top_k=3, seed=9))
+    d = _to_dev(x)
+    padded = dict(d)
+    for key in ("q", "k", "v"):
+        t = d[key]
+        buf = torch.full((t.numel() + 64 * 128 * 8,), float("nan"),
+                         dtype=t.dtype, device=t.device)
+        padded[key] = buf[:t.numel()].view(t.shape)
+        padded[key].copy_(t)
+    a = _run_gpu(gpu_lib, d)
+    b = _run_gpu(gpu_lib, padded)
+    for u, v in zip(a, b):
+        if u.dtype == torch.bfloat16:
+            u, v = u.view(torch.int16), v.view(torch.int16)
+        assert torch.equal(u, v)
+
+
 def test_every_head_retrieval_one_head_per_group(gpu_lib):
     # G = 1 and no streaming heads: only the sparse kernel runs
     x = make_prefill(_wl(64 * 21 + 3, Hq=3, Hkv=3, ret=(0, 1, 2), window=64,
