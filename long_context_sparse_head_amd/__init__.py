@@ -10,6 +10,31 @@ used for device memory and streams only.
 
 The library must be built (``python -m long_context_sparse_head_amd.build``);
 every call raises if it is missing. There is no fallback.
+
+A layer, end to end (bf16 tensors on the GPU; ``is_retrieval`` a host
+sequence of 0/1 per query head; ``p_q``, ``p_k`` fp32 [n_ret, r, 128])::
+
+    import long_context_sparse_head_amd as rtp
+    # prefill: q [Hq,S,128], k and v [Hkv,S,128]
+    out = rtp.hybrid_attn_prefill(q, k, v, is_retrieval, 8192, p_q, p_k,
+                                  top_k=64)
+    # decode cache [B,Hkv,Lmax,128] holding the prompt; lengths int32 [B]
+    cent = rtp.build_centroids(k_cache, cache_len, is_retrieval, p_k)
+    for _ in range(steps):
+        rtp.decode_append(k_cache, v_cache, cache_len, k_new, v_new,
+                          is_retrieval, p_k, cent)   # k_new [B,Hkv,128]
+        o = rtp.hybrid_attn_decode(q_t, k_cache, v_cache, cache_len,
+                                   is_retrieval, 8192, p_q, cent, top_k=64)
+    # or cluster the keys first and decode over the clusters
+    tables = rtp.cluster_keys(k_cache, cache_len, is_retrieval, p_k, cent,
+                              iters=2)
+    o = rtp.hybrid_attn_decode_clustered(q_t, k_cache, v_cache, cache_len,
+                                         is_retrieval, 8192, p_q, cent,
+                                         tables, top_k=64)
+
+Each call has a ``*_workspace_bytes`` companion; passing ``ws=`` (a
+uint8 tensor of that size) avoids an allocation per call. Paged caches go
+through :class:`PagedCache` and the ``*_paged`` calls.
 """
 from __future__ import annotations
 
