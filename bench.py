@@ -613,8 +613,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU "
-              "path (see DESIGN.md for how it would shard); run with --gpus 1",
-              file=sys.stderr)
+              "path (prefill would shard by KV group or by query positions, "
+              "decode by sequence); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import long_context_sparse_head_amd as rtp
