@@ -86,7 +86,14 @@ for _base, _key, _kern, _f, _w in (
         (_CL, "cl_assign@cluster", "cl_assign", 3018200269, 1475449651),
         (_CL, "cl_update@cluster", "cl_update", 5420282880, 31043072),
         (_DEC, "dec_attn_retrieval@cluster", "dec_attn_retrieval", 523299430,
-         698573)):
+         698573),
+        # bench.py --leg decode --steps 4 --warmup 1
+        (_DEC, "dec_attn_window@decode", "dec_attn_window", 539505843,
+         3761872),
+        (_DEC, "dec_attn_retrieval@decode", "dec_attn_retrieval", 340548365,
+         697123),
+        (_DEC, "dec_select@decode", "dec_select", 42693939, 52480),
+        (_DEC, "dec_merge@decode", "dec_merge", 4352205, 262144)):
     COUNTERS[_key] = dict(_base, kernel=_kern, fetch_bytes=_f, write_bytes=_w)
 TRAFFIC_KEY = "attn_window@128k"
 
@@ -408,6 +415,7 @@ def bench_decode(rtp, torch, w, steps, warmup):
         if name in ks:
             res[name + "_gbs_alg"] = part / (ks[name]["ms_per_launch"] / 1e3) / 1e9
     res["step_frac_hbm"] = res["step_gbs_alg"] / PEAK_HBM_GBS
+    res["hbm_counters"] = hbm_counters("decode", ks)
     del y, ws, out, cent
     torch.cuda.empty_cache()
     return res
