@@ -3,8 +3,12 @@
 // step are in attn_core.h; the window kernel is in attn_window.hip.
 //
 // Each wave runs its own (retrieval head, query block) job over its block
-// list in 32-key half tiles; K and V^T half tiles are staged per wave by LDS
-// DMA, three ahead of the one whose P.V runs.
+// list in 32-key half tiles. K half tiles are staged per wave by LDS DMA;
+// the V^T operands of a half tile are loaded straight into registers (V^T
+// blocks are stored in MFMA operand order, one contiguous KiB per operand),
+// four half tiles ahead of their P.V.
+#include <type_traits>
+
 #include "attn_core.h"
 
 namespace rtp {
@@ -12,10 +16,9 @@ namespace rtp {
 // =====================================================================
 // Sparse kernel
 // =====================================================================
-constexpr int VHALF_B = 8192;  // V^T of 32 keys: 128 d x 64 B
 constexpr int KHALF_B = 8192;  // K of 32 keys: 32 rows x 256 B
-// per wave: a ring of 2 K and 3 V^T half tiles (4 waves: 160 KiB of LDS)
-constexpr int SP_WAVE_B = 2 * KHALF_B + 3 * VHALF_B;
+// per wave: a ring of 2 K half tiles (4 waves: 64 KiB of LDS)
+constexpr int SP_WAVE_B = 2 * KHALF_B;
 
 struct SparseParams {
   const u16* q; const u16* k; const u16* vt; u16* out; float* lse;
@@ -29,25 +32,6 @@ struct SparseParams {
   int16_t rho_begin[kMaxHeads + 1];
   uint8_t head_of_rho[kMaxHeads];
 };
-
-// V^T half tile (32 keys): row d x 4 chunks of 16 B, chunk c at
-// c ^ ((d >> 2) & 3), so the 16 rows that 16 consecutive lanes read hit 16
-// distinct bank groups. Load ins (0..7) covers rows 16 ins .. 16 ins + 15;
-// the lane part of the global offset is the same for every load and tile.
-__device__ __forceinline__ uint32_t sp_v_lane_off(int lane) {
-  const int c = (lane & 3) ^ ((lane >> 4) & 3);
-  return (uint32_t)((lane >> 2) * 128 + c * 16);
-}
-
-// rv: buffer descriptor of the KV group's V^T blocks; k0: first key of the
-// half tile
-__device__ __forceinline__ void sp_issue_v(__amdgpu_buffer_rsrc_t rv, int k0,
-                                           uint32_t voff, char* slot) {
-  const uint32_t toff = (uint32_t)(k0 >> 6) * (64 * kD * 2) + (k0 & 63) * 2;
-#pragma unroll
-  for (int ins = 0; ins < 8; ++ins)
-    buf_dma16(rv, voff + ins * 16 * 128, toff, slot + ins * 1024);
-}
 
 __device__ __forceinline__ void wait_vm24() {
   __builtin_amdgcn_s_waitcnt((24 & 15) | (7 << 4) | (15 << 8) | ((24 >> 4) << 14));
@@ -121,11 +105,10 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   cnt = cnt < 0 ? 0 : (cnt > p.sel_stride ? p.sel_stride : cnt);
   const int nt = 2 * cnt;  // 32-key half tiles (even)
   char* const kslots = smem + wave * SP_WAVE_B;
-  char* const vslots = kslots + 2 * KHALF_B;
   const __amdgpu_buffer_rsrc_t kbase =
       buf_rsrc(p.k + (size_t)g * S * kD, (uint32_t)S * (kD * 2));
-  const __amdgpu_buffer_rsrc_t vbase = buf_rsrc(
-      p.vt + (size_t)g * p.n_b * 64 * kD, (uint32_t)p.n_b * (64 * kD * 2));
+  // this lane's 16 bytes of each V^T operand of the KV group's blocks
+  const u16* const vblk = p.vt + (size_t)g * p.n_b * 64 * kD + lane * 8;
   // Half tile t: blocks from the last (the diagonal) to the first, halves
   // ascending, so the first half tile holds every query's own key and sets
   // the reference. Indices past the end re-read the last half tile, so every
@@ -142,9 +125,7 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
   };
   uint32_t koffs[4];
   sp_k_lane_offs(lane, koffs);
-  const uint32_t voff = sp_v_lane_off(lane);
-  // this lane's operand rows: K row perm_row(n) (chunk 2 ks + g, swizzled),
-  // V^T row 32 mt + n (chunk 2 h + g, swizzled)
+  // this lane's K operand row: perm_row(n) (chunk 2 ks + g, swizzled)
   const int g2 = lane >> 5, n32 = lane & 31;
   const int kr_row = perm_row(n32);
   auto kop_at = [=](const char* slot) {
@@ -153,12 +134,13 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
       return *reinterpret_cast<const bf16x8*>(slot + kr_row * 256 + c * 16);
     };
   };
-  auto vop_at = [=](const char* slot) {
-    return [=](int h, int mt) {
-      const int d = 32 * mt + n32;
-      const int c = (2 * h + g2) ^ ((d >> 2) & 3);
-      return *reinterpret_cast<const bf16x8*>(slot + d * 64 + c * 16);
-    };
+  // the eight V^T operands (h = 0, 1; mt = 0..3, index 4 h + mt) of the
+  // half tile starting at key k0
+  auto load_v = [&](int k0, bf16x8 (&dst)[8]) {
+    const u16* b = vblk + (size_t)(k0 >> 6) * (64 * kD) + ((k0 >> 5) & 1) * 4096;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dst[i] = *reinterpret_cast<const bf16x8*>(b + i * 512);
   };
 
   bf16x8 qf[2][8];
@@ -185,53 +167,66 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
     }
   };
 
-  // K of half tile t lives in K slot t % 2, V^T in V slot t % 3, both
-  // staged by LDS DMA; every step issues one half tile (8 + 8 loads), three
-  // ahead of the half tile whose P.V it runs.
+  // K of half tile t lives in K slot t % 2 (LDS DMA, two half tiles ahead
+  // of its QK), its V^T operands in register slot t % 4 (loaded four half
+  // tiles ahead of its P.V). Issue order: V0 K0 V1 K1 V2, then K2 V3 after
+  // the first QK, then step t issues K(t+3) and V(t+4) at its end, so
+  // before step t everything up to K(t+1) has landed once at most 24 newer
+  // loads remain (V(t+2), K(t+2), V(t+3)); V(t) is older than K(t+1).
+  bf16x8 vr[4][8];
   f32x16 sa[1][2], sb[1][2];
   for (int attempt = 0;; ++attempt) {
-    const int k0_0 = tile_k0(0), k0_1 = tile_k0(1), k0_2 = tile_k0(2);
+    const int k0_0 = tile_k0(0), k0_1 = tile_k0(1);
+    load_v(k0_0, vr[0]);
     sp_issue_k(kbase, S, k0_0, koffs, kslots, lane);
-    sp_issue_v(vbase, k0_0, voff, vslots);
+    load_v(k0_1, vr[1]);
     sp_issue_k(kbase, S, k0_1, koffs, kslots + KHALF_B, lane);
-    sp_issue_v(vbase, k0_1, voff, vslots + VHALF_B);
+    load_v(tile_k0(2), vr[2]);
     wait_vm24();  // K(0) resident
     qk_lds(kslots, sa);
     mask(sa, k0_0);
     if (attempt == 0) raise_refs<1>(sa, sf);
     wait_lgkm0();  // reads of K slot 0 done
-    sp_issue_k(kbase, S, k0_2, koffs, kslots, lane);
-    sp_issue_v(vbase, k0_2, voff, vslots + 2 * VHALF_B);
-    char* vcur = vslots;  // V slot of the current half tile t
-    char* vn1 = vslots + VHALF_B;
-    char* vn2 = vslots + 2 * VHALF_B;
+    sp_issue_k(kbase, S, tile_k0(2), koffs, kslots, lane);
+    load_v(tile_k0(3), vr[3]);
     bool over = false;
-    // step t: S(t) in sc -> P.V with V^T(t); QK(t+1) from K slot (t+1) % 2
-    // -> sn; then the loads of half tile t+3 (K into that K slot, V^T into
-    // t's V slot)
-    auto step = [&](int t, char* kslot, f32x16 (&sc)[1][2],
+    // step t: S(t) in sc -> P.V with V^T(t) (registers, slot t % 4); QK(t+1)
+    // from K slot (t+1) % 2 -> sn; then K(t+3) into that K slot and V^T(t+4)
+    // into register slot t % 4
+    auto step = [&](auto ring, int t, f32x16 (&sc)[1][2],
                     f32x16 (&sn)[1][2]) {
-      wait_vm24();  // K(t+1) and V^T(t) resident
-      over |= attn_step<false>(kop_at(kslot), vop_at(vcur), [](int) {}, qf, sc, sn,
-                        sf, acc, p.c);
-      const int k0f = tile_k0(t + 3);
-      wait_lgkm0();  // this wave's reads of both slots are done
-      sp_issue_k(kbase, S, k0f, koffs, kslot, lane);
-      sp_issue_v(vbase, k0f, voff, vcur);
-      char* const done = vcur;
-      vcur = vn1;
-      vn1 = vn2;
-      vn2 = done;
+      constexpr int R = decltype(ring)::value;
+      char* const kslot = kslots + ((R + 1) & 1) * KHALF_B;
+      wait_vm24();  // K(t+1) resident, and V^T(t) before it
+      over |= attn_step<false>(
+          kop_at(kslot), [&](int h, int mt) { return vr[R][4 * h + mt]; },
+          [](int) {}, qf, sc, sn, sf, acc, p.c);
+      const int k0k = tile_k0(t + 3), k0v = tile_k0(t + 4);
+      wait_lgkm0();  // this wave's reads of the K slot are done
+      sp_issue_k(kbase, S, k0k, koffs, kslot, lane);
+      load_v(k0v, vr[R]);
     };
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
+    using R3 = std::integral_constant<int, 3>;
     // Rows are strictly ascending, so only the first block processed can be
     // the diagonal one: step 0 masks S(1), later steps need no masks.
-    step(0, kslots + KHALF_B, sa, sb);
+    step(R0{}, 0, sa, sb);
     mask(sb, k0_1);
-    for (int t = 1; t + 1 < nt; t += 2) {
-      step(t, kslots, sb, sa);
-      step(t + 1, kslots + KHALF_B, sa, sb);
+    int t = 1;
+    for (; t + 4 <= nt; t += 4) {
+      step(R1{}, t, sb, sa);
+      step(R2{}, t + 1, sa, sb);
+      step(R3{}, t + 2, sb, sa);
+      step(R0{}, t + 3, sa, sb);
     }
-    step(nt - 1, kslots, sb, sa);
+    // nt is even, so 1 or 3 steps remain
+    step(R1{}, t, sb, sa);
+    if (t + 1 < nt) {
+      step(R2{}, t + 1, sa, sb);
+      step(R3{}, t + 2, sb, sa);
+    }
     wait_vm_all();  // no DMA may still target this wave's LDS slots
     if (attempt > 0 || !__any(over)) break;
     // Rare: a score far above its row's reference. Find every row's true
@@ -253,8 +248,12 @@ __global__ __launch_bounds__(256, 1) void attn_sparse_kernel(const SparseParams 
 }
 
 // =====================================================================
-// V transpose: V [Hkv,S,128] -> V^T in 64-key blocks [Hkv][n_b][128][64]
-// (zero beyond S), so every key block's V^T is one contiguous 16 KiB read
+// V transpose: V [Hkv,S,128] -> V^T in 64-key blocks of 16 KiB (zero
+// beyond S), each block in MFMA operand order: unit u = ((hf * 2 + h) * 4 +
+// mt) * 64 + 32 g + n (16 bytes) holds V[32 hf + 16 h + 8 g + e][32 mt + n],
+// e = 0..7, the A operand of P.V for d 32 mt .. 32 mt + 31 and keys
+// 32 hf + 16 h .. + 15. So one 32-key half tile's eight operands are eight
+// contiguous KiB, and a lane's part of each is one 16-byte load.
 // =====================================================================
 constexpr int TSTR = 136;
 __global__ __launch_bounds__(256) void transpose_v_kernel(
@@ -271,17 +270,19 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
     *reinterpret_cast<uint4*>(t + row * TSTR + ch * 8) = x;
   }
   __syncthreads();
+  u16* dst = vt + ((size_t)g * (S_pad / 64) + kb) * (64 * kD);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, dr = c >> 3, kc = c & 7;
+    const int u = tid + 256 * i;  // consecutive threads: consecutive units
+    const int n = u & 31, gg = (u >> 5) & 1, mt = (u >> 6) & 3;
+    const int key0 = 16 * (u >> 8) + 8 * gg;  // 32 hf + 16 h + 8 g
+    const int d = 32 * mt + n;
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)t[(kc * 8 + 2 * e) * TSTR + dr] |
-             ((uint32_t)t[(kc * 8 + 2 * e + 1) * TSTR + dr] << 16);
-    *reinterpret_cast<uint4*>(
-        vt + (((size_t)g * (S_pad / 64) + kb) * kD + dr) * 64 + kc * 8) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+      w[e] = (uint32_t)t[(key0 + 2 * e) * TSTR + d] |
+             ((uint32_t)t[(key0 + 2 * e + 1) * TSTR + d] << 16);
+    *reinterpret_cast<uint4*>(dst + u * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 

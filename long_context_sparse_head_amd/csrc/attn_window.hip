@@ -24,14 +24,15 @@ constexpr int WSTAGES = 3;
 // Padded LDS rows (conflict-free for 8 consecutive rows, and every operand
 // address of a lane is one base register plus an immediate offset).
 constexpr int KROW_B = 272;                 // 256 B of K + 16 B pad
-constexpr int VROW_B = 144;                 // 128 B of V^T + 16 B pad
+// V^T is staged as stored: a 64-key block in MFMA operand order, where each
+// operand is one KiB read by the 64 lanes in order (conflict-free).
 constexpr int KTILE_B = 64 * KROW_B;        // 17408
-constexpr int VTILE_B = 128 * VROW_B;       // 18432
-constexpr int STAGE_B = KTILE_B + VTILE_B;  // 35840
+constexpr int VTILE_B = 64 * kD * 2;        // 16384
+constexpr int STAGE_B = KTILE_B + VTILE_B;  // 33792
 constexpr int K_DMA = KTILE_B / 1024;       // 17 loads of 1 KB
-constexpr int V_DMA = VTILE_B / 1024;       // 18 loads of 1 KB
+constexpr int V_DMA = VTILE_B / 1024;       // 16 loads of 1 KB
 constexpr int DMA_PER_WAVE = (K_DMA + V_DMA + 3) / 4;  // 9
-static_assert(K_DMA == 17 && V_DMA == 18 && DMA_PER_WAVE == 9,
+static_assert(K_DMA == 17 && V_DMA == 16 && DMA_PER_WAVE == 9,
               "win_issue deals the loads for this split");
 
 // Workgroups are dealt round-robin to the chip's 8 XCDs (each with its own
@@ -59,10 +60,10 @@ struct WinParams {
   int32_t pack_win[kMaxHeads];      // window of each pack
 };
 
-// The 35 DMA loads of a tile (17 K, 18 V^T) are dealt round-robin to the 4
+// The 33 DMA loads of a tile (17 K, 16 V^T) are dealt round-robin to the 4
 // waves. Load i writes LDS bytes [1024 i, 1024 i + 1024) of the stage (K rows
-// first, then V^T rows); a lane's 16-byte unit either holds data or is a pad
-// unit (then it re-reads a neighbouring chunk). A lane's global byte offset
+// first, then the V^T block); a lane's 16-byte K unit either holds data or is
+// a pad unit (then it re-reads a neighbouring chunk). A lane's global byte offset
 // inside a tile does not depend on the tile, so it is computed once.
 // K row r (MFMA row order) holds key (r & 32) + perm_row(r & 31).
 struct WinLaneOffsets {
@@ -75,9 +76,7 @@ __device__ __forceinline__ uint32_t win_unit_offset(int ld, int lane) {
     const int r = u / 17, c = min(u % 17, 15);
     return (uint32_t)(((r & 32) + perm_row(r & 31)) * 256 + c * 16);
   }
-  const int u = 64 * (ld - K_DMA) + lane;
-  const int d = u / 9, c = min(u % 9, 7);
-  return (uint32_t)(d * 128 + c * 16);  // V^T block row d: 64 keys, 128 B
+  return (uint32_t)((64 * (ld - K_DMA) + lane) * 16);  // V^T: as stored
 }
 
 __device__ __forceinline__ WinLaneOffsets win_offsets(int wave, int lane) {
@@ -116,8 +115,8 @@ __device__ __forceinline__ WinSrc win_src(const WinParams& p, int g) {
 
 // Load j (0..8) of this wave for a full tile: loads 0..3 are K rows, load 4 is
 // K for wave 0 and V^T for the others, loads 5..8 are V^T. The stage has only
-// 35 loads, so wave 3 repeats its load 7 as load 8 (same bytes, same place),
-// which keeps the issue free of branches.
+// 33 loads, so waves 1..3 repeat their load 7 as load 8 (same bytes, same
+// place), which keeps the issue free of branches.
 __device__ __forceinline__ void win_issue_one(const WinSrc& src, int kb,
                                               char* stage,
                                               const WinLaneOffsets& o,
@@ -131,7 +130,7 @@ __device__ __forceinline__ void win_issue_one(const WinSrc& src, int kb,
   } else if (j < 8) {
     buf_dma16(src.v, o.off[j], toff, stage + wave * 1024 + j * 4096);
   } else {
-    const int jj = wave < 3 ? 8 : 7;
+    const int jj = wave == 0 ? 8 : 7;
     buf_dma16(src.v, o.off[jj], toff, stage + wave * 1024 + jj * 4096);
   }
 }
@@ -177,14 +176,13 @@ __device__ __forceinline__ void win_qk(const char* stage, int st,
 __device__ __forceinline__ void win_pv(const char* stage, int st,
                                        const bf16x8 (&pb)[1][2][2],
                                        f32x16 (&acc)[2][4], int lane) {
-  const int g = lane >> 5, n = lane & 31;
-  const char* base = stage + KTILE_B + n * VROW_B + 16 * g + 64 * st;
+  const char* base = stage + KTILE_B + st * 8192 + lane * 16;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          base + 32 * mt * VROW_B + 32 * ks);
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(base + (ks * 4 + mt) * 1024);
       acc[0][mt] = mfma32(a, pb[0][0][ks], acc[0][mt]);
       acc[1][mt] = mfma32(a, pb[0][1][ks], acc[1][mt]);
     }
@@ -257,12 +255,11 @@ __device__ __forceinline__ bool win_step(const char* kst, int kh,
                                          int lane, DOp dop) {
   const int g = lane >> 5, n = lane & 31;
   const char* krow = kst + (32 * kh + n) * KROW_B + 16 * g;
-  const char* vrow = vst + KTILE_B + n * VROW_B + 16 * g + 64 * vh;
+  const char* vops = vst + KTILE_B + vh * 8192 + lane * 16;
   return attn_step<true>(
       [&](int ks) { return *reinterpret_cast<const bf16x8*>(krow + 32 * ks); },
       [&](int h, int mt) {
-        return *reinterpret_cast<const bf16x8*>(vrow + 32 * mt * VROW_B +
-                                                32 * h);
+        return *reinterpret_cast<const bf16x8*>(vops + (h * 4 + mt) * 1024);
       },
       dop, qf, s, sn, sf, acc, c);
 }
