@@ -47,21 +47,21 @@ COUNTERS = {
     "attn_window@128k": {
         "kernel": "attn_window", "unit": "attn_window.hip",
         "sources": [_K + "attn_window.hip", _K + "attn_core.h"],
-        "sha256": "84947ce2ccc820f9d461a8c01a6b3ff6cd451c7f05c754aea2410f88eb4aa194",
-        "fetch_bytes": 2935474530, "write_bytes": 906254451},
+        "sha256": "e988f16308a9848a871682a27ea745cd9d6d1a288e861fe66a4fd55897294521",
+        "fetch_bytes": 2935521280, "write_bytes": 906108211},
     "attn_sparse@128k": {
         "kernel": "attn_sparse", "unit": "attn.hip",
         "sources": [_K + "attn.hip", _K + "attn_core.h"],
-        "sha256": "e97c68e03aa9a9fd389b7a9b76819127d0092e31a63f1c24e61825af99e3e7d0",
-        "fetch_bytes": 16581650227,
-        "write_bytes": 168367411},
+        "sha256": "834f4571ea4b656c0830fac12fb27fe7456b9715abdd45b7b2f643ce33e3f866",
+        "fetch_bytes": 16634910925,
+        "write_bytes": 167957811},
     # bench.py --leg 1m --steps 2 --warmup 1
     "attn_sparse@1m": {
         "kernel": "attn_sparse", "unit": "attn.hip",
         "sources": [_K + "attn.hip", _K + "attn_core.h"],
-        "sha256": "e97c68e03aa9a9fd389b7a9b76819127d0092e31a63f1c24e61825af99e3e7d0",
-        "fetch_bytes": 2761143410073,
-        "write_bytes": 6217822925},
+        "sha256": "834f4571ea4b656c0830fac12fb27fe7456b9715abdd45b7b2f643ce33e3f866",
+        "fetch_bytes": 2409851323392,
+        "write_bytes": 6185473024},
 }
 _IDX = {"unit": "indexer.hip",
         "sources": [_K + "indexer.hip", _K + "proj.h", _K + "select.h"],
