@@ -357,7 +357,9 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const float* __restrict__ scores, int n_b, int top_k, int stride,
     int32_t* __restrict__ sel, int32_t* __restrict__ sel_cnt,
     float* __restrict__ kth) {
-  __shared__ uint32_t keys[TK_LDS + TK_LDS / 32];
+  // the row's keys (one pad word per 32): sized at launch for the longest
+  // row, so short sequences keep several workgroups per CU
+  extern __shared__ uint32_t keys[];
   __shared__ TopkShared sh;
   const int qb = blockIdx.x, rho = blockIdx.y, tid = threadIdx.x;
   const int n_c = max(qb - 1, 0);  // candidates 1 .. qb-1
@@ -1240,9 +1242,11 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t st) {
       prof_end(st);
     }
     prof_begin("topk", st);
-    hipLaunchKernelGGL(topk_kernel, dim3(a.n_b, a.n_ret), dim3(256), 0, st,
-                       scores, a.n_b, a.top_k, a.top_k + 2, a.sel, a.sel_cnt,
-                       a.kth);
+    const int nk = a.n_b < TK_LDS ? a.n_b : TK_LDS;
+    const size_t keys_bytes = ((size_t)nk + nk / 32 + 1) * 4;
+    hipLaunchKernelGGL(topk_kernel, dim3(a.n_b, a.n_ret), dim3(256),
+                       keys_bytes, st, scores, a.n_b, a.top_k, a.top_k + 2,
+                       a.sel, a.sel_cnt, a.kth);
     prof_end(st);
     return hipGetLastError();
   }
