@@ -65,21 +65,21 @@ COUNTERS = {
 }
 _IDX = {"unit": "indexer.hip",
         "sources": [_K + "indexer.hip", _K + "proj.h", _K + "select.h"],
-        "sha256": "c2db51d848f9447bab3ecb5bd178cf0557c57d8a3c8f5de32a8844a30ed7f013"}
+        "sha256": "a641ea7d7fc242ba52532275e7c229d901a796f838bba88284e9fe2b45e1acdc"}
 _CL = {"unit": "cluster.hip", "sources": [_K + "cluster.hip", _K + "proj.h"],
        "sha256": "4909d7ada22d4370f545ea56ee46ba2f0a1e014964cd583820e60cf8a796a1c7"}
 _DEC = {"unit": "decode.hip", "sources": [_K + "decode.hip", _K + "select.h"],
         "sha256": "baf70ffab5a270962dfac5930a881915017b3b38de9b3f542797acb1c77b26aa"}
 for _base, _key, _kern, _f, _w in (
         # bench.py --only-main --no-cpu-baseline --steps 3 --warmup 1
-        (_IDX, "proj_keys@128k", "proj_keys", 68202906, 41943040),
-        (_IDX, "proj_qmeans@128k", "proj_qmeans", 168183603, 656384),
-        (_IDX, "block_scores@128k", "block_scores", 263554867, 42320896),
-        (_IDX, "topk@128k", "topk", 43121254, 5898240),
+        (_IDX, "proj_keys@128k", "proj_keys", 68072499, 41943040),
+        (_IDX, "proj_qmeans@128k", "proj_qmeans", 168183706, 656608),
+        (_IDX, "block_scores@128k", "block_scores", 263814477, 42334682),
+        (_IDX, "topk@128k", "topk", 43118182, 5898240),
         # bench.py --leg 1m --steps 2 --warmup 1
-        (_IDX, "proj_keys@1m", "proj_keys", 1091617178, 1543503974),
-        (_IDX, "proj_qmeans@1m", "proj_qmeans", 6175664742, 24131174),
-        (_IDX, "score_select@1m", "score_select", 57276927181, 14497168384),
+        (_IDX, "proj_keys@1m", "proj_keys", 1090001632, 1543503968),
+        (_IDX, "proj_qmeans@1m", "proj_qmeans", 6175660384, 24130680),
+        (_IDX, "score_select@1m", "score_select", 57249297440, 14480385896),
         # bench.py --leg cluster --steps 4 --warmup 1 (per launch: one
         # projection and one Lloyd step's kernels)
         (_CL, "cl_project@cluster", "cl_project", 10740339507, 2682495181),
