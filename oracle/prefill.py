@@ -221,7 +221,9 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     NaN); sel_rows restricts which selection rows are computed (default: all
     rows, or the query_blocks when given).
 
-    Returns out (fp32 [Hq,S,d]), out_bf16 (uint16), lse (fp32 [Hq,S]), and
+    Returns out (fp32 [Hq,S,d]), out_bf16 (uint16), lse (fp32 [Hq,S]) (all
+    three None when no output rows are requested: heads or query_blocks
+    empty; out_bf16 holds the bf16 NaN pattern outside the computed rows), and
     for retrieval heads sel [n_ret,n_b,k+2] (ascending, -1 padded),
     sel_count [n_ret,n_b], kth [n_ret,n_b,2], centroids [n_ret,n_b,r].
     """
@@ -240,8 +242,13 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
         sel_rows = qblocks
     sel_rows = sorted(set(sel_rows))
 
-    out = np.full((Hq, S, d), np.nan, dtype=F32)
-    lse = np.full((Hq, S), np.nan, dtype=F32)
+    # Output arrays only when some output row is asked for: a selection-only
+    # call at long S would otherwise fill (and round) Hq*S*d unused values.
+    want_out = len(heads) > 0 and len(qblocks) > 0
+    out = np.full((Hq, S, d), np.nan, dtype=F32) if want_out else None
+    lse = np.full((Hq, S), np.nan, dtype=F32) if want_out else None
+    out_bf16 = (np.full((Hq, S, d), 0x7FC0, dtype=np.uint16) if want_out
+                else None)
     n_ret = len(ret_heads)
     sel_arr = np.full((n_ret, n_b, top_k + 2), -1, dtype=np.int32)
     sel_cnt = np.zeros((n_ret, n_b), dtype=np.int32)
@@ -253,7 +260,8 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
     def kv(g):
         if g not in kv_cache:
             kv_cache.clear()
-            kv_cache[g] = (bf16_to_f32(k_bits[g]), bf16_to_f32(v_bits[g]))
+            kv_cache[g] = (bf16_to_f32(k_bits[g]),
+                           bf16_to_f32(v_bits[g]) if want_out else None)
         return kv_cache[g]
 
     for h in heads:
@@ -287,7 +295,8 @@ def hybrid_prefill(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray,
                 union, member = swa_block_keys(rows, head_window(window, h))
             o, l = attend(qf[rows], kf[union], vf[union], member, scale)
             out[h, rows] = o
+            out_bf16[h, rows] = f32_to_bf16(o)
             lse[h, rows] = l
-    return dict(out=out, out_bf16=f32_to_bf16(out), lse=lse, sel=sel_arr,
+    return dict(out=out, out_bf16=out_bf16, lse=lse, sel=sel_arr,
                 sel_count=sel_cnt, kth=kth, centroids=cents,
                 retrieval_heads=np.array(ret_heads, dtype=np.int64))
