@@ -60,7 +60,8 @@
  *    Hq <= 128, Hq % Hkv == 0. A prefill's S may be any size from 0 to
  *    16 777 152 = 2^24 - 64 (a ragged last block is handled; one KV head's
  *    K must fit a 4 GiB buffer descriptor); larger S returns
- *    RTP_EUNSUPPORTED.
+ *    RTP_EUNSUPPORTED. top_k and n_recent are at most 262 143 (the most
+ *    64-token blocks such a sequence has); larger values return RTP_EINVAL.
  *  - Two calls that share a workspace must not overlap in time.
  */
 #ifndef RTP_H
@@ -75,7 +76,8 @@ extern "C" {
 
 /* Status codes. */
 #define RTP_OK 0
-#define RTP_EINVAL (-1)       /* null pointer, negative or inconsistent size */
+#define RTP_EINVAL (-1)       /* null pointer, negative, too large or
+                                 inconsistent size */
 #define RTP_EUNSUPPORTED (-2) /* d != 128, block != 64, bad r, Hq > 128,
                                 prefill S > 2^24 - 64 */
 #define RTP_EWORKSPACE (-3)   /* ws too small or not 256-byte aligned */

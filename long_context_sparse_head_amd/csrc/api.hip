@@ -54,7 +54,8 @@ int check_shape(int S, int Hq, int Hkv, int d) {
 
 int check_indexer(int n_ret, int r, int block, int top_k) {
   if (block != rtp::kBlk) return fail(RTP_EUNSUPPORTED, "only block = 64 is supported");
-  if (top_k < 0) return fail(RTP_EINVAL, "top_k must be >= 0");
+  if (top_k < 0 || top_k > rtp::kMaxBlocks)
+    return fail(RTP_EINVAL, "top_k must be in [0, 262143] (the most blocks a sequence has)");
   if (n_ret > 0 && (r < 16 || r > 128 || r % 16))
     return fail(RTP_EUNSUPPORTED, "r must be a multiple of 16 in [16, 128]");
   return RTP_OK;
@@ -671,7 +672,7 @@ size_t rtp_decode_workspace_bytes(int B, int Lmax, int Hq, int Hkv, int d,
                                   const uint8_t* is_retrieval, int r,
                                   int block, int top_k, int n_recent) {
   if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0 ||
-      n_recent < 1)
+      n_recent < 1 || n_recent > rtp::kMaxBlocks)
     return 0;
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
@@ -683,7 +684,7 @@ size_t rtp_decode_clustered_workspace_bytes(int B, int Lmax, int Hq, int Hkv,
                                             int r, int block, int top_k,
                                             int n_recent) {
   if (check_shape(0, Hq, Hkv, d) || !is_retrieval || B < 0 || Lmax < 0 ||
-      n_recent < 1)
+      n_recent < 1 || n_recent > rtp::kMaxBlocks)
     return 0;
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (check_indexer(hi.n_ret, r, block, top_k)) return 0;
@@ -717,7 +718,8 @@ int cluster_keys_impl(const void* k_cache, const int32_t* cache_len, int B,
   if (int e = check_indexer(hi.n_ret, r, block, 0)) return e;
   if (hi.n_ret > 0 && r > 64)
     return fail(RTP_EUNSUPPORTED, "clustering supports r in {16, 32, 48, 64}");
-  if (n_recent < 1) return fail(RTP_EINVAL, "n_recent must be >= 1");
+  if (n_recent < 1 || n_recent > rtp::kMaxBlocks)
+    return fail(RTP_EINVAL, "n_recent must be in [1, 262143]");
   if (iters < 0 || iters > 1000) return fail(RTP_EINVAL, "iters must be in [0, 1000]");
   if (B == 0 || hi.n_ret == 0 || Lmax < 64) return RTP_OK;
   if (!k_cache || !cache_len || !p_k || !centroids || !cl_m || !cl_off ||
@@ -809,8 +811,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (B < 0 || Lmax < 1) return fail(RTP_EINVAL, "B must be >= 0 and Lmax >= 1");
   if (!is_retrieval) return fail(RTP_EINVAL, "is_retrieval is NULL");
   if (window < 1) return fail(RTP_EINVAL, "window must be >= 1");
-  if (n_recent < 1)
-    return fail(RTP_EINVAL, "n_recent must be >= 1 (the block of the new token is always kept)");
+  if (n_recent < 1 || n_recent > rtp::kMaxBlocks)
+    return fail(RTP_EINVAL, "n_recent must be in [1, 262143] (the block of the new token is always kept)");
   const HeadInfo hi = scan_mask(is_retrieval, Hq);
   if (int e = check_indexer(hi.n_ret, r, block, top_k)) return e;
   if (B == 0) return RTP_OK;

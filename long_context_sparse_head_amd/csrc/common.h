@@ -16,6 +16,8 @@ constexpr int kBlk = 64;     // indexer block = attention key tile
 constexpr int kMaxHeads = 128;
 // Longest prefill: one KV head's K (S x 256 B) must fit a buffer descriptor.
 constexpr int kMaxSeq = (1 << 24) - 64;
+// the most 64-token blocks a sequence has; top_k and n_recent are capped by it
+constexpr int kMaxBlocks = kMaxSeq / 64;
 
 // MFMA lane layouts on gfx950 (checked on hardware against a CPU matmul):
 //  v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8*(l/32)+e] and

@@ -118,6 +118,34 @@ def test_prefill_argument_validation_returns_codes():
     assert _prefill(lib, mp2, Hq=130, Hkv=130) == -2
 
 
+def test_top_k_and_n_recent_are_capped_at_the_most_blocks():
+    # 262 143 = (2^24 - 64) / 64 blocks: a larger budget could only overflow
+    # the selection width (top_k + 2, top_k + 1 + n_recent), so it is refused
+    lib = rtp.load()
+    m, mp = _mask([1, 0, 0, 0])
+    big = (1 << 31) - 2
+    assert _prefill(lib, mp, top_k=262143) == -3   # valid, needs a workspace
+    assert _prefill(lib, mp, top_k=262144) == -1
+    assert _prefill(lib, mp, top_k=big) == -1
+    assert b"262143" in lib.rtp_last_error()
+    assert lib.rtp_prefill_workspace_bytes(128, 4, 1, 128, mp, 16, 64,
+                                           big) == 0
+    m1, mp1 = _mask([0, 1])
+    assert lib.rtp_decode_workspace_bytes(2, 4096, 2, 1, 128, mp1, 16, 64, 8,
+                                          262143) > 0
+    assert lib.rtp_decode_workspace_bytes(2, 4096, 2, 1, 128, mp1, 16, 64, 8,
+                                          262144) == 0
+    assert lib.rtp_decode_workspace_bytes(2, 4096, 2, 1, 128, mp1, 16, 64,
+                                          big, 2) == 0
+    P = ctypes.c_void_p
+    for top_k, n_recent in ((big, 2), (8, big)):
+        st = lib.rtp_hybrid_attn_decode(P(1), P(1), P(1), P(1), 2, 4096, 2, 1,
+                                        128, mp1, 64, P(1), P(1), 16, 64,
+                                        top_k, n_recent, 0.0, P(1), None, None,
+                                        None, 0, None)
+        assert st == -1, (top_k, n_recent)
+
+
 def _headwise(lib, mp, windows, **kw):
     a = dict(q=1, k=1, v=1, S=128, Hq=4, Hkv=1, d=128, mode=0, pq=1, pk=1,
              r=16, block=64, top_k=4, scale=0.0, sel_in=None, cnt_in=None,
