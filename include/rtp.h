@@ -59,8 +59,8 @@
  *  - Supported shapes: d = 128, block = 64, r a multiple of 16 in [16, 128],
  *    Hq <= 128, Hq % Hkv == 0. A prefill's S may be any size from 0 to
  *    16 777 152 = 2^24 - 64 (a ragged last block is handled; one KV head's
- *    K must fit a 4 GiB buffer descriptor); larger S returns
- *    RTP_EUNSUPPORTED. top_k and n_recent are at most 262 143 (the most
+ *    K must fit a 4 GiB buffer descriptor; that largest S is tested against
+ *    the oracle); larger S returns RTP_EUNSUPPORTED. top_k and n_recent are at most 262 143 (the most
  *    64-token blocks such a sequence has); larger values return RTP_EINVAL.
  *  - Two calls that share a workspace must not overlap in time.
  */
