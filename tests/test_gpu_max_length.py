@@ -1,4 +1,5 @@
-"""GPU parity of a prefill at the largest supported length, S = 2^24 - 64.
+"""GPU parity at the largest supported length: a prefill of S = 2^24 - 64
+tokens, and a decode step on a cache of S + 1 tokens.
 
 One KV head's K (and V^T) then fills a 4 GiB buffer descriptor up to its
 last 16 KiB, every offset of the attention and indexer kernels takes its
@@ -7,7 +8,9 @@ key blocks. One streaming head (window 4096) and one retrieval head share
 the KV head. The oracle checks sampled selection rows (the first, around
 S/2, the last and random ones, each up to 262 141 candidates) and the
 outputs and LSE of sampled query blocks of both heads, under the GPU's
-selection (identical to the oracle's except at logged ties).
+selection (identical to the oracle's except at logged ties). The decode
+step chooses among 262 141 candidate blocks, attends a window of 8192 and
+the chosen blocks, and is checked like every other decode test.
 """
 import numpy as np
 import pytest
@@ -15,7 +18,8 @@ import torch
 
 import oracle
 from tests import parity
-from workloads import PrefillWorkload, make_prefill, bf16_bits
+from tests.test_gpu_decode import _wl as _dec_wl, check as dec_check
+from workloads import PrefillWorkload, make_prefill, make_decode, bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +89,11 @@ def test_prefill_at_the_largest_supported_length(gpu_lib):
                                      f"max length h={h} qb={qb}")
     print(f"[max] outputs of {len(qbs)} query blocks x 2 heads: max |dO| "
           f"{worst:.2e}", flush=True)
+
+
+def test_decode_after_the_largest_supported_prefill(gpu_lib):
+    L = S_MAX + 1  # the prompt plus the new token (a one-token last block)
+    print(f"[max] decode L={L}", flush=True)
+    y = make_decode(_dec_wl(1, L, Hq=2, Hkv=1, ret=(1,), window=8192,
+                            top_k=64, seed=13), device="cuda")
+    dec_check(gpu_lib, y, "decode max length")
